@@ -1,0 +1,340 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the fused MoE forward layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls this file;
+ * only the test-suite, the smoke check and the benchmark's CPU-baseline leg
+ * load it.  It shares no code, header or table with the HIP path.
+ *
+ * What it computes (tilelang.dataflow README, section 3.5 "Fused MoE: map ->
+ * reshared -> map"): tokens are grouped by expert from their routing
+ * metadata, GEMM-1 applies the gate and up shards of the expert's weights and
+ * forms the gated intermediate, GEMM-2 applies the down projection, scales by
+ * the routing weight and the rows are written back per token.  The result is
+ * the plain MoE definition
+ *
+ *     out[t] = sum_{j<k} w[t,j] * W2[e] . ( silu(W1g[e] . x[t]) * (W1u[e] . x[t]) ),
+ *     e = ids[t,j],
+ *
+ * with the activation taken on the unrounded fp32 accumulator (PipeLink,
+ * section 5.5 "Fused GEMM and Activation": the FP32 accumulator stays
+ * unrounded through the activation, the activation is then stored as BF16).
+ *
+ * Precision: arithmetic is fp32 (the accumulator precision the pages name).
+ * Every operation is evaluated in double and rounded to float right after
+ * (exact emulation of fp32 +,-,*,/ because 53 >= 2*24+2).  Flag
+ * ORACLE_ACC64 skips that rounding so the same code runs in fp64; the
+ * fp32-vs-fp64 gap bounds the oracle's own rounding error.
+ *
+ * Reading of the pages where they are silent (each listed in the design
+ * notes): OCP E4M3FN is the FP8 format; dequantisation is code * fp32 scale;
+ * in FP8 mode the intermediate is requantised per row per 128 columns with
+ * scale amax/448; ids outside [0,E) are dropped; the top-k sum runs in
+ * ascending slot order from +0.0 with one final rounding.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL 1
+#define ORACLE_ENOMEM 2
+
+/* modes: which dtypes the layer is fed */
+#define ORACLE_MODE_F32ACT 0 /* x fp32, W bf16, out fp32 */
+#define ORACLE_MODE_BF16 1   /* x bf16, W bf16, out bf16 */
+#define ORACLE_MODE_FP8 2    /* x e4m3 + scales, W e4m3 + 128x128 block scales, out bf16 */
+
+/* flags */
+#define ORACLE_MIRROR_H 1 /* round the intermediate where the method stores it */
+#define ORACLE_ACC64 2    /* evaluate in fp64 instead of fp32 */
+
+#define QBLK 128 /* block-scale granularity along every dimension */
+
+/* ------------------------------------------------------------------ codecs */
+
+/* OCP 8-bit floating point, E4M3FN variant: 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6;
+ * S.1111.111 is NaN; there is no infinity; the largest finite value is 448. */
+double oracle_e4m3_decode(uint8_t code) {
+    int sign = code >> 7;
+    int ex = (code >> 3) & 15;
+    int man = code & 7;
+    double mag;
+    if (ex == 15 && man == 7) return NAN;
+    if (ex == 0)
+        mag = ldexp((double)man / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)man / 8.0, ex - 7);
+    return sign ? -mag : mag;
+}
+
+/* The 256 decoded values, filled once from the definition above so the
+ * inner loops below index a table instead of re-deriving each value. */
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+
+static void oracle_init(void) {
+    int c;
+    if (e4m3_table_ready) return;
+    for (c = 0; c < 256; ++c) e4m3_table[c] = oracle_e4m3_decode((uint8_t)c);
+    e4m3_table_ready = 1;
+}
+
+/* Nearest E4M3FN code to v, ties to the code with an even mantissa field;
+ * finite magnitudes above 448 saturate to 448; NaN maps to 0x7F.  Written as a
+ * search over the 127 non-negative finite codes so it follows the format's
+ * definition directly. */
+uint8_t oracle_e4m3_encode(double v) {
+    uint8_t sign;
+    double a, best_d;
+    int c, best;
+    oracle_init();
+    if (isnan(v)) return 0x7F;
+    sign = signbit(v) ? 0x80 : 0x00;
+    a = fabs(v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    best = 0;
+    best_d = a; /* distance to code 0 */
+    for (c = 1; c <= 0x7E; ++c) {
+        double d = fabs(e4m3_table[c] - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best_d = d;
+            best = c;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* bfloat16: the upper 16 bits of an IEEE binary32.  Encoding rounds the
+ * binary32 value to nearest with ties to even on the dropped 16 bits; NaN
+ * stays a quiet NaN. */
+uint16_t oracle_bf16_encode(float f) {
+    uint32_t u, lsb;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+    lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+float oracle_bf16_decode(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------- arithmetic */
+
+/* One rounding step: to binary32 unless the fp64 flag is set. */
+static inline double R(double v, int f64) { return f64 ? v : (double)(float)v; }
+
+/* Per-row-per-128 requantisation of a chunk of the intermediate (FP8 mode):
+ * s = amax / 448 (s = 1 for an all-zero chunk); value -> decode(encode(v/s)) * s.
+ * Exported for the tests. */
+void oracle_requant_chunk(double* a, int64_t n, int f64) {
+    double amax = 0.0, s;
+    int64_t i;
+    oracle_init();
+    for (i = 0; i < n; ++i)
+        if (fabs(a[i]) > amax) amax = fabs(a[i]);
+    s = amax > 0.0 ? R(amax / 448.0, f64) : 1.0;
+    for (i = 0; i < n; ++i) {
+        double q = e4m3_table[oracle_e4m3_encode(R(a[i] / s, f64))];
+        a[i] = R(q * s, f64);
+    }
+}
+
+/* Dequantised element loaders. */
+static inline double ld_x(int mode, int f64, const void* x, const float* xs, int64_t d_h, int64_t t, int64_t c) {
+    if (mode == ORACLE_MODE_F32ACT) return ((const float*)x)[t * d_h + c];
+    if (mode == ORACLE_MODE_BF16) return oracle_bf16_decode(((const uint16_t*)x)[t * d_h + c]);
+    return R(e4m3_table[((const uint8_t*)x)[t * d_h + c]] * xs[t * (d_h / QBLK) + c / QBLK], f64);
+}
+
+/* W is [E, rows, cols] row-major; scales are [E, rows/128, cols/128]. */
+static inline double ld_w(int mode, int f64, const void* w, const float* ws, int64_t rows, int64_t cols,
+                          int64_t e, int64_t r, int64_t c) {
+    int64_t i = (e * rows + r) * cols + c;
+    if (mode != ORACLE_MODE_FP8) return oracle_bf16_decode(((const uint16_t*)w)[i]);
+    return R(e4m3_table[((const uint8_t*)w)[i]] * ws[(e * (rows / QBLK) + r / QBLK) * (cols / QBLK) + c / QBLK],
+             f64);
+}
+
+static int check_dims(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_e) {
+    if (T < 0 || E < 1 || k < 1 || d_h < 1 || d_e < 1) return 0;
+    if (mode < 0 || mode > 2) return 0;
+    if (mode == ORACLE_MODE_FP8 && (d_h % QBLK || d_e % QBLK)) return 0;
+    return 1;
+}
+
+/* Expert FFN of one assignment: y = W2[e] . (silu(g) * u), g and u from
+ * W1[e] rows [0,d_e) and [d_e,2 d_e).  Accumulations run in ascending index
+ * order.  a is scratch of d_e doubles, y receives d_h values. */
+static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void* x, const float* xs, int64_t t,
+                       const void* w1, const float* w1s, const void* w2, const float* w2s, int64_t e, double* a,
+                       double* y) {
+    int f64 = (flags & ORACLE_ACC64) != 0;
+    int64_t r, c, n;
+    for (r = 0; r < d_e; ++r) {
+        double g = 0.0, u = 0.0, sg;
+        for (c = 0; c < d_h; ++c) {
+            double xv = ld_x(mode, f64, x, xs, d_h, t, c);
+            g = R(g + R(ld_w(mode, f64, w1, w1s, 2 * d_e, d_h, e, r, c) * xv, f64), f64);
+            u = R(u + R(ld_w(mode, f64, w1, w1s, 2 * d_e, d_h, e, d_e + r, c) * xv, f64), f64);
+        }
+        /* SiLU(g) = g / (1 + exp(-g)) */
+        sg = f64 ? g / (1.0 + exp(-g)) : R(g / R(1.0 + (double)expf((float)-g), 0), 0);
+        a[r] = R(sg * u, f64);
+    }
+    if (flags & ORACLE_MIRROR_H) {
+        if (mode == ORACLE_MODE_FP8) {
+            for (r = 0; r < d_e; r += QBLK) oracle_requant_chunk(a + r, QBLK, f64);
+        } else {
+            for (r = 0; r < d_e; ++r) a[r] = oracle_bf16_decode(oracle_bf16_encode((float)a[r]));
+        }
+    }
+    for (n = 0; n < d_h; ++n) {
+        double s = 0.0;
+        for (r = 0; r < d_e; ++r) s = R(s + R(ld_w(mode, f64, w2, w2s, d_h, d_e, e, n, r) * a[r], f64), f64);
+        y[n] = s;
+    }
+}
+
+/*
+ * Forward pass for the tokens listed in rows[0..nrows) (all T tokens when rows
+ * is NULL, nrows then ignored).  out_acc [nrows, d_h] receives the fp32 (or
+ * fp64) top-k sum before the final cast; out (optional) receives it cast to the
+ * mode's output dtype (fp32 in F32ACT mode, bf16 bits otherwise).
+ */
+int moe_oracle_forward(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_e, const void* x,
+                       const float* x_scale, const int32_t* topk_ids, const float* topk_w, const void* w1,
+                       const float* w1_scale, const void* w2, const float* w2_scale, int flags,
+                       const int64_t* rows, int64_t nrows, double* out_acc, void* out) {
+    int64_t i;
+    int f64 = (flags & ORACLE_ACC64) != 0;
+    int failed = 0;
+    if (!check_dims(mode, T, E, k, d_h, d_e)) return ORACLE_EINVAL;
+    if (!x || !topk_ids || !topk_w || !w1 || !w2 || !out_acc) return ORACLE_EINVAL;
+    if (mode == ORACLE_MODE_FP8 && (!x_scale || !w1_scale || !w2_scale)) return ORACLE_EINVAL;
+    if (!rows) nrows = T;
+    oracle_init();
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nrows; ++i) {
+        int64_t t = rows ? rows[i] : i;
+        double* a = (double*)malloc(sizeof(double) * (size_t)(d_e + d_h));
+        double* y = a ? a + d_e : NULL;
+        double* acc = out_acc + i * d_h;
+        int64_t n;
+        int j;
+        if (!a || t < 0 || t >= T) {
+#pragma omp atomic write
+            failed = 1;
+            free(a);
+            continue;
+        }
+        for (n = 0; n < d_h; ++n) acc[n] = 0.0;
+        for (j = 0; j < k; ++j) {
+            int64_t p = t * k + j;
+            int32_t e = topk_ids[p];
+            double wt = topk_w[p];
+            if (e < 0 || e >= E) continue; /* dropped assignment */
+            expert_ffn(mode, flags, d_h, d_e, x, x_scale, t, w1, w1_scale, w2, w2_scale, e, a, y);
+            for (n = 0; n < d_h; ++n) acc[n] = R(acc[n] + R(wt * y[n], f64), f64);
+        }
+        if (out) {
+            for (n = 0; n < d_h; ++n) {
+                if (mode == ORACLE_MODE_F32ACT)
+                    ((float*)out)[i * d_h + n] = (float)acc[n];
+                else
+                    ((uint16_t*)out)[i * d_h + n] = oracle_bf16_encode((float)acc[n]);
+            }
+        }
+        free(a);
+    }
+    return failed ? ORACLE_EINVAL : ORACLE_OK;
+}
+
+/*
+ * Routing metadata of the grouped-by-expert layout (tilelang.dataflow README,
+ * section 3.5, step 1: group sizes, offsets, padded offsets and the expert of
+ * each group block).  Assignment p = t*k + j has expert ids[p]; ids outside
+ * [0,E) are dropped.  Within an expert, assignments keep ascending p (a stable
+ * counting sort, written as one ascending pass).  Each expert's group is padded
+ * to a multiple of bm rows; an expert with no rows gets no block.
+ *
+ *   counts[E]            rows per expert
+ *   offsets[E+1]         exclusive prefix sum of counts
+ *   padded_offsets[E+1]  exclusive prefix sum of bm*ceil(counts/bm)
+ *   pos[N]               offsets[e] + rank of p within e, -1 if dropped
+ *   sorted_p[N]          sorted_p[pos[p]] = p for the first offsets[E] entries, -1 after
+ *   ppos[N]              padded_offsets[e] + rank, -1 if dropped
+ *   row_src[n_pad_cap]   p at ppos[p], -1 on padding rows and beyond padded_offsets[E]
+ *   tile_expert[tile_cap], tile_row0[tile_cap]  expert and first padded row of
+ *                        each bm-row block in ascending expert order, -1 after
+ *   stats[2]             {dropped, number of blocks}
+ */
+int moe_oracle_route(const int32_t* ids, int64_t N, int E, int bm, int32_t* counts, int32_t* offsets,
+                     int32_t* padded_offsets, int32_t* pos, int32_t* sorted_p, int32_t* ppos, int32_t* row_src,
+                     int64_t n_pad_cap, int32_t* tile_expert, int32_t* tile_row0, int64_t tile_cap,
+                     int64_t* stats) {
+    int64_t p, i;
+    int e;
+    int64_t ntiles = 0, dropped = 0;
+    int32_t* seen;
+    if (!ids || N < 0 || E < 1 || bm < 1) return ORACLE_EINVAL;
+    seen = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+    if (!seen) return ORACLE_ENOMEM;
+    for (e = 0; e < E; ++e) counts[e] = 0;
+    for (p = 0; p < N; ++p) {
+        if (ids[p] >= 0 && ids[p] < E)
+            counts[ids[p]]++;
+        else
+            dropped++;
+    }
+    offsets[0] = 0;
+    padded_offsets[0] = 0;
+    for (e = 0; e < E; ++e) {
+        int32_t tiles = (counts[e] + bm - 1) / bm;
+        offsets[e + 1] = offsets[e] + counts[e];
+        padded_offsets[e + 1] = padded_offsets[e] + tiles * bm;
+        ntiles += tiles;
+    }
+    if (padded_offsets[E] > n_pad_cap || ntiles > tile_cap) {
+        free(seen);
+        return ORACLE_EINVAL;
+    }
+    for (p = 0; p < N; ++p) sorted_p[p] = -1;
+    for (i = 0; i < n_pad_cap; ++i) row_src[i] = -1;
+    for (p = 0; p < N; ++p) {
+        int32_t id = ids[p];
+        if (id < 0 || id >= E) {
+            pos[p] = -1;
+            ppos[p] = -1;
+            continue;
+        }
+        pos[p] = offsets[id] + seen[id];
+        ppos[p] = padded_offsets[id] + seen[id];
+        seen[id]++;
+        sorted_p[pos[p]] = (int32_t)p;
+        row_src[ppos[p]] = (int32_t)p;
+    }
+    for (i = 0; i < tile_cap; ++i) {
+        tile_expert[i] = -1;
+        tile_row0[i] = -1;
+    }
+    i = 0;
+    for (e = 0; e < E; ++e) {
+        int32_t r0;
+        for (r0 = padded_offsets[e]; r0 < padded_offsets[e + 1]; r0 += bm) {
+            tile_expert[i] = e;
+            tile_row0[i] = r0;
+            ++i;
+        }
+    }
+    stats[0] = dropped;
+    stats[1] = ntiles;
+    free(seen);
+    return ORACLE_OK;
+}

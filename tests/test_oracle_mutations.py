@@ -1,0 +1,49 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case edits one plausible mistake into a copy of the oracle's C source
+(dropped term, wrong sign, wrong index, transposed operand, broken rounding,
+broken stability), builds it, and runs the CPU pin tests against it in a
+subprocess; the run must fail.  The product path is not involved.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
+
+MUTATIONS = {
+    "gate_up_swapped": ("e, d_e + r, c) * xv", "e, r, c) * xv"),
+    "routing_weight_dropped": ("R(wt * y[n], f64)", "y[n]"),
+    "silu_sign": ("expf((float)-g)", "expf((float)g)"),
+    "w2_transposed": ("d_h, d_e, e, n, r)", "d_h, d_e, e, r, n)"),
+    "requant_scale_240": ("amax / 448.0", "amax / 240.0"),
+    "scatter_unstable": ("pos[p] = offsets[id] + seen[id];", "pos[p] = offsets[id] + counts[id] - 1 - seen[id];"),
+    "no_padding": ("padded_offsets[e] + tiles * bm", "padded_offsets[e] + counts[e]"),
+    "bf16_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
+    "e4m3_bias_8": ("ex - 7)", "ex - 8)"),
+    "first_slot_skipped": ("for (j = 0; j < k; ++j)", "for (j = 1; j < k; ++j)"),
+    "x_scale_block_ignored": ("xs[t * (d_h / QBLK) + c / QBLK]", "xs[t * (d_h / QBLK)]"),
+    "w_scale_col_block_ignored": ("* (cols / QBLK) + c / QBLK]", "* (cols / QBLK)]"),
+}
+
+PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_routing.py", "tests/test_oracle_forward.py"]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor not found: {old}"
+    mutated = src.replace(old, new)
+    c = tmp_path / "mut.c"
+    so = tmp_path / "libmut.so"
+    c.write_text(mutated)
+    subprocess.run(["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-shared", "-fPIC", str(c),
+                    "-o", str(so), "-lm"], check=True)
+    env = dict(os.environ, MOE_ORACLE_LIB=str(so))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_TESTS],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
