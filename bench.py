@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Fused MoE layer benchmark on one MI355X.
+
+A step is one moe_fused_forward call (routing -> GEMM-1 + SwiGLU -> GEMM-2 +
+routing weight -> combine) over the synthetic workload, inputs resident in
+HBM.  W untimed warmup steps, then K timed steps, each bracketed by HIP
+events on the stream the library launches on; the line reports the p50 step
+time, TFLOP/s at that p50 (algorithmic FLOPs = 6*d_h*d_e per valid
+assignment), the dominant kernel's roofline fraction from its own event-timed
+duration, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused MoE layer p50 µs + TFLOP/s (% MFMA/HBM roofline), 1 MI355X"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 5000.0}  # dense MFMA: bf16 (F32ACT runs bf16 MFMA), fp8
+DTYPE = {0: "bf16", 1: "bf16", 2: "fp8_e4m3"}
+DEFAULT_CONFIG = "qwen_bf16"
+
+
+def gemm1_alg_bytes(w):
+    """Bytes GEMM-1 must move once: active experts' W1 (+ block scales), x (+ scales), h (+ scales)."""
+    from skew_aware_grouped_amd import workloads as W
+    a = w.active_experts()
+    wb = 1 if w.mode == W.MODE_FP8 else 2
+    xb = {W.MODE_F32ACT: 4, W.MODE_BF16: 2, W.MODE_FP8: 1}[w.mode]
+    nv = w.valid_assignments()
+    b = a * 2 * w.d_e * w.d_h * wb + w.T * w.d_h * xb + nv * w.d_e * wb
+    if w.mode == W.MODE_FP8:
+        b += a * (2 * w.d_e // 128) * (w.d_h // 128) * 4 + w.T * (w.d_h // 128) * 4 + nv * (w.d_e // 128) * 4
+    return float(b)
+
+
+def gemm2_alg_bytes(w):
+    from skew_aware_grouped_amd import workloads as W
+    a = w.active_experts()
+    wb = 1 if w.mode == W.MODE_FP8 else 2
+    yb = 4 if w.mode == W.MODE_F32ACT else 2
+    nv = w.valid_assignments()
+    b = a * w.d_h * w.d_e * wb + nv * w.d_e * wb + nv * w.d_h * yb
+    if w.mode == W.MODE_FP8:
+        b += a * (w.d_h // 128) * (w.d_e // 128) * 4 + nv * (w.d_e // 128) * 4
+    return float(b)
+
+
+def cpu_baseline(w, target_s=15.0):
+    """The oracle as it stands, on a bounded sample of the workload's tokens."""
+    from oracle import moe_oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    rng = np.random.default_rng(0)
+    # calibrate on a few tokens, then size the sample to ~target_s
+    probe = rng.choice(w.T, size=min(4, w.T), replace=False)
+    t0 = time.perf_counter()
+    moe_oracle.forward(w, rows=probe)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    n = int(min(w.T, max(len(probe), len(probe) * target_s / dt)))
+    rows = np.sort(rng.choice(w.T, size=n, replace=False))
+    t0 = time.perf_counter()
+    moe_oracle.forward(w, rows=rows)
+    dt = time.perf_counter() - t0
+    sub_ids = w.topk_ids[rows]
+    nv = int(((sub_ids >= 0) & (sub_ids < w.E)).sum())
+    flops = 6.0 * w.d_h * w.d_e * nv
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {w.T} tokens ({nv} assignments) of {w.name}, {dt:.2f} s, fp32 C oracle with "
+                      f"OpenMP over tokens",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this layer runs on one GPU; --gpus above 1 is not supported (the multi-GPU expert-"
+              "parallel path is a design, not a build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from skew_aware_grouped_amd import device, moe, workloads as W
+
+    torch.cuda.set_device(0)
+    w = W.config(args.config)
+    d = device.upload(w)
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
+    ws = moe.workspace_for(dims, "cuda:0")
+    odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
+    out = torch.empty(w.T, w.d_h, dtype=odt, device="cuda:0")
+
+    # correctness gate before timing: a few sampled rows against the oracle
+    from oracle import moe_oracle
+    device.run(d, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    rows = sorted(set(np.random.default_rng(1).choice(w.T, size=min(8, w.T), replace=False).tolist()))
+    acc, _ = moe_oracle.forward(w, rows=rows)
+    got = device.out_to_f64(out)[rows]
+    gate_err = float(np.abs(got - acc).max() / np.abs(acc).max())
+    tol = 3e-2 if w.mode == W.MODE_FP8 else 1e-2
+    if not gate_err <= tol:
+        print(f"bench.py: correctness gate failed (normwise err {gate_err:.3e} > {tol})", file=sys.stderr)
+        sys.exit(1)
+
+    for _ in range(args.warmup):
+        device.run(d, out=out, workspace=ws)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        device.run(d, out=out, workspace=ws, stream=stream, events=ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([e[0].elapsed_time(e[4]) for e in ev])
+    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+    p50 = float(np.median(step_ms))
+    flops = W.flops(w)
+    alg_bytes = W.algorithmic_bytes(w)
+    tflops = flops / (p50 * 1e-3) / 1e12
+    stages = {n: round(float(np.mean(stage_ms[:, j])) * 1e3, 2) for j, n in
+              enumerate(["route", "gemm1_swiglu", "gemm2_weight", "combine"])}
+    g1_us = float(np.mean(stage_ms[:, 1])) * 1e3
+    g1_bytes = gemm1_alg_bytes(w)
+    g1_gbs = g1_bytes / (g1_us * 1e-6) / 1e9
+    layer_gbs = alg_bytes / (p50 * 1e-3) / 1e9
+    bound = "hbm"
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(p50, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE[w.mode],
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": w.T, "experts": w.E, "top_k": w.k, "d_hidden": w.d_h,
+                   "d_expert": w.d_e, "active_experts": w.active_experts(),
+                   "valid_assignments": w.valid_assignments(), "routing": str(w.meta.get("routing"))},
+        "p50_us": round(p50 * 1e3, 2),
+        "p10_us": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+        "p90_us": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+        "wall_us_per_step": round(wall / args.steps * 1e6, 2),
+        "gflop": round(flops / 1e9, 4),
+        "alg_mb": round(alg_bytes / 1e6, 3),
+        "layer_gbs": round(layer_gbs, 1),
+        "layer_roofline_frac": round(max(layer_gbs / PEAK_HBM_GBS, tflops / PEAK_TFLOPS[w.mode]), 4),
+        "stage_us": stages,
+        "gate_normwise_err": round(gate_err, 6),
+        "roofline": {"kernel": "gemm1_swiglu", "bound": bound, "achieved": round(g1_gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g1_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "alg_bytes_per_launch": g1_bytes, "avg_launch_us": round(g1_us, 2)},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

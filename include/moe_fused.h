@@ -1,0 +1,179 @@
+/*
+ * moe_fused.h -- C ABI of the MI355X (gfx950) fused Mixture-of-Experts forward layer.
+ *
+ * The layer is the fused MoE of the tilelang.dataflow README, section 3.5
+ * ("Fused MoE: map -> reshared -> map"): routed tokens are grouped by expert
+ * (group sizes, offsets, padded offsets, expert of each group block), GEMM-1
+ * applies each expert's gate and up weights and forms the gated intermediate,
+ * GEMM-2 applies the down projection, scales each row by its routing weight and
+ * the per-token rows are summed.  The activation is SwiGLU, silu(gate) * up,
+ * taken on the unrounded fp32 accumulator (PipeLink, section 5.5 "Fused GEMM
+ * and Activation").  FP8 is OCP E4M3FN with fp32 block scales.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP global memory) of the current
+ *    device, dense row-major, 16-byte aligned.  Sizes are element counts.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *    stream).  Work is only enqueued: no call synchronises the host, none
+ *    reads routing back to the host, and none allocates device memory.
+ *  - The caller owns every buffer and keeps it alive until the stream work has
+ *    completed.  Outputs must not alias inputs.  Calls that share a workspace
+ *    must be ordered on one stream.
+ *  - Return value: MOE_OK (0) or an error code.  Argument checks run on the host
+ *    before anything is enqueued; on error nothing is enqueued.  MOE_ERR_HIP
+ *    reports a failed launch (the HIP error is then cleared).
+ */
+#ifndef MOE_FUSED_H
+#define MOE_FUSED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbols of the shared library (everything else is hidden). */
+#define MOE_API __attribute__((visibility("default")))
+
+/* Error codes. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1 /* null pointer, bad shape, misaligned pointer */
+#define MOE_ERR_UNSUPPORTED 2 /* shape outside the supported envelope (see moe_dims) */
+#define MOE_ERR_WORKSPACE 3   /* workspace missing or smaller than moe_workspace_bytes() */
+#define MOE_ERR_HIP 4         /* a HIP launch or device query failed */
+
+/* Data modes (dtypes of x / weights / out):
+ *  MOE_MODE_F32ACT  x fp32 [T,d_h]; W1, W2 bf16; out fp32.  The GEMMs run on
+ *                   bf16 MFMA, so x is rounded to bf16 (nearest-even) on load.
+ *  MOE_MODE_BF16    x, W1, W2, out bf16.
+ *  MOE_MODE_FP8     x, W1, W2 e4m3 codes with fp32 scales; out bf16. */
+#define MOE_MODE_F32ACT 0
+#define MOE_MODE_BF16 1
+#define MOE_MODE_FP8 2
+
+/* Layer shape.  Supported envelope: 0 <= num_tokens, 1 <= num_experts <= 256,
+ * 1 <= top_k <= 8, num_tokens*top_k < 2^31, d_hidden and d_expert positive
+ * multiples of 128. */
+typedef struct {
+    int32_t mode;        /* MOE_MODE_* */
+    int32_t num_tokens;  /* T */
+    int32_t num_experts; /* E */
+    int32_t top_k;       /* k */
+    int32_t d_hidden;    /* d_h */
+    int32_t d_expert;    /* d_e */
+} moe_dims;
+
+/* FP8 block scales (fp32, dequantised value = code * scale).  Required in
+ * MOE_MODE_FP8, ignored otherwise.
+ *  x_scale   [T, d_h/128]                 one scale per token per 128 columns
+ *  w1_scale  [E, 2*d_e/128, d_h/128]      one scale per 128x128 block of W1
+ *  w2_scale  [E, d_h/128, d_e/128]        one scale per 128x128 block of W2 */
+typedef struct {
+    const float* x_scale;
+    const float* w1_scale;
+    const float* w2_scale;
+} moe_scales;
+
+/* Bytes of device workspace moe_fused_forward needs for these dims (routing
+ * metadata, task lists, the intermediate and the per-assignment rows).
+ * Returns 0 if the dims are invalid. */
+MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
+
+/*
+ * Fused MoE forward:
+ *   out[t] = sum_{j<k} topk_w[t,j] * W2[e] . ( silu(W1[e][0:d_e] . x[t]) * (W1[e][d_e:2d_e] . x[t]) ),
+ *   e = topk_ids[t,j].
+ *
+ *  x         [T, d_h]            fp32 / bf16 / e4m3 per mode
+ *  topk_ids  [T, k] int32        expert of each assignment p = t*k + j; ids
+ *                                outside [0,E) are dropped (contribute 0)
+ *  topk_w    [T, k] fp32         routing weights, used as given
+ *  w1        [E, 2*d_e, d_h]     rows [0,d_e) gate, [d_e,2*d_e) up; K (d_h) contiguous
+ *  w2        [E, d_h, d_e]       K (d_e) contiguous
+ *  scales    FP8 mode only (may be NULL otherwise)
+ *  out       [T, d_h]            fp32 (F32ACT) or bf16; every row is written
+ *  workspace device buffer of at least moe_workspace_bytes(dims) bytes, 256-byte aligned
+ *
+ * Steps enqueued on `stream`: routing (histogram, prefix scan, stable scatter,
+ * block map and task lists), grouped GEMM-1 with the SwiGLU epilogue,
+ * grouped GEMM-2 with the routing-weight epilogue, and the top-k combine in
+ * ascending slot order.  The result is bitwise identical across calls.
+ */
+MOE_API int moe_fused_forward(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                      const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* moe_fused_forward with stage timing: records events[0..4] (hipEvent_t,
+ * created by the caller) on `stream` before routing, before GEMM-1, before
+ * GEMM-2, before the combine and after the combine, so the caller can time
+ * each kernel with hipEventElapsedTime.  Same result and errors as
+ * moe_fused_forward; MOE_ERR_INVALID_ARG if events or any of its 5 entries is
+ * NULL. */
+MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, const int32_t* topk_ids,
+                                       const float* topk_w, const void* w1, const void* w2,
+                                       const moe_scales* scales, void* out, void* workspace,
+                                       size_t workspace_bytes, void* stream, void* const* events);
+
+/* Rows per group block: each expert's group of routed rows is padded to a
+ * multiple of this (tilelang.dataflow README section 3.5, "padded offsets"). */
+MOE_API int32_t moe_block_m(void);
+
+/* Capacities of the padded row space and of the block map for N = T*k
+ * assignments over E experts: n_pad_cap = N + min(E,N)*(block_m-1),
+ * tile_cap = n_pad_cap / block_m. */
+MOE_API int moe_route_caps(int32_t num_tokens, int32_t top_k, int32_t num_experts, int64_t* n_pad_cap,
+                   int64_t* tile_cap);
+
+/* Device output buffers of moe_route (all int32, caller-owned):
+ *  counts[E]          rows routed to each expert
+ *  offsets[E+1]       exclusive prefix sum of counts
+ *  padded_offsets[E+1] exclusive prefix sum of block_m*ceil(counts/block_m)
+ *  pos[N]             offsets[e] + rank of p among expert e's assignments (ascending p), -1 if dropped
+ *  sorted_p[N]        sorted_p[pos[p]] = p; -1 beyond offsets[E]
+ *  ppos[N]            padded_offsets[e] + rank, -1 if dropped
+ *  row_src[n_pad_cap] p for each padded row, -1 on padding rows and beyond padded_offsets[E]
+ *  tile_expert[tile_cap], tile_row0[tile_cap]  expert and first padded row of each
+ *                     block in ascending expert order, -1 beyond the last block
+ *  stats[4]           {dropped, number of blocks, padded rows, 0} */
+typedef struct {
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* padded_offsets;
+    int32_t* pos;
+    int32_t* sorted_p;
+    int32_t* ppos;
+    int32_t* row_src;
+    int32_t* tile_expert;
+    int32_t* tile_row0;
+    int32_t* stats;
+} moe_route_out;
+
+/* Routing metadata alone (the first step of moe_fused_forward, same kernel),
+ * for N = T*k flat assignment ids. */
+MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
+              const moe_route_out* out, void* stream);
+
+/* Byte offsets of the workspace sections moe_fused_forward uses, for tests and
+ * inspection after a call (the routing arrays hold the layout described for
+ * moe_route; tasks are int32 quadruples {expert, first padded row, row
+ * blocks, column block}, GEMM-1's list first).  stats holds {dropped, blocks,
+ * padded rows, GEMM-1 tasks, GEMM-2 tasks, GEMM-1 counter, GEMM-2 counter, 0}.
+ * Returns MOE_ERR_INVALID_ARG for invalid dims. */
+typedef struct {
+    size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, tile_expert, tile_row0, stats;
+    size_t tasks1, tasks2, h, h_scale, y, total;
+    int64_t n_pad_cap, tile_cap, task1_cap, task2_cap;
+    int32_t block_n1, block_n2, max_row_blocks;
+} moe_ws_layout;
+
+MOE_API int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* layout);
+
+/* Human-readable name of an error code (static string). */
+MOE_API const char* moe_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FUSED_H */

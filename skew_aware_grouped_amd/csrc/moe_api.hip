@@ -1,0 +1,288 @@
+// C-ABI host side of the fused MoE library: argument checks, workspace
+// layout, persistent-grid sizing and the launch sequence
+// route -> GEMM-1 (+SwiGLU) -> GEMM-2 (+routing weight) -> combine.
+#include <mutex>
+
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool dims_ok(const moe_dims* d) {
+    if (!d) return false;
+    if (d->mode < MOE_MODE_F32ACT || d->mode > MOE_MODE_FP8) return false;
+    if (d->num_tokens < 0 || d->num_experts < 1 || d->num_experts > kMaxExperts) return false;
+    if (d->top_k < 1 || d->top_k > 8) return false;
+    if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return false;
+    if (d->d_hidden < 128 || d->d_hidden % 128 || d->d_expert < 128 || d->d_expert % 128) return false;
+    return true;
+}
+
+void route_caps(int64_t N, int64_t E, int64_t* n_pad_cap, int64_t* tile_cap) {
+    *n_pad_cap = N + (E < N ? E : N) * (kBlockM - 1);
+    *tile_cap = *n_pad_cap / kBlockM;
+}
+
+void layout_of(const moe_dims* d, moe_ws_layout* L) {
+    const int64_t N = (int64_t)d->num_tokens * d->top_k;
+    const int64_t E = d->num_experts;
+    route_caps(N, E, &L->n_pad_cap, &L->tile_cap);
+    // M-tiles: each expert's blocks grouped kMaxRowBlocks at a time
+    const int64_t mtile_cap = L->tile_cap / kMaxRowBlocks + (E < N ? E : N);
+    L->block_n1 = gemm1_block_n(d->mode);
+    L->block_n2 = gemm2_block_n(d->mode);
+    L->max_row_blocks = kMaxRowBlocks;
+    L->task1_cap = mtile_cap * (d->d_expert / L->block_n1);
+    L->task2_cap = mtile_cap * (d->d_hidden / L->block_n2);
+    const size_t hb = d->mode == MOE_MODE_FP8 ? 1 : 2;
+    const size_t yb = d->mode == MOE_MODE_F32ACT ? 4 : 2;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + (bytes ? bytes : 1));
+        return at;
+    };
+    L->counts = take(4 * E);
+    L->offsets = take(4 * (E + 1));
+    L->padded_offsets = take(4 * (E + 1));
+    L->pos = take(4 * N);
+    L->sorted_p = take(4 * N);
+    L->ppos = take(4 * N);
+    L->row_src = take(4 * L->n_pad_cap);
+    L->tile_expert = take(4 * L->tile_cap);
+    L->tile_row0 = take(4 * L->tile_cap);
+    L->stats = take(4 * kStatCount);
+    L->tasks1 = take(16 * L->task1_cap);
+    L->tasks2 = take(16 * L->task2_cap);
+    L->h = take(hb * L->n_pad_cap * d->d_expert);
+    L->h_scale = take(d->mode == MOE_MODE_FP8 ? 4 * L->n_pad_cap * (d->d_expert / kQ) : 0);
+    L->y = take(yb * N * d->d_hidden);
+    L->total = o;
+}
+
+// Per-device cache of the chip size and of the GEMM kernels' occupancy.
+struct DeviceInfo {
+    bool ready = false;
+    int cus = 0;
+    int occ1[3] = {0, 0, 0};
+    int occ2[3] = {0, 0, 0};
+};
+std::mutex g_mu;
+DeviceInfo g_dev[64];
+
+hipError_t device_info(int mode, int* cus, int* occ1, int* occ2) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_mu);
+    DeviceInfo& di = g_dev[dev];
+    if (!di.ready) {
+        err = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        for (int m = 0; m < 3; ++m) {
+            err = gemm_occupancy(m, &di.occ1[m], &di.occ2[m]);
+            if (err != hipSuccess) return err;
+            if (di.occ1[m] < 1) di.occ1[m] = 1;
+            if (di.occ2[m] < 1) di.occ2[m] = 1;
+        }
+        di.ready = true;
+    }
+    *cus = di.cus;
+    *occ1 = di.occ1[mode];
+    *occ2 = di.occ2[mode];
+    return hipSuccess;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename T>
+T* at(void* base, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_error_string(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP launch or query failed";
+        default: return "unknown error";
+    }
+}
+
+int32_t moe_block_m(void) { return kBlockM; }
+
+int moe_route_caps(int32_t num_tokens, int32_t top_k, int32_t num_experts, int64_t* n_pad_cap, int64_t* tile_cap) {
+    if (!n_pad_cap || !tile_cap || num_tokens < 0 || top_k < 1 || num_experts < 1) return MOE_ERR_INVALID_ARG;
+    route_caps((int64_t)num_tokens * top_k, num_experts, n_pad_cap, tile_cap);
+    return MOE_OK;
+}
+
+int moe_workspace_layout(const moe_dims* dims, moe_ws_layout* layout) {
+    if (!layout || !dims_ok(dims)) return MOE_ERR_INVALID_ARG;
+    layout_of(dims, layout);
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_dims* dims) {
+    if (!dims_ok(dims)) return 0;
+    moe_ws_layout L;
+    layout_of(dims, &L);
+    return L.total;
+}
+
+int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
+              const moe_route_out* out, void* stream) {
+    if (!out || num_tokens < 0 || top_k < 1 || top_k > 8 || num_experts < 1 || num_experts > kMaxExperts)
+        return MOE_ERR_INVALID_ARG;
+    if ((int64_t)num_tokens * top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    if (!out->counts || !out->offsets || !out->padded_offsets || !out->row_src || !out->tile_expert ||
+        !out->tile_row0 || !out->stats)
+        return MOE_ERR_INVALID_ARG;
+    const int64_t N = (int64_t)num_tokens * top_k;
+    if (N > 0 && (!topk_ids || !out->pos || !out->sorted_p || !out->ppos)) return MOE_ERR_INVALID_ARG;
+    RouteArgs a{};
+    a.ids = topk_ids;
+    a.N = (int32_t)N;
+    a.E = num_experts;
+    route_caps(N, num_experts, &a.n_pad_cap, &a.tile_cap);
+    a.nb1 = a.nb2 = 0;
+    a.counts = out->counts;
+    a.offsets = out->offsets;
+    a.padded_offsets = out->padded_offsets;
+    a.pos = out->pos;
+    a.sorted_p = out->sorted_p;
+    a.ppos = out->ppos;
+    a.row_src = out->row_src;
+    a.tile_expert = out->tile_expert;
+    a.tile_row0 = out->tile_row0;
+    a.stats = out->stats;
+    if (launch_route(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                        const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream, void* const* events) {
+    if (!dims) return MOE_ERR_INVALID_ARG;
+    if (!dims_ok(dims)) {
+        // shape fields present but outside the envelope
+        if (dims->mode < 0 || dims->mode > 2 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
+            dims->d_hidden <= 0 || dims->d_expert <= 0)
+            return MOE_ERR_INVALID_ARG;
+        return MOE_ERR_UNSUPPORTED;
+    }
+    const int mode = dims->mode;
+    const int64_t T = dims->num_tokens;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_ids || !topk_w || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out) || !aligned16(topk_ids) ||
+        !aligned16(topk_w))
+        return MOE_ERR_INVALID_ARG;
+    if (mode == MOE_MODE_FP8 && (!scales || !scales->x_scale || !scales->w1_scale || !scales->w2_scale))
+        return MOE_ERR_INVALID_ARG;
+    moe_ws_layout L;
+    layout_of(dims, &L);
+    if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
+
+    int cus = 0, occ1 = 1, occ2 = 1;
+    if (device_info(mode, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) -> bool {
+        return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+    };
+    const int32_t E = dims->num_experts, k = dims->top_k, d_h = dims->d_hidden, d_e = dims->d_expert;
+
+    RouteArgs r{};
+    r.ids = topk_ids;
+    r.N = (int32_t)(T * k);
+    r.E = E;
+    r.n_pad_cap = L.n_pad_cap;
+    r.tile_cap = L.tile_cap;
+    r.nb1 = d_e / L.block_n1;
+    r.nb2 = d_h / L.block_n2;
+    r.counts = at<int32_t>(workspace, L.counts);
+    r.offsets = at<int32_t>(workspace, L.offsets);
+    r.padded_offsets = at<int32_t>(workspace, L.padded_offsets);
+    r.pos = at<int32_t>(workspace, L.pos);
+    r.sorted_p = at<int32_t>(workspace, L.sorted_p);
+    r.ppos = at<int32_t>(workspace, L.ppos);
+    r.row_src = at<int32_t>(workspace, L.row_src);
+    r.tile_expert = at<int32_t>(workspace, L.tile_expert);
+    r.tile_row0 = at<int32_t>(workspace, L.tile_row0);
+    r.stats = at<int32_t>(workspace, L.stats);
+    r.tasks1 = at<int4>(workspace, L.tasks1);
+    r.tasks2 = at<int4>(workspace, L.tasks2);
+    if (!mark(0) || launch_route(r, s) != hipSuccess) return MOE_ERR_HIP;
+
+    Gemm1Args g1{};
+    g1.x = x;
+    g1.x_scale = mode == MOE_MODE_FP8 ? scales->x_scale : nullptr;
+    g1.w1 = w1;
+    g1.w1_scale = mode == MOE_MODE_FP8 ? scales->w1_scale : nullptr;
+    g1.row_src = r.row_src;
+    g1.tasks = r.tasks1;
+    g1.stats = r.stats;
+    g1.h = at<void>(workspace, L.h);
+    g1.h_scale = mode == MOE_MODE_FP8 ? at<float>(workspace, L.h_scale) : nullptr;
+    g1.k = k;
+    g1.d_h = d_h;
+    g1.d_e = d_e;
+    const int64_t grid1 = std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1);
+    if (!mark(1) || launch_gemm1(mode, g1, (int)std::max<int64_t>(grid1, 1), s) != hipSuccess) return MOE_ERR_HIP;
+
+    Gemm2Args g2{};
+    g2.h = g1.h;
+    g2.h_scale = g1.h_scale;
+    g2.w2 = w2;
+    g2.w2_scale = mode == MOE_MODE_FP8 ? scales->w2_scale : nullptr;
+    g2.row_src = r.row_src;
+    g2.topk_w = topk_w;
+    g2.tasks = r.tasks2;
+    g2.stats = r.stats;
+    g2.y = at<void>(workspace, L.y);
+    g2.d_h = d_h;
+    g2.d_e = d_e;
+    const int64_t grid2 = std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2);
+    if (!mark(2) || launch_gemm2(mode, g2, (int)std::max<int64_t>(grid2, 1), s) != hipSuccess) return MOE_ERR_HIP;
+
+    CombineArgs c{};
+    c.y = g2.y;
+    c.ids = topk_ids;
+    c.out = out;
+    c.T = (int32_t)T;
+    c.k = k;
+    c.E = E;
+    c.d_h = d_h;
+    if (!mark(3) || launch_combine(mode, c, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_fused_forward(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                      const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    return forward_impl(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,
+                        nullptr);
+}
+
+int moe_fused_forward_profiled(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                               const void* w1, const void* w2, const moe_scales* scales, void* out,
+                               void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
+    if (!events) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (!events[i]) return MOE_ERR_INVALID_ARG;
+    return forward_impl(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,
+                        events);
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Internal declarations shared by the HIP translation units of the fused MoE
+// library (kernels and the C-ABI host code).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_fused.h"
+
+namespace moe {
+
+// Rows per group block.  Equal to the M size of the 16x16 MFMA tiles, so a
+// cold expert with a handful of tokens pads to at most 15 rows.
+constexpr int kBlockM = 16;
+// A GEMM task covers up to this many consecutive group blocks of one expert
+// (64 rows); the kernels carry one fully unrolled body per block count.
+constexpr int kMaxRowBlocks = 4;
+// Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.
+constexpr int kGemmWaves = 4;
+constexpr int kGemmThreads = 64 * kGemmWaves;
+// Routing runs in one workgroup of 16 waves.
+constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kMaxExperts = 256;
+constexpr int kQ = 128;  // FP8 block-scale granularity
+
+// stats[] slots in the workspace
+enum { kStatDropped = 0, kStatTiles, kStatPadRows, kStatTasks1, kStatTasks2, kStatCounter1, kStatCounter2, kStatCount = 8 };
+
+// Columns of the intermediate per GEMM-1 task and of the output per GEMM-2 task.
+// FP8 mode needs 128 so that one task owns a whole 128-column requantisation
+// group (GEMM-1) and a single weight-scale block row (both GEMMs).
+inline int gemm1_block_n(int mode) { return mode == MOE_MODE_FP8 ? 128 : 64; }
+inline int gemm2_block_n(int mode) { return mode == MOE_MODE_FP8 ? 128 : 64; }
+
+struct RouteArgs {
+    const int32_t* ids;
+    int32_t N, E;
+    int64_t n_pad_cap, tile_cap;
+    int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
+    int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;
+    int32_t* stats;
+    int4* tasks1;
+    int4* tasks2;
+};
+
+struct Gemm1Args {
+    const void* x;
+    const float* x_scale;
+    const void* w1;
+    const float* w1_scale;
+    const int32_t* row_src;
+    const int4* tasks;
+    int32_t* stats;
+    void* h;
+    float* h_scale;
+    int32_t k, d_h, d_e;
+};
+
+struct Gemm2Args {
+    const void* h;
+    const float* h_scale;
+    const void* w2;
+    const float* w2_scale;
+    const int32_t* row_src;
+    const float* topk_w;
+    const int4* tasks;
+    int32_t* stats;
+    void* y;
+    int32_t d_h, d_e;
+};
+
+struct CombineArgs {
+    const void* y;
+    const int32_t* ids;
+    void* out;
+    int32_t T, k, E, d_h;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s);
+hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s);
+hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s);
+// Resident workgroups per CU of the persistent GEMM kernels (occupancy query).
+hipError_t gemm_occupancy(int mode, int* g1_blocks_per_cu, int* g2_blocks_per_cu);
+
+}  // namespace moe

@@ -1,0 +1,48 @@
+"""Move a synthetic workload (numpy, from ``workloads``) into device tensors and
+run the layer on it.  Marshalling only."""
+from __future__ import annotations
+
+import numpy as np
+
+from . import moe
+from .workloads import MODE_BF16, MODE_F32ACT, MODE_FP8, MoEWorkload
+
+
+def upload(w: MoEWorkload, device="cuda:0") -> dict:
+    import torch
+
+    def t(a, dt=None):
+        r = torch.from_numpy(np.ascontiguousarray(a)).to(device)
+        return r if dt is None else r.view(dt)
+
+    d = {"mode": w.mode}
+    if w.mode == MODE_F32ACT:
+        d["x"] = t(w.x)
+    elif w.mode == MODE_BF16:
+        d["x"] = t(w.x.view(np.int16), torch.bfloat16)
+    else:
+        d["x"] = t(w.x, torch.float8_e4m3fn)
+    if w.mode == MODE_FP8:
+        d["w1"] = t(w.w1, torch.float8_e4m3fn)
+        d["w2"] = t(w.w2, torch.float8_e4m3fn)
+        d["x_scale"] = t(w.x_scale)
+        d["w1_scale"] = t(w.w1_scale)
+        d["w2_scale"] = t(w.w2_scale)
+    else:
+        d["w1"] = t(w.w1.view(np.int16), torch.bfloat16)
+        d["w2"] = t(w.w2.view(np.int16), torch.bfloat16)
+        d["x_scale"] = d["w1_scale"] = d["w2_scale"] = None
+    d["topk_ids"] = t(w.topk_ids.astype(np.int32))
+    d["topk_w"] = t(w.topk_w.astype(np.float32))
+    return d
+
+
+def run(d: dict, out=None, workspace=None, stream=None, events=None):
+    return moe.fused_forward(d["x"], d["topk_ids"], d["topk_w"], d["w1"], d["w2"], out=out, x_scale=d["x_scale"],
+                             w1_scale=d["w1_scale"], w2_scale=d["w2_scale"], workspace=workspace, stream=stream,
+                             events=events)
+
+
+def out_to_f64(out) -> np.ndarray:
+    import torch
+    return out.float().cpu().numpy().astype(np.float64)

@@ -1,0 +1,212 @@
+"""Thin Python binding of ``libmoe_fused.so`` (the C ABI in include/moe_fused.h).
+
+The functions with the C names marshal arguments and call the library; every
+step of the layer runs in the HIP kernels.  ``fused_forward`` is a torch
+convenience on top: it derives the dims from tensor shapes, checks dtypes, keeps
+a workspace tensor per device and passes ``data_ptr()`` values and the current
+stream.  There is no fallback: if the library is missing, loading fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_fused.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe_fused.h")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+MOE_MODE_F32ACT = 0
+MOE_MODE_BF16 = 1
+MOE_MODE_FP8 = 2
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_expert", ctypes.c_int32)]
+
+
+class moe_scales(ctypes.Structure):
+    _fields_ = [("x_scale", ctypes.c_void_p), ("w1_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+
+
+class moe_route_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("counts", "offsets", "padded_offsets", "pos", "sorted_p", "ppos",
+                                                "row_src", "tile_expert", "tile_row0", "stats")]
+
+
+class moe_ws_layout(ctypes.Structure):
+    _fields_ = ([(n, ctypes.c_size_t) for n in ("counts", "offsets", "padded_offsets", "pos", "sorted_p", "ppos",
+                                                 "row_src", "tile_expert", "tile_row0", "stats", "tasks1", "tasks2",
+                                                 "h", "h_scale", "y", "total")]
+                + [(n, ctypes.c_int64) for n in ("n_pad_cap", "tile_cap", "task1_cap", "task2_cap")]
+                + [(n, ctypes.c_int32) for n in ("block_n1", "block_n2", "max_row_blocks")])
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where} failed: {moe_error_string(code)} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m skew_aware_grouped_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    L.moe_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_workspace_bytes.argtypes = [P(moe_dims)]
+    L.moe_fused_forward.restype = ctypes.c_int
+    L.moe_fused_forward.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, P(moe_scales), vp, vp, ctypes.c_size_t, vp]
+    L.moe_fused_forward_profiled.restype = ctypes.c_int
+    L.moe_fused_forward_profiled.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, P(moe_scales), vp, vp,
+                                             ctypes.c_size_t, vp, P(vp)]
+    L.moe_block_m.restype = ctypes.c_int32
+    L.moe_block_m.argtypes = []
+    L.moe_route_caps.restype = ctypes.c_int
+    L.moe_route_caps.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P(ctypes.c_int64),
+                                 P(ctypes.c_int64)]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_route.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, P(moe_route_out), vp]
+    L.moe_workspace_layout.restype = ctypes.c_int
+    L.moe_workspace_layout.argtypes = [P(moe_dims), P(moe_ws_layout)]
+    L.moe_error_string.restype = ctypes.c_char_p
+    L.moe_error_string.argtypes = [ctypes.c_int]
+    _lib = L
+    return L
+
+
+def header_symbols() -> list:
+    """Names of the entry points the public header declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+# ------------------------------------------------------------- C entry points
+def moe_workspace_bytes(dims: moe_dims) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(dims)))
+
+
+def moe_fused_forward(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream) -> int:
+    return int(lib().moe_fused_forward(ctypes.byref(dims) if dims is not None else None, x, topk_ids, topk_w, w1,
+                                       w2, ctypes.byref(scales) if scales is not None else None, out, workspace,
+                                       workspace_bytes, stream))
+
+
+def moe_fused_forward_profiled(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,
+                               events) -> int:
+    ev = (ctypes.c_void_p * 5)(*events) if events is not None else None
+    return int(lib().moe_fused_forward_profiled(ctypes.byref(dims), x, topk_ids, topk_w, w1, w2,
+                                                ctypes.byref(scales) if scales is not None else None, out,
+                                                workspace, workspace_bytes, stream, ev))
+
+
+def moe_block_m() -> int:
+    return int(lib().moe_block_m())
+
+
+def moe_route_caps(num_tokens: int, top_k: int, num_experts: int):
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib().moe_route_caps(num_tokens, top_k, num_experts, ctypes.byref(a), ctypes.byref(b))
+    if rc:
+        raise MoEError(rc, "moe_route_caps")
+    return a.value, b.value
+
+
+def moe_route(num_tokens, top_k, num_experts, topk_ids, out: moe_route_out, stream) -> int:
+    return int(lib().moe_route(num_tokens, top_k, num_experts, topk_ids, ctypes.byref(out), stream))
+
+
+def moe_workspace_layout(dims: moe_dims) -> moe_ws_layout:
+    L = moe_ws_layout()
+    rc = lib().moe_workspace_layout(ctypes.byref(dims), ctypes.byref(L))
+    if rc:
+        raise MoEError(rc, "moe_workspace_layout")
+    return L
+
+
+def moe_error_string(code: int) -> str:
+    return lib().moe_error_string(code).decode()
+
+
+# ------------------------------------------------------------ torch helpers
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _mode_of(x, w1):
+    import torch
+    if w1.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return MOE_MODE_FP8
+    if x.dtype == torch.float32:
+        return MOE_MODE_F32ACT
+    return MOE_MODE_BF16
+
+
+_workspaces = {}
+
+
+def workspace_for(dims: moe_dims, device):
+    """A cached uint8 workspace tensor large enough for ``dims`` on ``device``."""
+    import torch
+    need = moe_workspace_bytes(dims)
+    key = (str(device),)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def make_dims(x, topk_ids, w1, mode: Optional[int] = None) -> moe_dims:
+    T, d_h = x.shape
+    E, two_de, d_h2 = w1.shape
+    assert d_h2 == d_h and two_de % 2 == 0, "w1 must be [E, 2*d_expert, d_hidden]"
+    return moe_dims(mode=_mode_of(x, w1) if mode is None else mode, num_tokens=T, num_experts=E,
+                    top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2)
+
+
+def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=None, w2_scale=None,
+                  workspace=None, stream=None, events=None):
+    """Run ``moe_fused_forward`` on torch device tensors; returns ``out``.  With
+    ``events`` (5 torch.cuda.Event objects) the stage-timing variant is used."""
+    import torch
+    dims = make_dims(x, topk_ids, w1)
+    if out is None:
+        odt = torch.float32 if dims.mode == MOE_MODE_F32ACT else torch.bfloat16
+        out = torch.empty(x.shape[0], x.shape[1], dtype=odt, device=x.device)
+    for name, t in (("x", x), ("topk_ids", topk_ids), ("topk_w", topk_w), ("w1", w1), ("w2", w2), ("out", out)):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if topk_ids.dtype != torch.int32 or topk_w.dtype != torch.float32:
+        raise ValueError("topk_ids must be int32 and topk_w float32")
+    scales = None
+    if dims.mode == MOE_MODE_FP8:
+        scales = moe_scales(x_scale.data_ptr(), w1_scale.data_ptr(), w2_scale.data_ptr())
+    ws = workspace if workspace is not None else workspace_for(dims, x.device)
+    args = (dims, x.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w1.data_ptr(), w2.data_ptr(), scales,
+            out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    if events is None:
+        rc = moe_fused_forward(*args)
+    else:
+        rc = moe_fused_forward_profiled(*args, [e.cuda_event for e in events])
+    if rc:
+        raise MoEError(rc, "moe_fused_forward")
+    return out

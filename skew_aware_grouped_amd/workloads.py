@@ -190,18 +190,11 @@ def make_routing(index, T, E, k, routing):
     raise ValueError(kind)
 
 
-def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) -> MoEWorkload:
-    if mode == MODE_FP8:
-        assert d_h % QBLK == 0 and d_e % QBLK == 0
-    ids = make_routing(index, T, E, k, routing) if topk_ids is None else np.asarray(topk_ids, np.int32)
-    lg = _rng(index, STREAM_LOGITS).standard_normal((T, k))
-    ex = np.exp(lg - lg.max(axis=1, keepdims=True))
-    tw = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
-
-    xf = _rng(index, STREAM_X).standard_normal((T, d_h), dtype=np.float32)
+@functools.lru_cache(maxsize=2)
+def _weights(index, E, d_h, d_e, mode):
+    """Expert weights of one recipe; shared by every token count of that recipe."""
     r1, r2 = _rng(index, STREAM_W1), _rng(index, STREAM_W2)
     s1, s2 = np.float32(1.0 / np.sqrt(d_h)), np.float32(1.0 / np.sqrt(d_e))
-    w1_scale = w2_scale = x_scale = None
     if mode == MODE_FP8:
         w1 = np.empty((E, 2 * d_e, d_h), np.uint8)
         w2 = np.empty((E, d_h, d_e), np.uint8)
@@ -211,17 +204,32 @@ def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) 
             w1[e], w1_scale[e] = quantize_blocks(r1.standard_normal((2 * d_e, d_h), dtype=np.float32) * s1)
         for e in range(E):
             w2[e], w2_scale[e] = quantize_blocks(r2.standard_normal((d_h, d_e), dtype=np.float32) * s2)
+        return w1, w2, w1_scale, w2_scale
+    w1 = np.stack([to_bf16_bits(r1.standard_normal((2 * d_e, d_h), dtype=np.float32) * s1) for _ in range(E)])
+    w2 = np.stack([to_bf16_bits(r2.standard_normal((d_h, d_e), dtype=np.float32) * s2) for _ in range(E)])
+    return w1, w2, None, None
+
+
+def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) -> MoEWorkload:
+    if mode == MODE_FP8:
+        assert d_h % QBLK == 0 and d_e % QBLK == 0
+    ids = make_routing(index, T, E, k, routing) if topk_ids is None else np.asarray(topk_ids, np.int32)
+    lg = _rng(index, STREAM_LOGITS).standard_normal((T, k))
+    ex = np.exp(lg - lg.max(axis=1, keepdims=True))
+    tw = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    xf = _rng(index, STREAM_X).standard_normal((T, d_h), dtype=np.float32)
+    w1, w2, w1_scale, w2_scale = _weights(index, E, d_h, d_e, mode)
+    x_scale = None
+    if mode == MODE_FP8:
         x, x_scale = quantize_rows(xf)
     else:
-        w1 = np.stack([to_bf16_bits(r1.standard_normal((2 * d_e, d_h), dtype=np.float32) * s1) for _ in range(E)])
-        w2 = np.stack([to_bf16_bits(r2.standard_normal((d_h, d_e), dtype=np.float32) * s2) for _ in range(E)])
         x = xf if mode == MODE_F32ACT else to_bf16_bits(xf)
     return MoEWorkload(name=name, mode=mode, T=T, E=E, k=k, d_h=d_h, d_e=d_e, x=x, topk_ids=ids, topk_w=tw,
                        w1=w1, w2=w2, x_scale=x_scale, w1_scale=w1_scale, w2_scale=w2_scale,
                        meta={"index": index, "routing": routing})
 
 
-@functools.lru_cache(maxsize=4)
+@functools.lru_cache(maxsize=2)
 def config(name: str) -> MoEWorkload:
     c = dict(CONFIGS[name])
     return make_workload(name=name, **c)

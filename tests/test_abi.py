@@ -1,0 +1,80 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry
+point, and its host-side logic (sizes, layout, argument checks) behaves as the
+header states.  No call here touches a GPU."""
+import ctypes
+
+import pytest
+
+from skew_aware_grouped_amd import moe
+
+
+def test_library_exports_every_header_symbol():
+    L = moe.lib()
+    names = moe.header_symbols()
+    assert set(names) >= {"moe_fused_forward", "moe_route", "moe_workspace_bytes", "moe_block_m",
+                          "moe_route_caps", "moe_workspace_layout", "moe_error_string"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_block_m_and_caps():
+    assert moe.moe_block_m() == 16
+    assert moe.moe_route_caps(1024, 2, 32) == (2048 + 32 * 15, (2048 + 32 * 15) // 16)
+    assert moe.moe_route_caps(1, 2, 32) == (2 + 2 * 15, 2)
+
+
+def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048):
+    return moe.moe_dims(mode=mode, num_tokens=T, num_experts=E, top_k=k, d_hidden=d_h, d_expert=d_e)
+
+
+def test_workspace_layout_is_disjoint_and_aligned():
+    for mode in (0, 1, 2):
+        d = _dims(mode=mode)
+        L = moe.moe_workspace_layout(d)
+        offs = [L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.tile_expert,
+                L.tile_row0, L.stats, L.tasks1, L.tasks2, L.h, L.h_scale, L.y, L.total]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+        N = 2048
+        assert L.pos - L.ppos <= 0 and L.sorted_p - L.pos >= 4 * N
+        assert L.y + (4 if mode == 0 else 2) * N * 7168 <= L.total
+        assert moe.moe_workspace_bytes(d) == L.total
+
+
+def test_invalid_dims_rejected():
+    assert moe.moe_workspace_bytes(_dims(d_h=100)) == 0
+    assert moe.moe_workspace_bytes(_dims(E=0)) == 0
+    assert moe.moe_workspace_bytes(_dims(k=9)) == 0
+    assert moe.moe_workspace_bytes(_dims(mode=3)) == 0
+
+
+def test_forward_argument_errors_without_gpu():
+    p = 1 << 20  # fake, 256-aligned, never dereferenced: checks run before any launch
+    big = 1 << 40
+    args = dict(x=p, topk_ids=p, topk_w=p, w1=p, w2=p, out=p, workspace=p)
+    sc = moe.moe_scales(p, p, p)
+
+    def call(dims, scales=sc, ws_bytes=big, **over):
+        a = {**args, **over}
+        return moe.moe_fused_forward(dims, a["x"], a["topk_ids"], a["topk_w"], a["w1"], a["w2"], scales, a["out"],
+                                     a["workspace"], ws_bytes, None)
+
+    assert call(None) == moe.MOE_ERR_INVALID_ARG
+    assert call(_dims(mode=5)) == moe.MOE_ERR_INVALID_ARG
+    assert call(_dims(d_h=100)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(_dims(E=300)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(_dims(T=0)) == moe.MOE_OK  # empty batch: nothing to do
+    assert call(_dims(), x=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(_dims(), x=p + 4) == moe.MOE_ERR_INVALID_ARG  # misaligned
+    assert call(_dims(), scales=None) == moe.MOE_ERR_INVALID_ARG  # FP8 needs scales
+    assert call(_dims(), ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    assert call(_dims(), workspace=None) == moe.MOE_ERR_WORKSPACE
+    assert call(_dims(), workspace=p + 64) == moe.MOE_ERR_WORKSPACE  # workspace must be 256-aligned
+    for c in range(5):
+        assert moe.moe_error_string(c) != "unknown error"
+
+
+def test_route_argument_errors_without_gpu():
+    out = moe.moe_route_out()
+    assert moe.moe_route(4, 2, 0, 1 << 20, out, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_route(4, 9, 4, 1 << 20, out, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_route(4, 2, 4, 1 << 20, out, None) == moe.MOE_ERR_INVALID_ARG  # null outputs
