@@ -162,7 +162,7 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
  * Returns MOE_ERR_INVALID_ARG for invalid dims. */
 typedef struct {
     size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, tile_expert, tile_row0, stats;
-    size_t tasks1, tasks2, h, h_scale, y, total;
+    size_t tasks1, tasks2, h, h_scale, y, zero, x_bf16, total;
     int64_t n_pad_cap, tile_cap, task1_cap, task2_cap;
     int32_t block_n1, block_n2, max_row_blocks;
 } moe_ws_layout;

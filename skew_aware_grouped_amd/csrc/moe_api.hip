@@ -61,6 +61,9 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     L->h = take(hb * L->n_pad_cap * d->d_expert);
     L->h_scale = take(d->mode == MOE_MODE_FP8 ? 4 * L->n_pad_cap * (d->d_expert / kQ) : 0);
     L->y = take(yb * N * d->d_hidden);
+    L->zero = take(kZeroBytes);
+    // F32ACT: x rounded to bf16 once, then the bf16 GEMMs run on it
+    L->x_bf16 = take(d->mode == MOE_MODE_F32ACT ? 2 * (size_t)d->num_tokens * d->d_hidden : 0);
     L->total = o;
 }
 
@@ -223,16 +226,24 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.stats = at<int32_t>(workspace, L.stats);
     r.tasks1 = at<int4>(workspace, L.tasks1);
     r.tasks2 = at<int4>(workspace, L.tasks2);
+    r.zero = at<unsigned char>(workspace, L.zero);
     if (!mark(0) || launch_route(r, s) != hipSuccess) return MOE_ERR_HIP;
+    const void* xg = x;
+    if (mode == MOE_MODE_F32ACT) {
+        uint16_t* xb = at<uint16_t>(workspace, L.x_bf16);
+        if (launch_x_to_bf16(static_cast<const float*>(x), xb, T * d_h, s) != hipSuccess) return MOE_ERR_HIP;
+        xg = xb;
+    }
 
     Gemm1Args g1{};
-    g1.x = x;
+    g1.x = xg;
     g1.x_scale = mode == MOE_MODE_FP8 ? scales->x_scale : nullptr;
     g1.w1 = w1;
     g1.w1_scale = mode == MOE_MODE_FP8 ? scales->w1_scale : nullptr;
     g1.row_src = r.row_src;
     g1.tasks = r.tasks1;
     g1.stats = r.stats;
+    g1.zero = r.zero;
     g1.h = at<void>(workspace, L.h);
     g1.h_scale = mode == MOE_MODE_FP8 ? at<float>(workspace, L.h_scale) : nullptr;
     g1.k = k;
@@ -250,6 +261,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.topk_w = topk_w;
     g2.tasks = r.tasks2;
     g2.stats = r.stats;
+    g2.zero = r.zero;
     g2.y = at<void>(workspace, L.y);
     g2.d_h = d_h;
     g2.d_e = d_e;

@@ -14,86 +14,119 @@
 // with one atomic counter, so a hot expert's many tasks spread over all CUs
 // while empty experts contribute none.
 //
-// Tile mapping (16x16 MFMA, wave64): lane l holds A row (l % 16) and B row
-// (l % 16) with a K slice chosen by (l / 16); the accumulator element i of
-// lane l is C[4*(l/16) + i][l % 16].  A and B use the same K slice per lane,
-// so any per-lane K assignment is a valid split of the reduction.  The gate
-// and up accumulators of one output column sit in the same lane, so SwiGLU
-// needs no data movement.
+// Data movement.  Outside the hot expert of the largest batches these GEMMs
+// stream weights: every weight byte is used by at most a few dozen rows.  So
+// each K block (128 bytes of every operand row: 128 FP8 or 64 bf16 values)
+// moves from HBM straight into LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4: 64 lanes x 16 B land contiguously), in a ring of
+// kStages stages per workgroup.  A wave instruction covers 8 rows x 128 B, so
+// HBM sees full 128-byte lines, and tens of KB per CU stay in flight without
+// costing registers.  Routed token rows are gathered the same way, each lane
+// reading its row through row_src.  In LDS a row's eight 16-byte chunks are
+// XOR-swizzled by (row & 7) so the operand reads below hit distinct banks.
+//
+// MFMA tile mapping (16x16, wave64): lane l reads A row (l % 16) and B row
+// (l % 16); the K slice of a lane is chunks {g, g+4} of the 128-byte block,
+// g = l / 16 (FP8: 32 of the block's 128 values; bf16: chunk g for the first
+// 16x16x32 MFMA and g+4 for the second).  A and B use the same slices, so
+// each MFMA sums over whole K blocks.  The accumulator element i of lane l is
+// C[4*(l/16) + i][l % 16]; the gate and up accumulators of one output column
+// sit in the same lane, so SwiGLU needs no data movement.
 //
 // FP8 (E4M3FN): one 16x16x128 MFMA covers exactly one 128-wide scale block
-// of K, so each MFMA starts from zero and its result is promoted into the fp32
-// accumulator with (row scale of x or h) * (block scale of W) -- the block
-// dequantisation happens in registers.  bf16: 16x16x32 MFMA, accumulating
-// directly.
+// of K, so it starts from zero and its result is promoted into the fp32
+// accumulator with (row scale of x or h) * (block scale of W): the block
+// dequantisation happens in registers.  The row and block scales of each K
+// block ride in the same LDS stage as the operands.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef unsigned short v8u16 __attribute__((ext_vector_type(8)));
+
+constexpr int kRowBytes = 128;                  // bytes of one operand row per stage
+constexpr int kAMaxRows = 16 * kMaxRowBlocks;  // rows of the A tile
+
+// s_waitcnt immediate that waits for vmcnt <= n and nothing else (gfx9 encoding)
+template <int N>
+struct VmCnt {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    static constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+};
+
+template <int L, int R>
+__device__ __forceinline__ void wait_vm_stages(int rem) {
+    // wait until at most rem stages (L loads each) of this wave are in flight
+    if constexpr (R > 0) {
+        if (rem >= R) {
+            __builtin_amdgcn_s_waitcnt(VmCnt<L * R>::imm);
+            return;
+        }
+        wait_vm_stages<L, R - 1>(rem);
+    } else {
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+    }
+}
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0 (no MX scaling)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
-__device__ __forceinline__ v4f mfma_bf16(const v8bf& a, const v8bf& b, const v4f& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ v4f mfma_bf16(const v4i& a, const v4i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0,
+                                                   0, 0);
 }
 
 // binary32 -> bfloat16 bits, round to nearest even (values here are finite)
-__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+__device__ __forceinline__ unsigned f32_to_bf16(float f) {
     unsigned u = __float_as_uint(f);
     u += 0x7FFFu + ((u >> 16) & 1u);
-    return (unsigned short)(u >> 16);
+    return u >> 16;
 }
 
 // binary32 -> E4M3FN code via the hardware converter (round to nearest even)
-__device__ __forceinline__ unsigned char f32_to_e4m3(float f) {
-    return (unsigned char)(__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false) & 0xff);
+__device__ __forceinline__ unsigned f32_to_e4m3(float f) {
+    return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false) & 0xffu;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
-__device__ __forceinline__ v8i ld32(const unsigned char* p) { return *reinterpret_cast<const v8i*>(p); }
-
-// 16 bf16 values (32 bytes) split in two MFMA operands
-struct Bf16x16 {
-    v8bf lo, hi;
-};
-
-__device__ __forceinline__ Bf16x16 ld_bf16x16(const unsigned short* p) {
-    const v8i raw = *reinterpret_cast<const v8i*>(p);
-    Bf16x16 r;
-    __builtin_memcpy(&r, &raw, 32);
-    return r;
+// Direct-to-LDS loads: lane l's 16 (or 4) bytes from its own global address
+// land at LDS byte offset lds + 16*l (or 4*l); lds must be wave-uniform (it
+// goes to M0).  Issued from inline asm so that the compiler does not treat
+// every later LDS read as possibly aliasing an in-flight load (it would wait
+// for all loads, which serialises the ring); the kernel tracks completion
+// itself with s_waitcnt vmcnt.  Vector-memory loads complete in issue order,
+// so loads the compiler does not see can only make its own waits stricter.
+__device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void g2l4(const void* g, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 
-__device__ __forceinline__ Bf16x16 ld_f32x16_as_bf16(const float* p) {
-    const float4* q = reinterpret_cast<const float4*>(p);
-    unsigned short b[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float4 v = q[i];
-        b[4 * i + 0] = f32_to_bf16(v.x);
-        b[4 * i + 1] = f32_to_bf16(v.y);
-        b[4 * i + 2] = f32_to_bf16(v.z);
-        b[4 * i + 3] = f32_to_bf16(v.w);
-    }
-    Bf16x16 r;
-    __builtin_memcpy(&r, b, 32);
-    return r;
+__device__ __forceinline__ unsigned lds_offset(const void* p) { return (unsigned)(uintptr_t)p; }
+
+// stage hand-off: every wave has waited for its own loads of the stage; the
+// empty asm keeps the compiler from moving LDS accesses across the barrier
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ Bf16x16 zero_bf16x16() {
-    const v8i z = {0, 0, 0, 0, 0, 0, 0, 0};
-    Bf16x16 r;
-    __builtin_memcpy(&r, &z, 32);
-    return r;
+__device__ __forceinline__ v4i lds16(const unsigned char* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// the 32-byte K slice {chunk g, chunk g+4} of a swizzled 128-byte row
+__device__ __forceinline__ v8i lds_frag32(const unsigned char* row, int g, int swz) {
+    const v4i lo = lds16(row + ((g ^ swz) << 4));
+    const v4i hi = lds16(row + (((g + 4) ^ swz) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 __device__ __forceinline__ int pull_task(int32_t* counter, int* s_slot) {
@@ -104,211 +137,298 @@ __device__ __forceinline__ int pull_task(int32_t* counter, int* s_slot) {
     return t;
 }
 
-// ---------------------------------------------------------------- GEMM-1 FP8
-// Task: 16*NSUB rows x 128 intermediate columns; wave w owns columns
-// [32w, 32w+32) as two 16-column fragments, for both gate and up.
-template <int NSUB>
-__device__ __forceinline__ void gemm1_fp8_task(const Gemm1Args& a, int e, int row0, int cb, float* s_amax) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int d_h = a.d_h, d_e = a.d_e, kq = d_h / kQ;
-    const unsigned char* x = static_cast<const unsigned char*>(a.x);
-    const unsigned char* w1 = static_cast<const unsigned char*>(a.w1);
+// ------------------------------------------------------------------ configs
+template <int MODE, bool GATED>
+struct Cfg {
+    static constexpr bool kFP8 = MODE == MOE_MODE_FP8;
+    static constexpr int kWaves = kGemmWaves;
+    static constexpr int kNFW = (GATED && kFP8) ? 2 : 1;  // 16-column fragments per wave
+    static constexpr int kBN = 16 * kNFW * kWaves;         // output columns per task
+    static constexpr int kBRows = GATED ? 2 * kBN : kBN;   // weight rows per task
+    static constexpr int kBInstr = kBRows / 8 / kWaves;    // B loads per wave per stage
+    static constexpr int kStageB = kBRows * kRowBytes;
+    static constexpr int kStageA = kAMaxRows * kRowBytes;
+    static constexpr int kStageS = kFP8 ? 512 : 0;  // 64 row scales, then the block scale(s)
+    static constexpr int kStage = kStageB + kStageA + kStageS;
+    static constexpr int kStages = (GATED ? 3 : 4);
+    static constexpr int kLds = kStages * kStage;
+    // per-lane epilogue staging: one row of output per tile row, kBN columns
+    static constexpr int kOutBytes = (MODE == MOE_MODE_F32ACT && !GATED) ? 4 : (GATED && kFP8 ? 1 : 2);
+    static constexpr int kEpiRow = kBN * kOutBytes;
+    static_assert(kEpiRow * kAMaxRows + 1024 <= kLds, "epilogue staging must fit in the stage ring");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+};
 
-    const unsigned char* pa[NSUB];
-    bool va[NSUB];
-    const float* psx[NSUB][4];
-    bool vc[NSUB][4];
+template <int NSUB>
+struct ALoad {
+    static constexpr int kRowsPerWave = 16 * NSUB / kGemmWaves;  // 4*NSUB
+    static constexpr int kInstr = (kRowsPerWave * 8 + 63) / 64;
+};
+
+// ------------------------------------------------------------------ kernel
+// One task: rows [row0, row0 + 16*NSUB) of expert e, output column block cb.
+template <int MODE, bool GATED, int NSUB>
+__device__ __forceinline__ void gemm_task(const void* a_base, const float* a_scale, const int32_t* row_src,
+                                          int a_div, const void* wts, const float* w_scale, const unsigned char* zero,
+                                          int e, int row0, int cb, int K, int N_out, int k_top, unsigned char* smem,
+                                          const Gemm1Args* g1, const Gemm2Args* g2) {
+    using C = Cfg<MODE, GATED>;
+    constexpr bool kFP8 = C::kFP8;
+    constexpr int S = C::kStages;
+    constexpr int kAI = ALoad<NSUB>::kInstr;
+    constexpr int L = C::kBInstr + kAI + (kFP8 ? 1 : 0);  // loads per wave per stage
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nk = K / (kFP8 ? 128 : 64);
+    const unsigned smem_lds = lds_offset(smem);
+    const int64_t ld_bytes = (int64_t)K * (kFP8 ? 1 : 2);  // bytes per operand row
+
+    // ---- per-lane load sources (stage 0); a K block advances them by 128 bytes
+    const unsigned char* bsrc[C::kBInstr];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        const int p = a.row_src[row0 + 16 * s + lr];
-        va[s] = p >= 0;
-        pa[s] = x + (int64_t)(p >= 0 ? p / a.k : 0) * d_h + lg * 32;
+    for (int j = 0; j < C::kBInstr; ++j) {
+        const int r = (w * C::kBInstr + j) * 8 + (lane >> 3);  // tile row
+        const int c = (lane & 7) ^ (r & 7);
+        int64_t wrow;
+        if constexpr (GATED)
+            wrow = r < C::kBN ? (int64_t)cb * C::kBN + r : (int64_t)N_out + (int64_t)cb * C::kBN + (r - C::kBN);
+        else
+            wrow = (int64_t)cb * C::kBN + r;
+        const int64_t rows_per_expert = GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
+        bsrc[j] = static_cast<const unsigned char*>(wts) + ((int64_t)e * rows_per_expert + wrow) * ld_bytes + c * 16;
+    }
+    const unsigned char* asrc[kAI];
+    bool aon[kAI], apad[kAI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int pc = a.row_src[row0 + 16 * s + 4 * lg + i];
-            vc[s][i] = pc >= 0;
-            psx[s][i] = a.x_scale + (int64_t)(pc >= 0 ? pc / a.k : 0) * kq;
+    for (int j = 0; j < kAI; ++j) {
+        const int rl = j * 8 + (lane >> 3);
+        const int r = w * ALoad<NSUB>::kRowsPerWave + rl;
+        const int c = (lane & 7) ^ (r & 7);
+        aon[j] = rl < ALoad<NSUB>::kRowsPerWave;
+        int p = aon[j] ? row_src[row0 + r] : -1;
+        apad[j] = p < 0;
+        const int64_t arow = GATED ? (p >= 0 ? p / a_div : 0) : (int64_t)(row0 + r);
+        if (!GATED) apad[j] = false;  // GEMM-2 reads its own padded rows (zeros from GEMM-1)
+        asrc[j] = apad[j] ? zero + c * 16
+                          : static_cast<const unsigned char*>(a_base) + arow * ld_bytes + c * 16;
+    }
+    // scale sources: lanes 0..15 of wave w -> row scale of tile row 16w + lane;
+    // wave 3 lanes 16 (and 17) -> block scale(s) of W for this K block
+    const float* ssrc = nullptr;
+    bool son = false, spad = false;
+    if constexpr (kFP8) {
+        const int kq = K / kQ;
+        if (lane < 16) {
+            const int r = 16 * w + lane;
+            son = r < 16 * NSUB;
+            if (son) {
+                const int p = row_src[row0 + r];
+                if (GATED) {
+                    spad = p < 0;
+                    ssrc = spad ? reinterpret_cast<const float*>(zero) : a_scale + (int64_t)(p / a_div) * kq;
+                } else {
+                    ssrc = a_scale + (int64_t)(row0 + r) * kq;
+                }
+            }
+        } else if (w == kGemmWaves - 1 && lane < (GATED ? 18 : 17)) {
+            son = true;
+            // W1 scales [E][2 d_e/128][d_h/128]: gate block row cb, up block row d_e/128 + cb
+            // W2 scales [E][d_h/128][d_e/128]: block row (cb*64)/128
+            const int64_t nrb = GATED ? 2 * (int64_t)N_out / kQ : (int64_t)N_out / kQ;
+            const int64_t brow = GATED ? (lane == 16 ? cb : N_out / kQ + cb) : (int64_t)cb * C::kBN / kQ;
+            ssrc = w_scale + ((int64_t)e * nrb + brow) * kq;
         }
     }
-    const unsigned char* pg[2];
-    const unsigned char* pu[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const int row = cb * 128 + w * 32 + 16 * f + lr;
-        pg[f] = w1 + ((int64_t)e * 2 * d_e + row) * d_h + lg * 32;
-        pu[f] = pg[f] + (int64_t)d_e * d_h;
-    }
-    const float* psg = a.w1_scale + ((int64_t)e * (2 * d_e / kQ) + cb) * kq;
-    const float* psu = psg + (int64_t)(d_e / kQ) * kq;
 
-    v4f accg[NSUB][2], accu[NSUB][2];
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    auto issue = [&](int kc) {
+        const unsigned st = smem_lds + (unsigned)((kc % S) * C::kStage);
+        const int64_t koff = (int64_t)kc * kRowBytes;
+#pragma unroll
+        for (int j = 0; j < C::kBInstr; ++j) g2l16(bsrc[j] + koff, st + (unsigned)((w * C::kBInstr + j) * 1024));
+#pragma unroll
+        for (int j = 0; j < kAI; ++j) {
+            if (aon[j])
+                g2l16(apad[j] ? asrc[j] : asrc[j] + koff,
+                      st + (unsigned)(C::kStageB + (w * ALoad<NSUB>::kRowsPerWave + j * 8) * kRowBytes));
+        }
+        if constexpr (kFP8) {
+            if (son) g2l4(spad ? ssrc : ssrc + kc, st + (unsigned)(C::kStageB + C::kStageA + w * 64));
+        }
+    };
+
+    v4f acc[NSUB][C::kNFW][GATED ? 2 : 1];
+    const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-        for (int f = 0; f < 2; ++f) accg[s][f] = accu[s][f] = zero;
+        for (int f = 0; f < C::kNFW; ++f)
+#pragma unroll
+            for (int q = 0; q < (GATED ? 2 : 1); ++q) acc[s][f][q] = zero4;
 
-    const v8i vz = {0, 0, 0, 0, 0, 0, 0, 0};
-    v8i A[NSUB], BG[2], BU[2];
+    const int swz = lr & 7;
+    const int npro = nk < S - 1 ? nk : S - 1;
+    for (int kc = 0; kc < npro; ++kc) issue(kc);
+    for (int kc = 0; kc < nk; ++kc) {
+        const int rem = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
+        wait_vm_stages<L, S - 2>(rem);
+        stage_barrier();
+        if (kc + S - 1 < nk) issue(kc + S - 1);
+        const unsigned char* st = smem + (kc % S) * C::kStage;
+        const unsigned char* sb = st;
+        const unsigned char* sa = st + C::kStageB;
+        if constexpr (kFP8) {
+            const float* sc = reinterpret_cast<const float*>(st + C::kStageB + C::kStageA);
+            v8i A[NSUB];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) A[s] = va[s] ? ld32(pa[s]) : vz;
+            for (int s = 0; s < NSUB; ++s) A[s] = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
+            float sx[NSUB][4];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        BG[f] = ld32(pg[f]);
-        BU[f] = ld32(pu[f]);
-    }
-    for (int kb = 0; kb < kq; ++kb) {
-        // prefetch the next K block (clamped on the last iteration)
-        const int kn = (kb + 1 < kq ? kb + 1 : kb) * kQ;
-        v8i An[NSUB], BGn[2], BUn[2];
+            for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) An[s] = va[s] ? ld32(pa[s] + kn) : vz;
+                for (int i = 0; i < 4; ++i) sx[s][i] = sc[16 * s + 4 * lg + i];
+            const float swg = sc[64];  // written by lane 16 (and 17) of the last wave
+            const float swu = GATED ? sc[65] : 0.f;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            BGn[f] = ld32(pg[f] + kn);
-            BUn[f] = ld32(pu[f] + kn);
-        }
-        const float sg = psg[kb], su = psu[kb];
-        float sx[NSUB][4];
+            for (int f = 0; f < C::kNFW; ++f) {
+                const int brow = 16 * (C::kNFW * w + f) + lr;
+                const v8i Bg = lds_frag32(sb + brow * kRowBytes, lg, swz);
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s)
+                for (int s = 0; s < NSUB; ++s) {
+                    const v4f t = mfma_fp8(A[s], Bg, zero4);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sx[s][i] = vc[s][i] ? psx[s][i][kb] : 0.f;
+                    for (int i = 0; i < 4; ++i) acc[s][f][0][i] += t[i] * (sx[s][i] * swg);
+                }
+                if constexpr (GATED) {
+                    const v8i Bu = lds_frag32(sb + (C::kBN + brow) * kRowBytes, lg, swz);
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
+                    for (int s = 0; s < NSUB; ++s) {
+                        const v4f t = mfma_fp8(A[s], Bu, zero4);
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const v4f tg = mfma_fp8(A[s], BG[f], zero);
-                const v4f tu = mfma_fp8(A[s], BU[f], zero);
+                        for (int i = 0; i < 4; ++i) acc[s][f][GATED ? 1 : 0][i] += t[i] * (sx[s][i] * swu);
+                    }
+                }
+            }
+        } else {
+            // two 16x16x32 bf16 MFMAs per K block: chunk g, then chunk g+4
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    accg[s][f][i] += tg[i] * (sx[s][i] * sg);
-                    accu[s][f][i] += tu[i] * (sx[s][i] * su);
+            for (int half = 0; half < 2; ++half) {
+                const int ch = ((lg + 4 * half) ^ swz) << 4;
+                v4i A[NSUB];
+#pragma unroll
+                for (int s = 0; s < NSUB; ++s) A[s] = lds16(sa + (16 * s + lr) * kRowBytes + ch);
+#pragma unroll
+                for (int f = 0; f < C::kNFW; ++f) {
+                    const int brow = 16 * (C::kNFW * w + f) + lr;
+                    const v4i Bg = lds16(sb + brow * kRowBytes + ch);
+#pragma unroll
+                    for (int s = 0; s < NSUB; ++s) acc[s][f][0] = mfma_bf16(A[s], Bg, acc[s][f][0]);
+                    if constexpr (GATED) {
+                        const v4i Bu = lds16(sb + (C::kBN + brow) * kRowBytes + ch);
+#pragma unroll
+                        for (int s = 0; s < NSUB; ++s)
+                            acc[s][f][GATED ? 1 : 0] = mfma_bf16(A[s], Bu, acc[s][f][GATED ? 1 : 0]);
+                    }
                 }
             }
         }
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) A[s] = An[s];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            BG[f] = BGn[f];
-            BU[f] = BUn[f];
-        }
     }
 
-    // SwiGLU on the fp32 accumulators, then per-row-per-128 requantisation:
-    // amax over the task's 128 columns (2 fragments x 16 lanes x 4 waves).
-    float hv[NSUB][2][4];
-    float rmax[NSUB][4];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                hv[s][f][i] = silu_mul(accg[s][f][i], accu[s][f][i]);
-                m = fmaxf(m, fabsf(hv[s][f][i]));
-            }
-#pragma unroll
-            for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-            rmax[s][i] = m;
-        }
-    if (lr == 0) {
+    // ---- epilogue: stage the output tile in LDS, then 16-byte row stores
+    __syncthreads();  // every wave is done with the ring
+    unsigned char* stage = smem;                               // [kAMaxRows][kEpiRow]
+    float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * kAMaxRows);  // [waves][64]
+    if constexpr (GATED) {
+        float hv[NSUB][C::kNFW][4];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_amax[w * 64 + s * 16 + 4 * lg + i] = rmax[s][i];
-    }
-    __syncthreads();
-    unsigned char* h = static_cast<unsigned char*>(a.h);
+            for (int f = 0; f < C::kNFW; ++f)
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
+                for (int i = 0; i < 4; ++i) hv[s][f][i] = silu_mul(acc[s][f][0][i], acc[s][f][1][i]);
+        if constexpr (kFP8) {
+            // per-row-per-128 requantisation: amax over the task's 128 columns
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rr = s * 16 + 4 * lg + i;
-            float amax = fmaxf(fmaxf(s_amax[rr], s_amax[64 + rr]), fmaxf(s_amax[128 + rr], s_amax[192 + rr]));
-            const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-            const int64_t prow = row0 + rr;
+            for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-            for (int f = 0; f < 2; ++f)
-                h[prow * d_e + cb * 128 + w * 32 + 16 * f + lr] = f32_to_e4m3(hv[s][f][i] / sc);
-            if (w == 0 && lr == 0) a.h_scale[prow * (d_e / kQ) + cb] = sc;
+                for (int i = 0; i < 4; ++i) {
+                    float m = 0.f;
+#pragma unroll
+                    for (int f = 0; f < C::kNFW; ++f) m = fmaxf(m, fabsf(hv[s][f][i]));
+#pragma unroll
+                    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+                    if (lr == 0) s_amax[w * 64 + 16 * s + 4 * lg + i] = m;
+                }
+            __syncthreads();
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * s + 4 * lg + i;
+                    float amax = s_amax[rr];
+#pragma unroll
+                    for (int ww = 1; ww < kGemmWaves; ++ww) amax = fmaxf(amax, s_amax[ww * 64 + rr]);
+                    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+                    for (int f = 0; f < C::kNFW; ++f)
+                        stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] = (unsigned char)f32_to_e4m3(hv[s][f][i] / sc);
+                    if (w == 0 && lr == 0) g1->h_scale[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
+                }
+        } else {
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * s + 4 * lg + i;
+                    reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[16 * w + lr] =
+                        (unsigned short)f32_to_bf16(hv[s][0][i]);
+                }
         }
-    __syncthreads();
-}
-
-// --------------------------------------------------------------- GEMM-1 bf16
-// Task: 16*NSUB rows x 64 intermediate columns; wave w owns columns [16w, 16w+16).
-template <int NSUB, bool F32X>
-__device__ __forceinline__ void gemm1_bf16_task(const Gemm1Args& a, int e, int row0, int cb) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int d_h = a.d_h, d_e = a.d_e;
-    const unsigned short* w1 = static_cast<const unsigned short*>(a.w1);
-
-    int64_t ao[NSUB];
-    bool va[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        const int p = a.row_src[row0 + 16 * s + lr];
-        va[s] = p >= 0;
-        ao[s] = (int64_t)(p >= 0 ? p / a.k : 0) * d_h + lg * 16;
-    }
-    const int row = cb * 64 + w * 16 + lr;
-    const unsigned short* pg = w1 + ((int64_t)e * 2 * d_e + row) * d_h + lg * 16;
-    const unsigned short* pu = pg + (int64_t)d_e * d_h;
-
-    auto load_a = [&](int s, int k0) -> Bf16x16 {
-        if (!va[s]) return zero_bf16x16();
-        if (F32X) return ld_f32x16_as_bf16(static_cast<const float*>(a.x) + ao[s] + k0);
-        return ld_bf16x16(static_cast<const unsigned short*>(a.x) + ao[s] + k0);
-    };
-
-    v4f accg[NSUB], accu[NSUB];
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) accg[s] = accu[s] = zero;
-
-    const int nk = d_h / 64;
-    Bf16x16 A[NSUB], BG, BU;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) A[s] = load_a(s, 0);
-    BG = ld_bf16x16(pg);
-    BU = ld_bf16x16(pu);
-    for (int kc = 0; kc < nk; ++kc) {
-        const int kn = (kc + 1 < nk ? kc + 1 : kc) * 64;
-        Bf16x16 An[NSUB];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) An[s] = load_a(s, kn);
-        const Bf16x16 BGn = ld_bf16x16(pg + kn);
-        const Bf16x16 BUn = ld_bf16x16(pu + kn);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-            accg[s] = mfma_bf16(A[s].lo, BG.lo, accg[s]);
-            accg[s] = mfma_bf16(A[s].hi, BG.hi, accg[s]);
-            accu[s] = mfma_bf16(A[s].lo, BU.lo, accu[s]);
-            accu[s] = mfma_bf16(A[s].hi, BU.hi, accu[s]);
+        __syncthreads();
+        // h[row0 + r][cb*kBN ...]: kEpiRow bytes per row
+        constexpr int kChunks = C::kEpiRow / 16;
+        unsigned char* h = static_cast<unsigned char*>(g1->h);
+        const int64_t hrow_bytes = (int64_t)N_out * (kFP8 ? 1 : 2);
+        for (int i = threadIdx.x; i < 16 * NSUB * kChunks; i += kGemmThreads) {
+            const int r = i / kChunks, c = i - r * kChunks;
+            *reinterpret_cast<v4i*>(h + (int64_t)(row0 + r) * hrow_bytes + (int64_t)cb * C::kEpiRow + c * 16) =
+                *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
         }
+    } else {
+        constexpr bool kF32 = MODE == MOE_MODE_F32ACT;
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) A[s] = An[s];
-        BG = BGn;
-        BU = BUn;
-    }
-    unsigned short* h = static_cast<unsigned short*>(a.h);
+        for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t prow = row0 + s * 16 + 4 * lg + i;
-            h[prow * d_e + cb * 64 + w * 16 + lr] = f32_to_bf16(silu_mul(accg[s][i], accu[s][i]));
+            for (int i = 0; i < 4; ++i) {
+                const int rr = 16 * s + 4 * lg + i;
+                const int p = row_src[row0 + rr];
+                const float wt = p >= 0 ? g2->topk_w[p] : 0.f;
+                const float v = acc[s][0][0][i] * wt;
+                if constexpr (kF32)
+                    reinterpret_cast<float*>(stage + rr * C::kEpiRow)[16 * w + lr] = v;
+                else
+                    reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[16 * w + lr] =
+                        (unsigned short)f32_to_bf16(v);
+            }
+        __syncthreads();
+        constexpr int kChunks = C::kEpiRow / 16;
+        unsigned char* y = static_cast<unsigned char*>(g2->y);
+        const int64_t yrow_bytes = (int64_t)N_out * C::kOutBytes;
+        for (int i = threadIdx.x; i < 16 * NSUB * kChunks; i += kGemmThreads) {
+            const int r = i / kChunks, c = i - r * kChunks;
+            const int p = row_src[row0 + r];
+            if (p < 0) continue;
+            *reinterpret_cast<v4i*>(y + (int64_t)p * yrow_bytes + (int64_t)cb * C::kEpiRow + c * 16) =
+                *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
         }
+    }
+    __syncthreads();  // the ring is refilled by the next task
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
-    __shared__ float s_amax[kGemmWaves * 64];
+    constexpr int GM = MODE == MOE_MODE_F32ACT ? MOE_MODE_BF16 : MODE;  // x arrives as bf16
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg<GM, true>::kLds];
     __shared__ int s_slot;
     const int ntasks = a.stats[kStatTasks1];
     for (;;) {
@@ -316,152 +436,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
         if (t >= ntasks) break;
         const int4 task = a.tasks[t];
         const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
-        if constexpr (MODE == MOE_MODE_FP8) {
-            switch (nsub) {
-                case 1: gemm1_fp8_task<1>(a, e, row0, cb, s_amax); break;
-                case 2: gemm1_fp8_task<2>(a, e, row0, cb, s_amax); break;
-                case 3: gemm1_fp8_task<3>(a, e, row0, cb, s_amax); break;
-                default: gemm1_fp8_task<4>(a, e, row0, cb, s_amax); break;
-            }
-        } else {
-            constexpr bool F32X = MODE == MOE_MODE_F32ACT;
-            switch (nsub) {
-                case 1: gemm1_bf16_task<1, F32X>(a, e, row0, cb); break;
-                case 2: gemm1_bf16_task<2, F32X>(a, e, row0, cb); break;
-                case 3: gemm1_bf16_task<3, F32X>(a, e, row0, cb); break;
-                default: gemm1_bf16_task<4, F32X>(a, e, row0, cb); break;
-            }
+#define MOE_G1(NS)                                                                                              \
+    gemm_task<GM, true, NS>(a.x, a.x_scale, a.row_src, a.k, a.w1, a.w1_scale, a.zero, e, row0, cb, a.d_h, a.d_e, \
+                            a.k, smem, &a, nullptr)
+        switch (nsub) {
+            case 1: MOE_G1(1); break;
+            case 2: MOE_G1(2); break;
+            case 3: MOE_G1(3); break;
+            default: MOE_G1(4); break;
         }
+#undef MOE_G1
     }
-}
-
-// ---------------------------------------------------------------- GEMM-2 FP8
-// Task: 16*NSUB rows x 128 output columns; wave w owns [32w, 32w+32).
-template <int NSUB, int NF, bool F32OUT>
-__device__ __forceinline__ void store_y(const Gemm2Args& a, const v4f (&acc)[NSUB][2], int row0, int col0, int lg,
-                                        int lr) {
-    const int d_h = a.d_h;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = a.row_src[row0 + 16 * s + 4 * lg + i];
-            if (p < 0) continue;
-            const float wt = a.topk_w[p];
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                const float v = acc[s][f][i] * wt;
-                const int64_t off = (int64_t)p * d_h + col0 + 16 * f + lr;
-                if (F32OUT)
-                    static_cast<float*>(a.y)[off] = v;
-                else
-                    static_cast<unsigned short*>(a.y)[off] = f32_to_bf16(v);
-            }
-        }
-}
-
-template <int NSUB>
-__device__ __forceinline__ void gemm2_fp8_task(const Gemm2Args& a, int e, int row0, int cb) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int d_h = a.d_h, d_e = a.d_e, kq = d_e / kQ;
-    const unsigned char* h = static_cast<const unsigned char*>(a.h);
-    const unsigned char* w2 = static_cast<const unsigned char*>(a.w2);
-
-    const unsigned char* pa[NSUB];
-    const float* psh[NSUB][4];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        pa[s] = h + (int64_t)(row0 + 16 * s + lr) * d_e + lg * 32;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) psh[s][i] = a.h_scale + (int64_t)(row0 + 16 * s + 4 * lg + i) * kq;
-    }
-    const unsigned char* pb[2];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) pb[f] = w2 + ((int64_t)e * d_h + cb * 128 + w * 32 + 16 * f + lr) * d_e + lg * 32;
-    const float* psw = a.w2_scale + ((int64_t)e * (d_h / kQ) + cb) * kq;
-
-    v4f acc[NSUB][2];
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[s][0] = acc[s][1] = zero;
-    v8i A[NSUB], B[2];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) A[s] = ld32(pa[s]);
-#pragma unroll
-    for (int f = 0; f < 2; ++f) B[f] = ld32(pb[f]);
-    for (int kb = 0; kb < kq; ++kb) {
-        const int kn = (kb + 1 < kq ? kb + 1 : kb) * kQ;
-        v8i An[NSUB], Bn[2];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) An[s] = ld32(pa[s] + kn);
-#pragma unroll
-        for (int f = 0; f < 2; ++f) Bn[f] = ld32(pb[f] + kn);
-        const float sw = psw[kb];
-        float sh[NSUB][4];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sh[s][i] = psh[s][i][kb] * sw;
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                const v4f t = mfma_fp8(A[s], B[f], zero);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[s][f][i] += t[i] * sh[s][i];
-            }
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) A[s] = An[s];
-#pragma unroll
-        for (int f = 0; f < 2; ++f) B[f] = Bn[f];
-    }
-    store_y<NSUB, 2, false>(a, acc, row0, cb * 128 + w * 32, lg, lr);
-}
-
-// --------------------------------------------------------------- GEMM-2 bf16
-// Task: 16*NSUB rows x 64 output columns; wave w owns [16w, 16w+16).
-template <int NSUB, bool F32OUT>
-__device__ __forceinline__ void gemm2_bf16_task(const Gemm2Args& a, int e, int row0, int cb) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int d_h = a.d_h, d_e = a.d_e;
-    const unsigned short* h = static_cast<const unsigned short*>(a.h);
-    const unsigned short* w2 = static_cast<const unsigned short*>(a.w2);
-    const unsigned short* pa[NSUB];
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) pa[s] = h + (int64_t)(row0 + 16 * s + lr) * d_e + lg * 16;
-    const unsigned short* pb = w2 + ((int64_t)e * d_h + cb * 64 + w * 16 + lr) * d_e + lg * 16;
-
-    v4f acc[NSUB][2];
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) acc[s][0] = acc[s][1] = zero;
-    const int nk = d_e / 64;
-    Bf16x16 A[NSUB], B;
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) A[s] = ld_bf16x16(pa[s]);
-    B = ld_bf16x16(pb);
-    for (int kc = 0; kc < nk; ++kc) {
-        const int kn = (kc + 1 < nk ? kc + 1 : kc) * 64;
-        Bf16x16 An[NSUB];
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) An[s] = ld_bf16x16(pa[s] + kn);
-        const Bf16x16 Bn = ld_bf16x16(pb + kn);
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-            acc[s][0] = mfma_bf16(A[s].lo, B.lo, acc[s][0]);
-            acc[s][0] = mfma_bf16(A[s].hi, B.hi, acc[s][0]);
-        }
-#pragma unroll
-        for (int s = 0; s < NSUB; ++s) A[s] = An[s];
-        B = Bn;
-    }
-    store_y<NSUB, 1, F32OUT>(a, acc, row0, cb * 64 + w * 16, lg, lr);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg<MODE, false>::kLds];
     __shared__ int s_slot;
     const int ntasks = a.stats[kStatTasks2];
     for (;;) {
@@ -469,22 +459,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
         if (t >= ntasks) break;
         const int4 task = a.tasks[t];
         const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
-        if constexpr (MODE == MOE_MODE_FP8) {
-            switch (nsub) {
-                case 1: gemm2_fp8_task<1>(a, e, row0, cb); break;
-                case 2: gemm2_fp8_task<2>(a, e, row0, cb); break;
-                case 3: gemm2_fp8_task<3>(a, e, row0, cb); break;
-                default: gemm2_fp8_task<4>(a, e, row0, cb); break;
-            }
-        } else {
-            constexpr bool F32OUT = MODE == MOE_MODE_F32ACT;
-            switch (nsub) {
-                case 1: gemm2_bf16_task<1, F32OUT>(a, e, row0, cb); break;
-                case 2: gemm2_bf16_task<2, F32OUT>(a, e, row0, cb); break;
-                case 3: gemm2_bf16_task<3, F32OUT>(a, e, row0, cb); break;
-                default: gemm2_bf16_task<4, F32OUT>(a, e, row0, cb); break;
-            }
+#define MOE_G2(NS)                                                                                             \
+    gemm_task<MODE, false, NS>(a.h, a.h_scale, a.row_src, 1, a.w2, a.w2_scale, a.zero, e, row0, cb, a.d_e, a.d_h, \
+                               1, smem, nullptr, &a)
+        switch (nsub) {
+            case 1: MOE_G2(1); break;
+            case 2: MOE_G2(2); break;
+            case 3: MOE_G2(3); break;
+            default: MOE_G2(4); break;
         }
+#undef MOE_G2
     }
 }
 
@@ -526,23 +510,41 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     } else {
         uint4 o;
-        o.x = f32_to_bf16(acc[0]) | ((unsigned)f32_to_bf16(acc[1]) << 16);
-        o.y = f32_to_bf16(acc[2]) | ((unsigned)f32_to_bf16(acc[3]) << 16);
-        o.z = f32_to_bf16(acc[4]) | ((unsigned)f32_to_bf16(acc[5]) << 16);
-        o.w = f32_to_bf16(acc[6]) | ((unsigned)f32_to_bf16(acc[7]) << 16);
+        o.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+        o.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+        o.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+        o.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
         *reinterpret_cast<uint4*>(static_cast<unsigned short*>(a.out) + (int64_t)t * a.d_h + c) = o;
     }
 }
 
+__global__ __launch_bounds__(256) void x_to_bf16_kernel(const float* x, uint16_t* xb, int64_t n8) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const float4 u = reinterpret_cast<const float4*>(x)[2 * i];
+    const float4 v = reinterpret_cast<const float4*>(x)[2 * i + 1];
+    uint4 o;
+    o.x = f32_to_bf16(u.x) | (f32_to_bf16(u.y) << 16);
+    o.y = f32_to_bf16(u.z) | (f32_to_bf16(u.w) << 16);
+    o.z = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+    o.w = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+    reinterpret_cast<uint4*>(xb)[i] = o;
+}
+
 }  // namespace
+
+hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s) {
+    const int64_t n8 = n / 8;
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL(x_to_bf16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, xb, n8);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s) {
     if (mode == MOE_MODE_FP8)
         hipLaunchKernelGGL(gemm1_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, a);
-    else if (mode == MOE_MODE_BF16)
-        hipLaunchKernelGGL(gemm1_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, a);
     else
-        hipLaunchKernelGGL(gemm1_kernel<MOE_MODE_F32ACT>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipLaunchKernelGGL(gemm1_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -576,7 +578,7 @@ hipError_t gemm_occupancy(int mode, int* g1, int* g2) {
         e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_BF16>, kGemmThreads, 0);
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_BF16>, kGemmThreads, 0);
     } else {
-        e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_F32ACT>, kGemmThreads, 0);
+        e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_BF16>, kGemmThreads, 0);
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_F32ACT>, kGemmThreads, 0);
     }
     return e1 != hipSuccess ? e1 : e2;

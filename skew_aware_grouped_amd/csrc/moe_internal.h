@@ -23,15 +23,27 @@ constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxExperts = 256;
 constexpr int kQ = 128;  // FP8 block-scale granularity
+// Bytes of zeros kept in the workspace: padding rows of a group block read
+// their operand (and FP8 row scale) from here.
+constexpr int kZeroBytes = 256;
 
 // stats[] slots in the workspace
-enum { kStatDropped = 0, kStatTiles, kStatPadRows, kStatTasks1, kStatTasks2, kStatCounter1, kStatCounter2, kStatCount = 8 };
+enum {
+    kStatDropped = 0,
+    kStatTiles,
+    kStatPadRows,
+    kStatTasks1,
+    kStatTasks2,
+    kStatCounter1,
+    kStatCounter2,
+    kStatCount = 8
+};
 
-// Columns of the intermediate per GEMM-1 task and of the output per GEMM-2 task.
-// FP8 mode needs 128 so that one task owns a whole 128-column requantisation
-// group (GEMM-1) and a single weight-scale block row (both GEMMs).
+// Output columns per GEMM task.  GEMM-1 FP8 needs 128 so that one task owns
+// a whole 128-column requantisation group of the intermediate and a single
+// block row of W1's scales; the others use 64 (within one W2 scale block row).
 inline int gemm1_block_n(int mode) { return mode == MOE_MODE_FP8 ? 128 : 64; }
-inline int gemm2_block_n(int mode) { return mode == MOE_MODE_FP8 ? 128 : 64; }
+inline int gemm2_block_n(int) { return 64; }
 
 struct RouteArgs {
     const int32_t* ids;
@@ -42,16 +54,18 @@ struct RouteArgs {
     int32_t* stats;
     int4* tasks1;
     int4* tasks2;
+    unsigned char* zero;  // kZeroBytes to clear (may be null)
 };
 
 struct Gemm1Args {
-    const void* x;
+    const void* x;  // e4m3 codes or bf16 [T, d_h]
     const float* x_scale;
     const void* w1;
     const float* w1_scale;
     const int32_t* row_src;
     const int4* tasks;
     int32_t* stats;
+    const unsigned char* zero;
     void* h;
     float* h_scale;
     int32_t k, d_h, d_e;
@@ -66,6 +80,7 @@ struct Gemm2Args {
     const float* topk_w;
     const int4* tasks;
     int32_t* stats;
+    const unsigned char* zero;
     void* y;
     int32_t d_h, d_e;
 };
@@ -78,6 +93,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// x fp32 -> bf16 (round to nearest even), n elements, multiple of 8
+hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s);
 hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s);
 hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s);
 hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s);

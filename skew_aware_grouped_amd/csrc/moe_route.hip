@@ -84,6 +84,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
     if (tid == 0) s_dropped = 0;
+    if (a.zero)
+        for (int i = tid; i < kZeroBytes / 4; i += kRouteThreads) reinterpret_cast<int*>(a.zero)[i] = 0;
     __syncthreads();
 
     // 1. histogram (LDS atomics: the counts do not depend on their order)

@@ -45,7 +45,7 @@ class moe_route_out(ctypes.Structure):
 class moe_ws_layout(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_size_t) for n in ("counts", "offsets", "padded_offsets", "pos", "sorted_p", "ppos",
                                                  "row_src", "tile_expert", "tile_row0", "stats", "tasks1", "tasks2",
-                                                 "h", "h_scale", "y", "total")]
+                                                 "h", "h_scale", "y", "zero", "x_bf16", "total")]
                 + [(n, ctypes.c_int64) for n in ("n_pad_cap", "tile_cap", "task1_cap", "task2_cap")]
                 + [(n, ctypes.c_int32) for n in ("block_n1", "block_n2", "max_row_blocks")])
 
@@ -206,6 +206,9 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     if events is None:
         rc = moe_fused_forward(*args)
     else:
+        for e in events:
+            if not e.cuda_event:  # torch creates its event lazily, on first record
+                e.record(stream if stream is not None else torch.cuda.current_stream())
         rc = moe_fused_forward_profiled(*args, [e.cuda_event for e in events])
     if rc:
         raise MoEError(rc, "moe_fused_forward")
