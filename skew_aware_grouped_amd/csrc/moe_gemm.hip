@@ -116,6 +116,9 @@ __device__ __forceinline__ unsigned lds_offset(const void* p) { return (unsigned
 // empty asm keeps the compiler from moving LDS accesses across the barrier
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
+    // this wave's LDS reads of the previous stage are complete before any
+    // wave may overwrite that slot (s_waitcnt lgkmcnt(0), no vmcnt wait)
+    __builtin_amdgcn_s_waitcnt(VmCnt<63>::imm & ~(0xF << 8));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
@@ -176,7 +179,12 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     constexpr bool kFP8 = C::kFP8;
     constexpr int S = C::kStages;
     constexpr int kAI = ALoad<NSUB>::kInstr;
-    constexpr int L = C::kBInstr + kAI + (kFP8 ? 1 : 0);  // loads per wave per stage
+    // Loads every wave issues per stage: its B rows and its A rows.  The FP8
+    // scale load is issued only by the waves that own a row or block scale,
+    // so it is left out: waiting for at most L*R outstanding loads, with the
+    // smallest per-stage count a wave can have, retires the oldest stage on
+    // every wave whatever its own count.
+    constexpr int L = C::kBInstr + kAI;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
