@@ -54,28 +54,77 @@ def gemm2_alg_bytes(w):
     return float(b)
 
 
-def cpu_baseline(w, target_s=15.0):
-    """The oracle as it stands, on a bounded sample of the workload's tokens."""
+KERNEL_SOURCES = ["moe_gemm.hip", "moe_internal.h", "moe_route.hip"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "skew_aware_grouped_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM-side bytes per launch from the committed counter summary
+    (profiles/, FETCH_SIZE + WRITE_SIZE scaled by a copy of known size), or
+    None when no record exists or the kernel sources changed since it was taken."""
+    import glob
+    src = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                line = line.strip()
+                if not line.startswith("traffic_record:"):
+                    continue
+                rec = json.loads(line[len("traffic_record:"):])
+                if rec.get("kernel") == kernel and rec.get("workload") == workload and \
+                        rec.get("source_sha256_16") == src:
+                    return float(rec["traffic_bytes"])
+    return None
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The oracle as it stands, on a bounded sample of the workload: a token
+    subset when the whole batch would take longer than ~target_s, otherwise the
+    whole batch repeated until ~target_s of CPU work has run."""
     from oracle import moe_oracle
     threads = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
     rng = np.random.default_rng(0)
     # calibrate on a few tokens, then size the sample to ~target_s
-    probe = rng.choice(w.T, size=min(4, w.T), replace=False)
+    probe = rng.choice(w.T, size=min(16, w.T), replace=False)
     t0 = time.perf_counter()
     moe_oracle.forward(w, rows=probe)
     dt = max(time.perf_counter() - t0, 1e-6)
     n = int(min(w.T, max(len(probe), len(probe) * target_s / dt)))
     rows = np.sort(rng.choice(w.T, size=n, replace=False))
+    reps = 1 if n < w.T else max(1, int(round(target_s / (dt * w.T / len(probe)))))
     t0 = time.perf_counter()
-    moe_oracle.forward(w, rows=rows)
+    for _ in range(reps):
+        moe_oracle.forward(w, rows=rows)
     dt = time.perf_counter() - t0
     sub_ids = w.topk_ids[rows]
     nv = int(((sub_ids >= 0) & (sub_ids < w.E)).sum())
-    flops = 6.0 * w.d_h * w.d_e * nv
+    flops = 6.0 * w.d_h * w.d_e * nv * reps
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {w.T} tokens ({nv} assignments) of {w.name}, {dt:.2f} s, fp32 C oracle with "
-                      f"OpenMP over tokens",
+            "sample": f"{n} of {w.T} tokens ({nv} assignments) of {w.name}, {reps} pass(es), {dt:.2f} s, "
+                      f"fp32 C oracle with OpenMP over tokens",
             "seconds": round(dt, 3)}
+
+
+def copy_calibration(mb):
+    """A plain device-to-device copy of a known size, for scaling the HBM byte
+    counters of a profiler run (FETCH_SIZE / WRITE_SIZE read for this copy
+    against the bytes it must move)."""
+    import torch
+    n = mb * (1 << 20)
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -85,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain copy of this many MiB (for scaling profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this layer runs on one GPU; --gpus above 1 is not supported (the multi-GPU expert-"
@@ -95,6 +146,9 @@ def main():
     from skew_aware_grouped_amd import device, moe, workloads as W
 
     torch.cuda.set_device(0)
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
+        return
     w = W.config(args.config)
     d = device.upload(w)
     dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
@@ -118,14 +172,35 @@ def main():
     for _ in range(args.warmup):
         device.run(d, out=out, workspace=ws)
     stream = torch.cuda.current_stream()
+
+    def timed_steps(n, flush=None):
+        """n layer calls, each between two events on the library's stream (no
+        event between its kernels); with ``flush``, a read of a 1 GiB buffer
+        before each call, outside its events, leaves the L2s and the 256 MB
+        Infinity Cache holding other (clean) lines."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in evs:
+            if flush is not None:
+                flush.sum()
+            a.record(stream)
+            device.run(d, out=out, workspace=ws, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs]), time.perf_counter() - t0
+
+    step_ms, wall = timed_steps(args.steps)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+    cold_ms, _ = timed_steps(min(args.steps, 20), flush)
+    del flush
+    # per-kernel durations: the stage-event variant records an event between
+    # the kernels (each event adds a few microseconds of launch gap, so these
+    # steps are not the ones the headline p50 comes from)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         device.run(d, out=out, workspace=ws, stream=stream, events=ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = np.array([e[0].elapsed_time(e[4]) for e in ev])
     stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
     p50 = float(np.median(step_ms))
     flops = W.flops(w)
@@ -157,6 +232,9 @@ def main():
         "p50_us": round(p50 * 1e3, 2),
         "p10_us": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
         "p90_us": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+        "cold_p50_us": round(float(np.median(cold_ms)) * 1e3, 2),
+        "cold_p10_us": round(float(np.percentile(cold_ms, 10)) * 1e3, 2),
+        "cold_p90_us": round(float(np.percentile(cold_ms, 90)) * 1e3, 2),
         "wall_us_per_step": round(wall / args.steps * 1e6, 2),
         "gflop": round(flops / 1e9, 4),
         "alg_mb": round(alg_bytes / 1e6, 3),
@@ -166,7 +244,7 @@ def main():
         "gate_normwise_err": round(gate_err, 6),
         "roofline": {"kernel": "gemm1_swiglu", "bound": bound, "achieved": round(g1_gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(g1_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None, "alg_bytes_per_launch": g1_bytes, "avg_launch_us": round(g1_us, 2)},
+                     "traffic": measured_traffic("gemm1_kernel", w.name), "alg_bytes_per_launch": g1_bytes, "avg_launch_us": round(g1_us, 2)},
     }
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w)
