@@ -96,7 +96,7 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
  *  workspace device buffer of at least moe_workspace_bytes(dims) bytes, 256-byte aligned
  *
  * Steps enqueued on `stream`: routing (histogram, prefix scan, stable scatter,
- * block map and task lists), grouped GEMM-1 with the SwiGLU epilogue,
+ * block map and per-XCD task lists), grouped GEMM-1 with the SwiGLU epilogue,
  * grouped GEMM-2 with the routing-weight epilogue, and the top-k combine in
  * ascending slot order.  The result is bitwise identical across calls.
  */
@@ -155,10 +155,14 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
               const moe_route_out* out, void* stream);
 
 /* Byte offsets of the workspace sections moe_fused_forward uses, for tests and
- * inspection after a call (the routing arrays hold the layout described for
- * moe_route; tasks are int32 quadruples {expert, first padded row, row
- * blocks, column block}, GEMM-1's list first).  stats holds {dropped, blocks,
- * padded rows, GEMM-1 tasks, GEMM-2 tasks, GEMM-1 counter, GEMM-2 counter, 0}.
+ * inspection after a call.  The routing arrays hold the layout described for
+ * moe_route.  `stats` is a control block of int32 words: [0..4] = {dropped,
+ * blocks, padded rows, GEMM-1 tasks, GEMM-2 tasks}; words [272..280] and
+ * [288..296] hold the start of each of the 8 per-XCD segments (and the end of
+ * the last) of the GEMM-1 and GEMM-2 task lists.  Tasks are int32 quadruples
+ * {expert, first padded row, row blocks, column block}; within a segment they
+ * are ordered by descending expert row count, and all M-tiles of one
+ * (expert, column block) sit in the same segment, next to each other.
  * Returns MOE_ERR_INVALID_ARG for invalid dims. */
 typedef struct {
     size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, tile_expert, tile_row0, stats;

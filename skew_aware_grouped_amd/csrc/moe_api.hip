@@ -1,6 +1,7 @@
 // C-ABI host side of the fused MoE library: argument checks, workspace
 // layout, persistent-grid sizing and the launch sequence
 // route -> GEMM-1 (+SwiGLU) -> GEMM-2 (+routing weight) -> combine.
+#include <algorithm>
 #include <mutex>
 
 #include "moe_internal.h"
@@ -55,7 +56,7 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     L->row_src = take(4 * L->n_pad_cap);
     L->tile_expert = take(4 * L->tile_cap);
     L->tile_row0 = take(4 * L->tile_cap);
-    L->stats = take(4 * kStatCount);
+    L->stats = take(4 * kCtlWords);
     L->tasks1 = take(16 * L->task1_cap);
     L->tasks2 = take(16 * L->task2_cap);
     L->h = take(hb * L->n_pad_cap * d->d_expert);
@@ -169,7 +170,7 @@ int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, const int3
     a.row_src = out->row_src;
     a.tile_expert = out->tile_expert;
     a.tile_row0 = out->tile_row0;
-    a.stats = out->stats;
+    a.ctl = out->stats;  // only words 0..3 are written when no task lists are built
     if (launch_route(a, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
@@ -223,7 +224,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.row_src = at<int32_t>(workspace, L.row_src);
     r.tile_expert = at<int32_t>(workspace, L.tile_expert);
     r.tile_row0 = at<int32_t>(workspace, L.tile_row0);
-    r.stats = at<int32_t>(workspace, L.stats);
+    r.ctl = at<int32_t>(workspace, L.stats);
     r.tasks1 = at<int4>(workspace, L.tasks1);
     r.tasks2 = at<int4>(workspace, L.tasks2);
     r.zero = at<unsigned char>(workspace, L.zero);
@@ -242,7 +243,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.w1_scale = mode == MOE_MODE_FP8 ? scales->w1_scale : nullptr;
     g1.row_src = r.row_src;
     g1.tasks = r.tasks1;
-    g1.stats = r.stats;
+    g1.ctl = r.ctl;
     g1.zero = r.zero;
     g1.h = at<void>(workspace, L.h);
     g1.h_scale = mode == MOE_MODE_FP8 ? at<float>(workspace, L.h_scale) : nullptr;
@@ -260,7 +261,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.row_src = r.row_src;
     g2.topk_w = topk_w;
     g2.tasks = r.tasks2;
-    g2.stats = r.stats;
+    g2.ctl = r.ctl;
     g2.zero = r.zero;
     g2.y = at<void>(workspace, L.y);
     g2.d_h = d_h;

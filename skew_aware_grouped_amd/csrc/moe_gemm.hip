@@ -58,19 +58,22 @@ struct VmCnt {
     static constexpr int imm = (N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8);
 };
 
-template <int L, int R>
-__device__ __forceinline__ void wait_vm_stages(int rem) {
-    // wait until at most rem stages (L loads each) of this wave are in flight
-    if constexpr (R > 0) {
-        if (rem >= R) {
-            __builtin_amdgcn_s_waitcnt(VmCnt<L * R>::imm);
-            return;
-        }
-        wait_vm_stages<L, R - 1>(rem);
+// Wait until at most n (wave-uniform, 0 <= n) of this wave's vector-memory
+// operations are outstanding: a binary search over the immediates, at most
+// six scalar branches.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_le_tree(int n) {
+    if constexpr (LO == HI) {
+        __builtin_amdgcn_s_waitcnt(VmCnt<LO>::imm);
     } else {
-        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        constexpr int MID = (LO + HI + 1) / 2;
+        if (n >= MID)
+            wait_vm_le_tree<MID, HI>(n);
+        else
+            wait_vm_le_tree<LO, MID - 1>(n);
     }
 }
+__device__ __forceinline__ void wait_vm_le(int n) { wait_vm_le_tree<0, 63>(n < 63 ? n : 63); }
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0 (no MX scaling)
@@ -109,7 +112,6 @@ __device__ __forceinline__ void g2l16(const void* g, unsigned lds) {
 __device__ __forceinline__ void g2l4(const void* g, unsigned lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
-
 __device__ __forceinline__ unsigned lds_offset(const void* p) { return (unsigned)(uintptr_t)p; }
 
 // stage hand-off: every wave has waited for its own loads of the stage; the
@@ -132,65 +134,101 @@ __device__ __forceinline__ v8i lds_frag32(const unsigned char* row, int g, int s
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ int pull_task(int32_t* counter, int* s_slot) {
-    if (threadIdx.x == 0) *s_slot = atomicAdd(counter, 1);
+// XCD of the calling wave (HW_REG_XCC_ID).  Only the task placement depends
+// on it; any value in [0, 8) is correct.
+__device__ __forceinline__ int my_xcd() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcds - 1); }
+
+// Next task of this workgroup: from its own XCD's segment of the list first,
+// then from the other segments in turn (each segment keeps its own counter,
+// in its own cache line).  Returns -1 once every segment is exhausted.
+// s_seg holds the kXcds + 1 segment starts; s_mask the segments found empty.
+__device__ __forceinline__ int pull_task(int32_t* ctl, int counter_base, const int* s_seg, int xcd, int* s_slot,
+                                         unsigned* s_mask) {
+    if (threadIdx.x == 0) {
+        int slot = -1;
+        for (int i = 0; i < kXcds; ++i) {
+            const int x = (xcd + i) & (kXcds - 1);
+            if ((*s_mask >> x) & 1u) continue;
+            const int j = atomicAdd(&ctl[counter_base + kQueueStride * x], 1);
+            if (s_seg[x] + j < s_seg[x + 1]) {
+                slot = s_seg[x] + j;
+                break;
+            }
+            *s_mask |= 1u << x;
+        }
+        *s_slot = slot;
+    }
     __syncthreads();
-    const int t = *s_slot;
+    // readfirstlane: the slot is the same for every thread, and the compiler
+    // must know it, or it treats the task loop as divergent and may split a
+    // thread-0 region next to the loop's back-edge off the loop while the
+    // other lanes iterate on a stale slot
+    const int t = __builtin_amdgcn_readfirstlane(*s_slot);
     __syncthreads();
     return t;
 }
 
 // ------------------------------------------------------------------ configs
+// Stage of the ring for a task of NSUB group blocks: the K block of the
+// task's weight rows (B), of its 16*NSUB operand rows (A) and, in FP8 mode,
+// their scales.  The ring has a fixed byte size per kernel, so tasks with
+// fewer rows get more stages in flight.
 template <int MODE, bool GATED>
 struct Cfg {
     static constexpr bool kFP8 = MODE == MOE_MODE_FP8;
-    static constexpr int kWaves = kGemmWaves;
-    static constexpr int kNFW = (GATED && kFP8) ? 2 : 1;  // 16-column fragments per wave
-    static constexpr int kBN = 16 * kNFW * kWaves;         // output columns per task
+    static constexpr int kNFW = (GATED && !kFP8) ? 1 : 2;  // 16-column fragments per wave
+    static constexpr int kBN = 16 * kNFW * kGemmWaves;     // output columns per task
     static constexpr int kBRows = GATED ? 2 * kBN : kBN;   // weight rows per task
-    static constexpr int kBInstr = kBRows / 8 / kWaves;    // B loads per wave per stage
+    static constexpr int kBInstr = kBRows / 8 / kGemmWaves;  // B loads per wave per stage
     static constexpr int kStageB = kBRows * kRowBytes;
-    static constexpr int kStageA = kAMaxRows * kRowBytes;
     static constexpr int kStageS = kFP8 ? 512 : 0;  // 64 row scales, then the block scale(s)
-    static constexpr int kStage = kStageB + kStageA + kStageS;
-    static constexpr int kStages = (GATED ? 3 : 4);
-    static constexpr int kLds = kStages * kStage;
-    // per-lane epilogue staging: one row of output per tile row, kBN columns
+    static constexpr int stage_bytes(int nsub) { return kStageB + 16 * nsub * kRowBytes + kStageS; }
+    // ring: four stages of a one-block task (FP8 GEMM-1: one workgroup per
+    // CU; the others: two)
+    static constexpr int kRing = 4 * stage_bytes(1);
+    // stages in a ring of `ring` bytes
+    static constexpr int stages(int nsub, int ring) {
+        return ring / stage_bytes(nsub) < 8 ? ring / stage_bytes(nsub) : 8;
+    }
     static constexpr int kOutBytes = (MODE == MOE_MODE_F32ACT && !GATED) ? 4 : (GATED && kFP8 ? 1 : 2);
-    static constexpr int kEpiRow = kBN * kOutBytes;
-    static_assert(kEpiRow * kAMaxRows + 1024 <= kLds, "epilogue staging must fit in the stage ring");
-    static_assert(kLds <= 160 * 1024, "LDS budget");
-};
-
-template <int NSUB>
-struct ALoad {
-    static constexpr int kRowsPerWave = 16 * NSUB / kGemmWaves;  // 4*NSUB
-    static constexpr int kInstr = (kRowsPerWave * 8 + 63) / 64;
+    static constexpr int kEpiRow = kBN * kOutBytes;  // bytes of one staged output row
+    static_assert(kEpiRow * kAMaxRows + 1024 <= kRing, "epilogue staging must fit in the stage ring");
+    static_assert(stages(kMaxRowBlocks, kRing) >= 2, "ring too small");
+    static_assert(kRing <= 160 * 1024, "LDS budget");
+    static_assert(GATED || kBN == 128, "GEMM-2 tasks are 128 columns wide (one W2 scale block row)");
 };
 
 // ------------------------------------------------------------------ kernel
 // One task: rows [row0, row0 + 16*NSUB) of expert e, output column block cb.
-template <int MODE, bool GATED, int NSUB>
+//   GATED (GEMM-1): A rows are tokens x[row_src[r] / k] (zero row for padding),
+//     B rows are W1[e] gate rows cb*kBN.. and up rows d_e + cb*kBN..; the
+//     epilogue writes h[row0 + r][cb*kBN ..] (+ FP8 scale).
+//   !GATED (GEMM-2): A rows are h[row0 + r], B rows W2[e] rows cb*kBN..; the
+//     epilogue scales by topk_w[row_src[r]] and writes y[row_src[r]][cb*kBN ..].
+// K is the contraction length (d_h or d_e); N_out is d_e (GATED) or d_h.
+template <int MODE, bool GATED, int NSUB, int RING>
 __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_scale, const int32_t* row_src,
                                           int a_div, const void* wts, const float* w_scale, const unsigned char* zero,
-                                          int e, int row0, int cb, int K, int N_out, int k_top, unsigned char* smem,
+                                          int e, int row0, int cb, int K, int N_out, unsigned char* smem,
                                           const Gemm1Args* g1, const Gemm2Args* g2) {
     using C = Cfg<MODE, GATED>;
     constexpr bool kFP8 = C::kFP8;
-    constexpr int S = C::kStages;
-    constexpr int kAI = ALoad<NSUB>::kInstr;
-    // Loads every wave issues per stage: its B rows and its A rows.  The FP8
-    // scale load is issued only by the waves that own a row or block scale,
-    // so it is left out: waiting for at most L*R outstanding loads, with the
-    // smallest per-stage count a wave can have, retires the oldest stage on
-    // every wave whatever its own count.
-    constexpr int L = C::kBInstr + kAI;
+    constexpr int S = C::stages(NSUB, RING);
+    static_assert(RING >= C::kRing, "ring smaller than this GEMM's");
+    constexpr int kStage = C::stage_bytes(NSUB);
+    constexpr int kStageA = 16 * NSUB * kRowBytes;
+    constexpr int kAInstr = 2 * NSUB;  // A loads per stage: 8 rows each
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int nk = K / (kFP8 ? 128 : 64);
     const unsigned smem_lds = lds_offset(smem);
     const int64_t ld_bytes = (int64_t)K * (kFP8 ? 1 : 2);  // bytes per operand row
+    // vector-memory loads this wave issues per stage: its B rows, its A rows
+    // (instructions w, w+4, ...) and, in FP8 mode, the row scales (wave 0) or
+    // the block scales (wave 1)
+    const int n_a = w < kAInstr ? (kAInstr - 1 - w) / kGemmWaves + 1 : 0;
+    const int loads_per_stage = C::kBInstr + n_a + ((kFP8 && w < 2) ? 1 : 0);
 
     // ---- per-lane load sources (stage 0); a K block advances them by 128 bytes
     const unsigned char* bsrc[C::kBInstr];
@@ -206,62 +244,67 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         const int64_t rows_per_expert = GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
         bsrc[j] = static_cast<const unsigned char*>(wts) + ((int64_t)e * rows_per_expert + wrow) * ld_bytes + c * 16;
     }
-    const unsigned char* asrc[kAI];
-    bool aon[kAI], apad[kAI];
+    constexpr int kAMaxPerWave = (kAInstr + kGemmWaves - 1) / kGemmWaves;
+    const unsigned char* asrc[kAMaxPerWave];
+    bool apad[kAMaxPerWave];
 #pragma unroll
-    for (int j = 0; j < kAI; ++j) {
-        const int rl = j * 8 + (lane >> 3);
-        const int r = w * ALoad<NSUB>::kRowsPerWave + rl;
+    for (int j = 0; j < kAMaxPerWave; ++j) {
+        const int ai = w + kGemmWaves * j;  // A instruction: rows 8*ai .. 8*ai+7
+        const int r = 8 * ai + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
-        aon[j] = rl < ALoad<NSUB>::kRowsPerWave;
-        int p = aon[j] ? row_src[row0 + r] : -1;
-        apad[j] = p < 0;
-        const int64_t arow = GATED ? (p >= 0 ? p / a_div : 0) : (int64_t)(row0 + r);
-        if (!GATED) apad[j] = false;  // GEMM-2 reads its own padded rows (zeros from GEMM-1)
-        asrc[j] = apad[j] ? zero + c * 16
-                          : static_cast<const unsigned char*>(a_base) + arow * ld_bytes + c * 16;
+        apad[j] = false;
+        asrc[j] = zero;
+        if (ai < kAInstr) {
+            if constexpr (GATED) {
+                const int p = row_src[row0 + r];
+                apad[j] = p < 0;
+                asrc[j] = apad[j] ? zero + c * 16
+                                  : static_cast<const unsigned char*>(a_base) + (int64_t)(p / a_div) * ld_bytes + c * 16;
+            } else {
+                // GEMM-2 reads its own padded rows (GEMM-1 wrote zeros there)
+                asrc[j] = static_cast<const unsigned char*>(a_base) + (int64_t)(row0 + r) * ld_bytes + c * 16;
+            }
+        }
     }
-    // scale sources: lanes 0..15 of wave w -> row scale of tile row 16w + lane;
-    // wave 3 lanes 16 (and 17) -> block scale(s) of W for this K block
+    // scale sources: wave 0 lane r -> row scale of tile row r; wave 1 lane 0
+    // (and 1) -> block scale(s) of W for this K block
     const float* ssrc = nullptr;
     bool son = false, spad = false;
     if constexpr (kFP8) {
         const int kq = K / kQ;
-        if (lane < 16) {
-            const int r = 16 * w + lane;
-            son = r < 16 * NSUB;
-            if (son) {
-                const int p = row_src[row0 + r];
-                if (GATED) {
-                    spad = p < 0;
-                    ssrc = spad ? reinterpret_cast<const float*>(zero) : a_scale + (int64_t)(p / a_div) * kq;
-                } else {
-                    ssrc = a_scale + (int64_t)(row0 + r) * kq;
-                }
+        if (w == 0 && lane < 16 * NSUB) {
+            son = true;
+            const int p = row_src[row0 + lane];
+            if (GATED) {
+                spad = p < 0;
+                ssrc = spad ? reinterpret_cast<const float*>(zero) : a_scale + (int64_t)(p / a_div) * kq;
+            } else {
+                ssrc = a_scale + (int64_t)(row0 + lane) * kq;
             }
-        } else if (w == kGemmWaves - 1 && lane < (GATED ? 18 : 17)) {
+        } else if (w == 1 && lane < (GATED ? 2 : 1)) {
             son = true;
             // W1 scales [E][2 d_e/128][d_h/128]: gate block row cb, up block row d_e/128 + cb
-            // W2 scales [E][d_h/128][d_e/128]: block row (cb*64)/128
+            // W2 scales [E][d_h/128][d_e/128]: block row cb (128-column tasks)
             const int64_t nrb = GATED ? 2 * (int64_t)N_out / kQ : (int64_t)N_out / kQ;
-            const int64_t brow = GATED ? (lane == 16 ? cb : N_out / kQ + cb) : (int64_t)cb * C::kBN / kQ;
+            const int64_t brow = GATED ? (lane == 0 ? cb : N_out / kQ + cb) : (int64_t)cb;
             ssrc = w_scale + ((int64_t)e * nrb + brow) * kq;
         }
     }
 
     auto issue = [&](int kc) {
-        const unsigned st = smem_lds + (unsigned)((kc % S) * C::kStage);
+        const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
         const int64_t koff = (int64_t)kc * kRowBytes;
 #pragma unroll
         for (int j = 0; j < C::kBInstr; ++j) g2l16(bsrc[j] + koff, st + (unsigned)((w * C::kBInstr + j) * 1024));
 #pragma unroll
-        for (int j = 0; j < kAI; ++j) {
-            if (aon[j])
-                g2l16(apad[j] ? asrc[j] : asrc[j] + koff,
-                      st + (unsigned)(C::kStageB + (w * ALoad<NSUB>::kRowsPerWave + j * 8) * kRowBytes));
+        for (int j = 0; j < kAMaxPerWave; ++j) {
+            const int ai = w + kGemmWaves * j;
+            if (ai < kAInstr) g2l16(apad[j] ? asrc[j] : asrc[j] + koff, st + (unsigned)(C::kStageB + ai * 1024));
         }
         if constexpr (kFP8) {
-            if (son) g2l4(spad ? ssrc : ssrc + kc, st + (unsigned)(C::kStageB + C::kStageA + w * 64));
+            // wave 0 reads the row scales, wave 1 the weights' block scales
+            const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
+            if (son) g2l4(spad ? ssrc : ssrc + kc, w == 0 ? ss : ss + 256u);
         }
     };
 
@@ -278,15 +321,16 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     const int npro = nk < S - 1 ? nk : S - 1;
     for (int kc = 0; kc < npro; ++kc) issue(kc);
     for (int kc = 0; kc < nk; ++kc) {
-        const int rem = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
-        wait_vm_stages<L, S - 2>(rem);
+        // stage kc is complete once at most the younger stages' loads remain
+        const int younger = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
+        wait_vm_le(younger * loads_per_stage);
         stage_barrier();
         if (kc + S - 1 < nk) issue(kc + S - 1);
-        const unsigned char* st = smem + (kc % S) * C::kStage;
+        const unsigned char* st = smem + (kc % S) * kStage;
         const unsigned char* sb = st;
         const unsigned char* sa = st + C::kStageB;
         if constexpr (kFP8) {
-            const float* sc = reinterpret_cast<const float*>(st + C::kStageB + C::kStageA);
+            const float* sc = reinterpret_cast<const float*>(st + C::kStageB + kStageA);
             v8i A[NSUB];
 #pragma unroll
             for (int s = 0; s < NSUB; ++s) A[s] = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
@@ -295,7 +339,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             for (int s = 0; s < NSUB; ++s)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sx[s][i] = sc[16 * s + 4 * lg + i];
-            const float swg = sc[64];  // written by lane 16 (and 17) of the last wave
+            const float swg = sc[64];  // written by lane 0 (and 1) of wave 1
             const float swu = GATED ? sc[65] : 0.f;
 #pragma unroll
             for (int f = 0; f < C::kNFW; ++f) {
@@ -344,7 +388,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
 
     // ---- epilogue: stage the output tile in LDS, then 16-byte row stores
     __syncthreads();  // every wave is done with the ring
-    unsigned char* stage = smem;                               // [kAMaxRows][kEpiRow]
+    unsigned char* stage = smem;                                              // [16*NSUB][kEpiRow]
     float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * kAMaxRows);  // [waves][64]
     if constexpr (GATED) {
         float hv[NSUB][C::kNFW][4];
@@ -379,18 +423,21 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
                     for (int f = 0; f < C::kNFW; ++f)
-                        stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] = (unsigned char)f32_to_e4m3(hv[s][f][i] / sc);
+                        stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] =
+                            (unsigned char)f32_to_e4m3(hv[s][f][i] / sc);
                     if (w == 0 && lr == 0) g1->h_scale[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
                 }
         } else {
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int rr = 16 * s + 4 * lg + i;
-                    reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[16 * w + lr] =
-                        (unsigned short)f32_to_bf16(hv[s][0][i]);
-                }
+                for (int f = 0; f < C::kNFW; ++f)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = 16 * s + 4 * lg + i;
+                        reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[16 * (C::kNFW * w + f) + lr] =
+                            (unsigned short)f32_to_bf16(hv[s][f][i]);
+                    }
         }
         __syncthreads();
         // h[row0 + r][cb*kBN ...]: kEpiRow bytes per row
@@ -411,12 +458,15 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                 const int rr = 16 * s + 4 * lg + i;
                 const int p = row_src[row0 + rr];
                 const float wt = p >= 0 ? g2->topk_w[p] : 0.f;
-                const float v = acc[s][0][0][i] * wt;
-                if constexpr (kF32)
-                    reinterpret_cast<float*>(stage + rr * C::kEpiRow)[16 * w + lr] = v;
-                else
-                    reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[16 * w + lr] =
-                        (unsigned short)f32_to_bf16(v);
+#pragma unroll
+                for (int f = 0; f < C::kNFW; ++f) {
+                    const float v = acc[s][f][0][i] * wt;
+                    const int col = 16 * (C::kNFW * w + f) + lr;
+                    if constexpr (kF32)
+                        reinterpret_cast<float*>(stage + rr * C::kEpiRow)[col] = v;
+                    else
+                        reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[col] = (unsigned short)f32_to_bf16(v);
+                }
             }
         __syncthreads();
         constexpr int kChunks = C::kEpiRow / 16;
@@ -436,17 +486,22 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
     constexpr int GM = MODE == MOE_MODE_F32ACT ? MOE_MODE_BF16 : MODE;  // x arrives as bf16
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg<GM, true>::kLds];
-    __shared__ int s_slot;
-    const int ntasks = a.stats[kStatTasks1];
+    constexpr int RING = Cfg<GM, true>::kRing;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[RING];
+    __shared__ int s_slot, s_seg[kXcds + 1];
+    __shared__ unsigned s_mask;
+    if (threadIdx.x <= kXcds) s_seg[threadIdx.x] = a.ctl[kCtlSeg1 + threadIdx.x];
+    if (threadIdx.x == 0) s_mask = 0;
+    __syncthreads();
+    const int xcd = my_xcd();
     for (;;) {
-        const int t = pull_task(&a.stats[kStatCounter1], &s_slot);
-        if (t >= ntasks) break;
+        const int t = pull_task(a.ctl, kCtlQueue1, s_seg, xcd, &s_slot, &s_mask);
+        if (t < 0) break;
         const int4 task = a.tasks[t];
         const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
-#define MOE_G1(NS)                                                                                              \
-    gemm_task<GM, true, NS>(a.x, a.x_scale, a.row_src, a.k, a.w1, a.w1_scale, a.zero, e, row0, cb, a.d_h, a.d_e, \
-                            a.k, smem, &a, nullptr)
+#define MOE_G1(NS)                                                                                                \
+    gemm_task<GM, true, NS, RING>(a.x, a.x_scale, a.row_src, a.k, a.w1, a.w1_scale, a.zero, e, row0, cb, a.d_h, a.d_e, \
+                                  smem, &a, nullptr)
         switch (nsub) {
             case 1: MOE_G1(1); break;
             case 2: MOE_G1(2); break;
@@ -459,17 +514,22 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
 
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Cfg<MODE, false>::kLds];
-    __shared__ int s_slot;
-    const int ntasks = a.stats[kStatTasks2];
+    constexpr int RING = Cfg<MODE, false>::kRing;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[RING];
+    __shared__ int s_slot, s_seg[kXcds + 1];
+    __shared__ unsigned s_mask;
+    if (threadIdx.x <= kXcds) s_seg[threadIdx.x] = a.ctl[kCtlSeg2 + threadIdx.x];
+    if (threadIdx.x == 0) s_mask = 0;
+    __syncthreads();
+    const int xcd = my_xcd();
     for (;;) {
-        const int t = pull_task(&a.stats[kStatCounter2], &s_slot);
-        if (t >= ntasks) break;
+        const int t = pull_task(a.ctl, kCtlQueue2, s_seg, xcd, &s_slot, &s_mask);
+        if (t < 0) break;
         const int4 task = a.tasks[t];
         const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
-#define MOE_G2(NS)                                                                                             \
-    gemm_task<MODE, false, NS>(a.h, a.h_scale, a.row_src, 1, a.w2, a.w2_scale, a.zero, e, row0, cb, a.d_e, a.d_h, \
-                               1, smem, nullptr, &a)
+#define MOE_G2(NS)                                                                                                 \
+    gemm_task<MODE, false, NS, RING>(a.h, a.h_scale, a.row_src, 1, a.w2, a.w2_scale, a.zero, e, row0, cb, a.d_e, a.d_h, \
+                                     smem, nullptr, &a)
         switch (nsub) {
             case 1: MOE_G2(1); break;
             case 2: MOE_G2(2); break;

@@ -27,23 +27,31 @@ constexpr int kQ = 128;  // FP8 block-scale granularity
 // their operand (and FP8 row scale) from here.
 constexpr int kZeroBytes = 256;
 
-// stats[] slots in the workspace
+// Control block of the workspace (int32 words): statistics, then the
+// per-XCD task queues of the two GEMM kernels.  Each queue has its own
+// 64-byte line for its counter so the eight XCDs' atomics do not share one.
 enum {
     kStatDropped = 0,
     kStatTiles,
     kStatPadRows,
     kStatTasks1,
     kStatTasks2,
-    kStatCounter1,
-    kStatCounter2,
-    kStatCount = 8
+    kStatCount = 8,
+    kXcds = 8,          // XCDs of an MI355X; a task list is split into this many segments
+    kQueueStride = 16,  // words between two queue counters
+    kCtlQueue1 = 16,    // GEMM-1 counters: [kCtlQueue1 + kQueueStride * x]
+    kCtlQueue2 = kCtlQueue1 + kXcds * kQueueStride,
+    kCtlSeg1 = kCtlQueue2 + kXcds * kQueueStride,  // GEMM-1 segment starts [kXcds + 1]
+    kCtlSeg2 = kCtlSeg1 + 16,                       // GEMM-2 segment starts [kXcds + 1]
+    kCtlWords = kCtlSeg2 + 16
 };
 
 // Output columns per GEMM task.  GEMM-1 FP8 needs 128 so that one task owns
 // a whole 128-column requantisation group of the intermediate and a single
-// block row of W1's scales; the others use 64 (within one W2 scale block row).
+// block row of W1's scales; bf16 GEMM-1 uses 64; GEMM-2 uses 128 (one W2
+// scale block row).
 inline int gemm1_block_n(int mode) { return mode == MOE_MODE_FP8 ? 128 : 64; }
-inline int gemm2_block_n(int) { return 64; }
+inline int gemm2_block_n(int) { return 128; }
 
 struct RouteArgs {
     const int32_t* ids;
@@ -51,7 +59,7 @@ struct RouteArgs {
     int64_t n_pad_cap, tile_cap;
     int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;
-    int32_t* stats;
+    int32_t* ctl;  // control block [kCtlWords]
     int4* tasks1;
     int4* tasks2;
     unsigned char* zero;  // kZeroBytes to clear (may be null)
@@ -64,7 +72,7 @@ struct Gemm1Args {
     const float* w1_scale;
     const int32_t* row_src;
     const int4* tasks;
-    int32_t* stats;
+    int32_t* ctl;
     const unsigned char* zero;
     void* h;
     float* h_scale;
@@ -79,7 +87,7 @@ struct Gemm2Args {
     const int32_t* row_src;
     const float* topk_w;
     const int4* tasks;
-    int32_t* stats;
+    int32_t* ctl;
     const unsigned char* zero;
     void* y;
     int32_t d_h, d_e;

@@ -7,13 +7,16 @@
 // the expert of each group block).  Here it is produced on the device so that
 // no host round trip of the routing is needed.
 //
-// One workgroup of 16 wave64s does everything in LDS: N = T*k is at most a few
-// ten thousand assignments on the paths this serves, so a single workgroup
-// finishes in a few microseconds and avoids any cross-workgroup protocol.
+// One workgroup of 16 wave64s does everything: N = T*k is at most a few ten
+// thousand assignments on the paths this serves.  Up to kLdsIds ids are read
+// from HBM once, into LDS, and every later pass reads them there; larger N
+// streams them from global memory round by round.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+constexpr int kLdsIds = 16384;
 
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
@@ -26,13 +29,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 
 // Exclusive scan of src[0..n) into dst[0..n], dst[n] = total; n <= 256; run by
 // one full wave.  Each lane owns four consecutive entries.
-__device__ __forceinline__ void wave_exclusive_scan256(const int* src, int* dst, int n, int lane) {
+template <typename F>
+__device__ __forceinline__ void wave_exclusive_scan256(F src, int* dst, int n, int lane) {
     int v[4];
     int local = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         int e = 4 * lane + i;
-        v[i] = e < n ? src[e] : 0;
+        v[i] = e < n ? src(e) : 0;
         local += v[i];
     }
     int incl = wave_inclusive_scan(local, lane);
@@ -60,7 +64,16 @@ __device__ __forceinline__ int upper_index(const int* off, int n, int r) {
     return lo;
 }
 
+// Column blocks cb in [0, nb) of expert rank r that go to XCD x: the task
+// group (r, cb) has global index r*nb + cb and XCD (r*nb + cb) mod 8.
+__device__ __forceinline__ int first_cb_on(int r, int nb, int x) { return (x - r * nb) & (kXcds - 1); }
+__device__ __forceinline__ int cbs_on(int r, int nb, int x) {
+    const int c0 = first_cb_on(r, nb, x);
+    return c0 < nb ? (nb - 1 - c0) / kXcds + 1 : 0;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
+    __shared__ int s_ids[kLdsIds];
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_tiles[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
@@ -70,6 +83,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ int s_order[kMaxExperts];
     __shared__ int s_mt[kMaxExperts];
     __shared__ int s_mtoff[kMaxExperts + 1];
+    __shared__ int s_xpre[2][kXcds][kMaxExperts + 1];  // per list and XCD: tasks of lower ranks
+    __shared__ int s_seg[2][kXcds + 1];
     __shared__ int s_dropped;
 
     const int tid = threadIdx.x;
@@ -77,6 +92,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int wave = tid >> 6;
     const int E = a.E;
     const int N = a.N;
+    const bool in_lds = N <= kLdsIds;
 
     for (int e = tid; e < kMaxExperts; e += kRouteThreads) {
         s_cnt[e] = 0;
@@ -88,10 +104,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         for (int i = tid; i < kZeroBytes / 4; i += kRouteThreads) reinterpret_cast<int*>(a.zero)[i] = 0;
     __syncthreads();
 
-    // 1. histogram (LDS atomics: the counts do not depend on their order)
+    // 1. histogram (LDS atomics: the counts do not depend on their order);
+    // the ids stay in LDS for the scatter when they fit
     int my_drop = 0;
     for (int p = tid; p < N; p += kRouteThreads) {
-        int id = a.ids[p];
+        const int id = a.ids[p];
+        if (in_lds) s_ids[p] = id;
         if ((unsigned)id < (unsigned)E)
             atomicAdd(&s_cnt[id], 1);
         else
@@ -103,10 +121,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // 2. prefix scans of the counts and of the padded counts
     for (int e = tid; e < E; e += kRouteThreads) s_tiles[e] = (s_cnt[e] + kBlockM - 1) / kBlockM;
     __syncthreads();
-    if (wave == 0) wave_exclusive_scan256(s_cnt, s_off, E, lane);
-    if (wave == 1) {
-        wave_exclusive_scan256(s_tiles, s_poff, E, lane);
-    }
+    if (wave == 0) wave_exclusive_scan256([&](int e) { return s_cnt[e]; }, s_off, E, lane);
+    if (wave == 1) wave_exclusive_scan256([&](int e) { return s_tiles[e]; }, s_poff, E, lane);
     __syncthreads();
     for (int e = tid; e <= E; e += kRouteThreads) s_poff[e] *= kBlockM;
     __syncthreads();
@@ -117,18 +133,27 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         a.offsets[e] = s_off[e];
         a.padded_offsets[e] = s_poff[e];
     }
-    for (int64_t i = tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
+    // padding rows of each group and the unused tail of the padded space
+    for (int e = wave; e < E; e += kRouteWaves)
+        for (int r = s_poff[e] + s_cnt[e] + lane; r < s_poff[e + 1]; r += 64) a.row_src[r] = -1;
+    for (int64_t i = n_pad + tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
     for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
-    __syncthreads();
 
     // 3. stable scatter, 1024 assignments per round.  Inside a wave, lanes with
     // the same expert find each other with 9 ballots over the id bits; the rank
     // of an assignment is the count of earlier rounds, of lower waves in this
     // round, and of lower lanes in its own wave.
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int next = (!in_lds && tid < N) ? a.ids[tid] : -1;
     for (int base = 0; base < N; base += kRouteThreads) {
         const int p = base + tid;
-        const int id = p < N ? a.ids[p] : -1;
+        int id;
+        if (in_lds) {
+            id = p < N ? s_ids[p] : -1;
+        } else {
+            id = next;
+            next = p + kRouteThreads < N ? a.ids[p + kRouteThreads] : -1;  // next round's id, in flight
+        }
         const bool valid = (unsigned)id < (unsigned)E;
         const int key = valid ? id : 511;
         uint64_t m = ~0ull;
@@ -177,17 +202,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
     }
     if (tid == 0) {
-        a.stats[kStatDropped] = s_dropped;
-        a.stats[kStatTiles] = ntiles;
-        a.stats[kStatPadRows] = n_pad;
-        a.stats[kStatTasks1] = 0;
+        a.ctl[kStatDropped] = s_dropped;
+        a.ctl[kStatTiles] = ntiles;
+        a.ctl[kStatPadRows] = n_pad;
+        a.ctl[kStatTasks1] = 0;
     }
     if (a.nb1 <= 0) return;
 
-    // 5. task lists.  Experts are ordered by descending row count (ties by id):
+    // 5. task lists.  Experts are ranked by descending row count (ties by id):
     // longest work first.  An expert's tasks are its M-tiles (up to
-    // kMaxRowBlocks group blocks) times the column blocks, M-tile fastest, so
-    // the tasks that read the same weight block are pulled back to back.
+    // kMaxRowBlocks group blocks) times the column blocks.  The task group
+    // (rank r, column block cb) -- every M-tile of one weight block -- goes to
+    // XCD (r*nb + cb) mod 8, so the M-tiles that read the same weights run
+    // side by side on one L2; each XCD's segment of the list keeps rank order.
     for (int e = tid; e < E; e += kRouteThreads) {
         const int c = s_cnt[e];
         int r = 0;
@@ -201,7 +228,22 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     for (int r = tid; r < E; r += kRouteThreads)
         s_mt[r] = (s_tiles[s_order[r]] + kMaxRowBlocks - 1) / kMaxRowBlocks;
     __syncthreads();
-    if (wave == 0) wave_exclusive_scan256(s_mt, s_mtoff, E, lane);
+    {
+        // waves 0..7: GEMM-1 list, XCD = wave; waves 8..15: GEMM-2 list
+        const int list = wave / kXcds, x = wave % kXcds;
+        const int nb = list == 0 ? a.nb1 : a.nb2;
+        wave_exclusive_scan256([&](int r) { return cbs_on(r, nb, x) * s_mt[r]; }, s_xpre[list][x], E, lane);
+    }
+    if (wave == 0) wave_exclusive_scan256([&](int r) { return s_mt[r]; }, s_mtoff, E, lane);
+    __syncthreads();
+    if (tid < 2) {
+        int run = 0;
+        for (int x = 0; x < kXcds; ++x) {
+            s_seg[tid][x] = run;
+            run += s_xpre[tid][x][E];
+        }
+        s_seg[tid][kXcds] = run;
+    }
     __syncthreads();
     const int n_mtiles = s_mtoff[E];
     for (int list = 0; list < 2; ++list) {
@@ -209,21 +251,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
         const int total = n_mtiles * nb;
         for (int i = tid; i < total; i += kRouteThreads) {
-            // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb)
+            // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb), column-major
             const int r = upper_index(s_mtoff, E, i / nb);
             const int mt = s_mt[r];
             const int local = i - s_mtoff[r] * nb;
-            const int col = local / mt;
-            const int m = local - col * mt;
+            const int cb = local / mt;
+            const int m = local - cb * mt;
             const int e = s_order[r];
+            const int x = (r * nb + cb) & (kXcds - 1);
+            const int q = (cb - first_cb_on(r, nb, x)) / kXcds;
             const int nsub = min(kMaxRowBlocks, s_tiles[e] - m * kMaxRowBlocks);
-            tasks[i] = make_int4(e, s_poff[e] + m * kMaxRowBlocks * kBlockM, nsub, col);
+            tasks[s_seg[list][x] + s_xpre[list][x][r] + q * mt + m] =
+                make_int4(e, s_poff[e] + m * kMaxRowBlocks * kBlockM, nsub, cb);
         }
-        if (tid == 0) a.stats[list == 0 ? kStatTasks1 : kStatTasks2] = total;
     }
-    if (tid == 0) {
-        a.stats[kStatCounter1] = 0;
-        a.stats[kStatCounter2] = 0;
+    if (tid < 2) a.ctl[tid == 0 ? kStatTasks1 : kStatTasks2] = s_seg[tid][kXcds];
+    if (tid < 2 * kXcds) a.ctl[(tid < kXcds ? kCtlQueue1 : kCtlQueue2 - kXcds * kQueueStride) + kQueueStride * tid] = 0;
+    if (tid < 2 * (kXcds + 1)) {
+        const int list = tid / (kXcds + 1), x = tid % (kXcds + 1);
+        a.ctl[(list == 0 ? kCtlSeg1 : kCtlSeg2) + x] = s_seg[list][x];
     }
 }
 

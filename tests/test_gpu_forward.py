@@ -47,7 +47,9 @@ def _check(w, oracle, rows=None, label=""):
     d = device.upload(w)
     odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
     out = torch.full((w.T, w.d_h), float("nan"), dtype=odt, device="cuda:0")  # sentinel: every row must be written
-    device.run(d, out=out)
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
+    ws = moe.workspace_for(dims, "cuda:0")
+    device.run(d, out=out, workspace=ws)
     torch.cuda.synchronize()
     g = device.out_to_f64(out)
     assert np.isfinite(g).all(), "unwritten or non-finite output rows"
@@ -153,9 +155,11 @@ def test_forward_routing_and_task_list(oracle):
     assert np.array_equal(arr(L.counts, w.E), r["counts"])
     assert np.array_equal(arr(L.pos, N), r["pos"])
     assert np.array_equal(arr(L.row_src, L.n_pad_cap), r["row_src"])
-    stats = arr(L.stats, 8)
-    for lst, off, nb in ((3, L.tasks1, w.d_e // L.block_n1), (4, L.tasks2, w.d_h // L.block_n2)):
-        nt = int(stats[lst])
+    ctl = arr(L.stats, 304)
+    for lst, off, nb, segw in ((3, L.tasks1, w.d_e // L.block_n1, 272), (4, L.tasks2, w.d_h // L.block_n2, 288)):
+        nt = int(ctl[lst])
+        seg = ctl[segw:segw + 9]
+        assert seg[0] == 0 and seg[8] == nt and np.all(np.diff(seg) >= 0)
         tasks = arr(off, 4 * nt).reshape(nt, 4)
         seen = {}
         for e, row0, nsub, cb in tasks.tolist():
@@ -165,7 +169,18 @@ def test_forward_routing_and_task_list(oracle):
                 assert r["padded_offsets"][e] <= r0 < r["padded_offsets"][e + 1]
                 seen[(r0, cb)] = seen.get((r0, cb), 0) + 1
         assert len(seen) == r["ntiles"] * nb and set(seen.values()) == {1}
-        # longest expert first
-        firsts = [t[0] for t in tasks.tolist()]
-        order = list(dict.fromkeys(firsts))
-        assert [r["counts"][e] for e in order] == sorted([r["counts"][e] for e in order], reverse=True)
+        for x in range(8):
+            part = tasks[seg[x]:seg[x + 1]].tolist()
+            # longest expert first within each XCD's segment
+            counts = [r["counts"][t[0]] for t in part]
+            assert counts == sorted(counts, reverse=True)
+            # every (expert, column block) group lives in one segment, contiguously
+            groups = [(t[0], t[3]) for t in part]
+            assert len(set(groups)) == len(list(dict.fromkeys(groups)))
+            for g in set(groups):
+                idx = [i for i, q in enumerate(groups) if q == g]
+                assert idx == list(range(idx[0], idx[0] + len(idx)))
+        owner = {}
+        for x in range(8):
+            for t in tasks[seg[x]:seg[x + 1]].tolist():
+                assert owner.setdefault((t[0], t[3]), x) == x
