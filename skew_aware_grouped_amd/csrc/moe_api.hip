@@ -32,13 +32,17 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     const int64_t N = (int64_t)d->num_tokens * d->top_k;
     const int64_t E = d->num_experts;
     route_caps(N, E, &L->n_pad_cap, &L->tile_cap);
-    // M-tiles: each expert's blocks grouped kMaxRowBlocks at a time
-    const int64_t mtile_cap = L->tile_cap / kMaxRowBlocks + (E < N ? E : N);
+    // M-tiles: each expert's blocks grouped kMaxRowBlocks1 (GEMM-1) or
+    // kMaxRowBlocks2 (GEMM-2) at a time
+    // (GEMM-1 may fall back to kMaxRowBlocks2-block tiles, so both lists are
+    // sized for those)
+    const int64_t mtile_cap2 = L->tile_cap / kMaxRowBlocks2 + (E < N ? E : N);
+    const int64_t mtile_cap1 = mtile_cap2;
     L->block_n1 = gemm1_block_n(d->mode);
     L->block_n2 = gemm2_block_n(d->mode);
-    L->max_row_blocks = kMaxRowBlocks;
-    L->task1_cap = mtile_cap * (d->d_expert / L->block_n1);
-    L->task2_cap = mtile_cap * (d->d_hidden / L->block_n2);
+    L->max_row_blocks = kMaxRowBlocks1;
+    L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
+    L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
     const size_t hb = d->mode == MOE_MODE_FP8 ? 1 : 2;
     const size_t yb = d->mode == MOE_MODE_F32ACT ? 4 : 2;
     size_t o = 0;
@@ -215,6 +219,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.tile_cap = L.tile_cap;
     r.nb1 = d_e / L.block_n1;
     r.nb2 = d_h / L.block_n2;
+    r.min_tasks1 = cus * occ1;
     r.counts = at<int32_t>(workspace, L.counts);
     r.offsets = at<int32_t>(workspace, L.offsets);
     r.padded_offsets = at<int32_t>(workspace, L.padded_offsets);

@@ -181,18 +181,21 @@ struct Cfg {
     static constexpr int kBRows = GATED ? 2 * kBN : kBN;   // weight rows per task
     static constexpr int kBInstr = kBRows / 8 / kGemmWaves;  // B loads per wave per stage
     static constexpr int kStageB = kBRows * kRowBytes;
-    static constexpr int kStageS = kFP8 ? 512 : 0;  // 64 row scales, then the block scale(s)
+    // FP8: up to 128 row scales (waves 0 and 2), then the block scale(s) (wave 1)
+    static constexpr int kStageS = kFP8 ? 1024 : 0;
     static constexpr int stage_bytes(int nsub) { return kStageB + 16 * nsub * kRowBytes + kStageS; }
-    // ring: four stages of a one-block task (FP8 GEMM-1: one workgroup per
-    // CU; the others: two)
-    static constexpr int kRing = 4 * stage_bytes(1);
+    // ring: FP8 GEMM-1 (256 weight rows per stage) takes a whole CU's LDS
+    // (three stages of a 128-row task, four of a 16-row one); the others take
+    // four stages of a one-block task, so two workgroups share a CU
+    static constexpr int kRing = (GATED && kFP8) ? 160 * 1024 - 256 : 4 * stage_bytes(1);
     // stages in a ring of `ring` bytes
     static constexpr int stages(int nsub, int ring) {
         return ring / stage_bytes(nsub) < 8 ? ring / stage_bytes(nsub) : 8;
     }
     static constexpr int kOutBytes = (MODE == MOE_MODE_F32ACT && !GATED) ? 4 : (GATED && kFP8 ? 1 : 2);
     static constexpr int kEpiRow = kBN * kOutBytes;  // bytes of one staged output row
-    static_assert(kEpiRow * kAMaxRows + 1024 <= kRing, "epilogue staging must fit in the stage ring");
+    static_assert(kEpiRow * kAMaxRows + kGemmWaves * kAMaxRows * 4 <= kRing,
+                  "epilogue staging must fit in the stage ring");
     static_assert(stages(kMaxRowBlocks, kRing) >= 2, "ring too small");
     static_assert(kRing <= 160 * 1024, "LDS budget");
     static_assert(GATED || kBN == 128, "GEMM-2 tasks are 128 columns wide (one W2 scale block row)");
@@ -228,7 +231,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     // (instructions w, w+4, ...) and, in FP8 mode, the row scales (wave 0) or
     // the block scales (wave 1)
     const int n_a = w < kAInstr ? (kAInstr - 1 - w) / kGemmWaves + 1 : 0;
-    const int loads_per_stage = C::kBInstr + n_a + ((kFP8 && w < 2) ? 1 : 0);
+    const int loads_per_stage = C::kBInstr + n_a + ((kFP8 && (w < 2 || (w == 2 && NSUB > 4))) ? 1 : 0);
 
     // ---- per-lane load sources (stage 0); a K block advances them by 128 bytes
     const unsigned char* bsrc[C::kBInstr];
@@ -266,20 +269,21 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             }
         }
     }
-    // scale sources: wave 0 lane r -> row scale of tile row r; wave 1 lane 0
-    // (and 1) -> block scale(s) of W for this K block
+    // scale sources: wave 0 lane r -> row scale of tile row r, wave 2 lane r
+    // -> row 64 + r; wave 1 lane 0 (and 1) -> block scale(s) of W for this K block
     const float* ssrc = nullptr;
     bool son = false, spad = false;
     if constexpr (kFP8) {
         const int kq = K / kQ;
-        if (w == 0 && lane < 16 * NSUB) {
+        const int srow = (w == 2 ? 64 : 0) + lane;
+        if ((w == 0 || w == 2) && srow < 16 * NSUB) {
             son = true;
-            const int p = row_src[row0 + lane];
+            const int p = row_src[row0 + srow];
             if (GATED) {
                 spad = p < 0;
                 ssrc = spad ? reinterpret_cast<const float*>(zero) : a_scale + (int64_t)(p / a_div) * kq;
             } else {
-                ssrc = a_scale + (int64_t)(row0 + lane) * kq;
+                ssrc = a_scale + (int64_t)(row0 + srow) * kq;
             }
         } else if (w == 1 && lane < (GATED ? 2 : 1)) {
             son = true;
@@ -304,7 +308,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         if constexpr (kFP8) {
             // wave 0 reads the row scales, wave 1 the weights' block scales
             const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
-            if (son) g2l4(spad ? ssrc : ssrc + kc, w == 0 ? ss : ss + 256u);
+            if (son) g2l4(spad ? ssrc : ssrc + kc, ss + (unsigned)(w == 1 ? 512 : w * 128));
         }
     };
 
@@ -339,8 +343,8 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             for (int s = 0; s < NSUB; ++s)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sx[s][i] = sc[16 * s + 4 * lg + i];
-            const float swg = sc[64];  // written by lane 0 (and 1) of wave 1
-            const float swu = GATED ? sc[65] : 0.f;
+            const float swg = sc[128];  // written by lane 0 (and 1) of wave 1
+            const float swu = GATED ? sc[129] : 0.f;
 #pragma unroll
             for (int f = 0; f < C::kNFW; ++f) {
                 const int brow = 16 * (C::kNFW * w + f) + lr;
@@ -389,7 +393,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     // ---- epilogue: stage the output tile in LDS, then 16-byte row stores
     __syncthreads();  // every wave is done with the ring
     unsigned char* stage = smem;                                              // [16*NSUB][kEpiRow]
-    float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * kAMaxRows);  // [waves][64]
+    float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * kAMaxRows);  // [waves][kAMaxRows]
     if constexpr (GATED) {
         float hv[NSUB][C::kNFW][4];
 #pragma unroll
@@ -409,7 +413,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     for (int f = 0; f < C::kNFW; ++f) m = fmaxf(m, fabsf(hv[s][f][i]));
 #pragma unroll
                     for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-                    if (lr == 0) s_amax[w * 64 + 16 * s + 4 * lg + i] = m;
+                    if (lr == 0) s_amax[w * kAMaxRows + 16 * s + 4 * lg + i] = m;
                 }
             __syncthreads();
 #pragma unroll
@@ -419,7 +423,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     const int rr = 16 * s + 4 * lg + i;
                     float amax = s_amax[rr];
 #pragma unroll
-                    for (int ww = 1; ww < kGemmWaves; ++ww) amax = fmaxf(amax, s_amax[ww * 64 + rr]);
+                    for (int ww = 1; ww < kGemmWaves; ++ww) amax = fmaxf(amax, s_amax[ww * kAMaxRows + rr]);
                     const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
                     for (int f = 0; f < C::kNFW; ++f)
@@ -506,7 +510,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
             case 1: MOE_G1(1); break;
             case 2: MOE_G1(2); break;
             case 3: MOE_G1(3); break;
-            default: MOE_G1(4); break;
+            case 4: MOE_G1(4); break;
+            case 5: MOE_G1(5); break;
+            case 6: MOE_G1(6); break;
+            case 7: MOE_G1(7); break;
+            default: MOE_G1(8); break;
         }
 #undef MOE_G1
     }

@@ -12,9 +12,14 @@ namespace moe {
 // Rows per group block.  Equal to the M size of the 16x16 MFMA tiles, so a
 // cold expert with a handful of tokens pads to at most 15 rows.
 constexpr int kBlockM = 16;
-// A GEMM task covers up to this many consecutive group blocks of one expert
-// (64 rows); the kernels carry one fully unrolled body per block count.
-constexpr int kMaxRowBlocks = 4;
+// A GEMM-1 task covers up to kMaxRowBlocks1 consecutive group blocks of one
+// expert (128 rows), so a hot expert's W1 is streamed once per 128 of its
+// rows; a GEMM-2 task up to kMaxRowBlocks2 (64 rows: the larger FP8 body
+// would need more registers than two workgroups per CU leave).  The kernels
+// carry one fully unrolled body per block count.
+constexpr int kMaxRowBlocks1 = 8;
+constexpr int kMaxRowBlocks2 = 4;
+constexpr int kMaxRowBlocks = kMaxRowBlocks1;
 // Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = 64 * kGemmWaves;
@@ -58,6 +63,7 @@ struct RouteArgs {
     int32_t N, E;
     int64_t n_pad_cap, tile_cap;
     int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
+    int32_t min_tasks1;  // GEMM-1 takes kMaxRowBlocks1-block M-tiles only if that leaves this many tasks
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;
     int32_t* ctl;  // control block [kCtlWords]
     int4* tasks1;

@@ -81,11 +81,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ int s_base[kMaxExperts];
     __shared__ int s_wcnt[kRouteWaves][kMaxExperts];
     __shared__ int s_order[kMaxExperts];
-    __shared__ int s_mt[kMaxExperts];
-    __shared__ int s_mtoff[kMaxExperts + 1];
+    __shared__ int s_mt[2][kMaxExperts];         // M-tiles per expert rank, per list
+    __shared__ int s_mtoff[2][kMaxExperts + 1];
     __shared__ int s_xpre[2][kXcds][kMaxExperts + 1];  // per list and XCD: tasks of lower ranks
     __shared__ int s_seg[2][kXcds + 1];
-    __shared__ int s_dropped;
+    __shared__ int s_dropped, s_mb1;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
     // 5. task lists.  Experts are ranked by descending row count (ties by id):
     // longest work first.  An expert's tasks are its M-tiles (up to
-    // kMaxRowBlocks group blocks) times the column blocks.  The task group
+    // kMaxRowBlocks1 / kMaxRowBlocks2 group blocks) times the column blocks.  The task group
     // (rank r, column block cb) -- every M-tile of one weight block -- goes to
     // XCD (r*nb + cb) mod 8, so the M-tiles that read the same weights run
     // side by side on one L2; each XCD's segment of the list keeps rank order.
@@ -225,16 +225,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         s_order[r] = e;
     }
     __syncthreads();
-    for (int r = tid; r < E; r += kRouteThreads)
-        s_mt[r] = (s_tiles[s_order[r]] + kMaxRowBlocks - 1) / kMaxRowBlocks;
+    // GEMM-1 M-tiles: kMaxRowBlocks1 blocks (fewer weight re-reads) when that
+    // still leaves min_tasks1 tasks, otherwise kMaxRowBlocks2 (more tasks to
+    // spread over the CUs)
+    if (wave == 0) {
+        int big = 0;
+        for (int e = lane; e < E; e += 64) big += (s_tiles[e] + kMaxRowBlocks1 - 1) / kMaxRowBlocks1;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) big += __shfl_xor(big, d, 64);
+        if (lane == 0) s_mb1 = big * a.nb1 >= a.min_tasks1 ? kMaxRowBlocks1 : kMaxRowBlocks2;
+    }
+    __syncthreads();
+    const int mb1 = s_mb1;
+    for (int r = tid; r < E; r += kRouteThreads) {
+        s_mt[0][r] = (s_tiles[s_order[r]] + mb1 - 1) / mb1;
+        s_mt[1][r] = (s_tiles[s_order[r]] + kMaxRowBlocks2 - 1) / kMaxRowBlocks2;
+    }
     __syncthreads();
     {
         // waves 0..7: GEMM-1 list, XCD = wave; waves 8..15: GEMM-2 list
         const int list = wave / kXcds, x = wave % kXcds;
         const int nb = list == 0 ? a.nb1 : a.nb2;
-        wave_exclusive_scan256([&](int r) { return cbs_on(r, nb, x) * s_mt[r]; }, s_xpre[list][x], E, lane);
+        wave_exclusive_scan256([&](int r) { return cbs_on(r, nb, x) * s_mt[list][r]; }, s_xpre[list][x], E,
+                               lane);
     }
-    if (wave == 0) wave_exclusive_scan256([&](int r) { return s_mt[r]; }, s_mtoff, E, lane);
+    if (wave < 2) wave_exclusive_scan256([&](int r) { return s_mt[wave][r]; }, s_mtoff[wave], E, lane);
     __syncthreads();
     if (tid < 2) {
         int run = 0;
@@ -245,24 +260,24 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         s_seg[tid][kXcds] = run;
     }
     __syncthreads();
-    const int n_mtiles = s_mtoff[E];
     for (int list = 0; list < 2; ++list) {
         const int nb = list == 0 ? a.nb1 : a.nb2;
+        const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
         int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
-        const int total = n_mtiles * nb;
+        const int total = s_mtoff[list][E] * nb;
         for (int i = tid; i < total; i += kRouteThreads) {
             // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb), column-major
-            const int r = upper_index(s_mtoff, E, i / nb);
-            const int mt = s_mt[r];
-            const int local = i - s_mtoff[r] * nb;
+            const int r = upper_index(s_mtoff[list], E, i / nb);
+            const int mt = s_mt[list][r];
+            const int local = i - s_mtoff[list][r] * nb;
             const int cb = local / mt;
             const int m = local - cb * mt;
             const int e = s_order[r];
             const int x = (r * nb + cb) & (kXcds - 1);
             const int q = (cb - first_cb_on(r, nb, x)) / kXcds;
-            const int nsub = min(kMaxRowBlocks, s_tiles[e] - m * kMaxRowBlocks);
+            const int nsub = min(mb, s_tiles[e] - m * mb);
             tasks[s_seg[list][x] + s_xpre[list][x][r] + q * mt + m] =
-                make_int4(e, s_poff[e] + m * kMaxRowBlocks * kBlockM, nsub, cb);
+                make_int4(e, s_poff[e] + m * mb * kBlockM, nsub, cb);
         }
     }
     if (tid < 2) a.ctl[tid == 0 ? kStatTasks1 : kStatTasks2] = s_seg[tid][kXcds];
