@@ -8,9 +8,9 @@
 // no host round trip of the routing is needed.
 //
 // One workgroup of 16 wave64s does everything: N = T*k is at most a few ten
-// thousand assignments on the paths this serves.  Up to kLdsIds ids are read
-// from HBM once, into LDS, and every later pass reads them there; larger N
-// streams them from global memory round by round.
+// thousand assignments on the paths this serves.  Each wave owns a contiguous
+// chunk of the assignments.  Up to kLdsIds ids are read from HBM once, into
+// LDS, and the scatter reads them there; larger N reads them twice.
 #include "moe_internal.h"
 
 namespace moe {
@@ -78,7 +78,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ int s_tiles[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
     __shared__ int s_poff[kMaxExperts + 1];
-    __shared__ int s_base[kMaxExperts];
     __shared__ int s_wcnt[kRouteWaves][kMaxExperts];
     __shared__ int s_order[kMaxExperts];
     __shared__ int s_mt[2][kMaxExperts];         // M-tiles per expert rank, per list
@@ -94,32 +93,45 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int N = a.N;
     const bool in_lds = N <= kLdsIds;
 
-    for (int e = tid; e < kMaxExperts; e += kRouteThreads) {
-        s_cnt[e] = 0;
-        s_base[e] = 0;
-    }
     for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
     if (tid == 0) s_dropped = 0;
     if (a.zero)
         for (int i = tid; i < kZeroBytes / 4; i += kRouteThreads) reinterpret_cast<int*>(a.zero)[i] = 0;
     __syncthreads();
 
-    // 1. histogram (LDS atomics: the counts do not depend on their order);
-    // the ids stay in LDS for the scatter when they fit
+    // Wave w owns the contiguous chunk [w*chunk, (w+1)*chunk) of the flat
+    // assignments (chunk a multiple of 64), so ranks follow ascending p
+    // across waves, then across the wave's 64-wide steps, then across lanes.
+    const int chunk = ((N + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
+    const int c_lo = wave * chunk;
+    const int c_hi = min(N, c_lo + chunk);
+
+    // 1. per-wave histograms (LDS atomics on the wave's own row); the ids
+    // stay in LDS for the scatter when they fit
     int my_drop = 0;
-    for (int p = tid; p < N; p += kRouteThreads) {
+    for (int p = c_lo + lane; p < c_hi; p += 64) {
         const int id = a.ids[p];
         if (in_lds) s_ids[p] = id;
         if ((unsigned)id < (unsigned)E)
-            atomicAdd(&s_cnt[id], 1);
+            atomicAdd(&s_wcnt[wave][id], 1);
         else
             ++my_drop;
     }
     if (my_drop) atomicAdd(&s_dropped, my_drop);
     __syncthreads();
 
-    // 2. prefix scans of the counts and of the padded counts
-    for (int e = tid; e < E; e += kRouteThreads) s_tiles[e] = (s_cnt[e] + kBlockM - 1) / kBlockM;
+    // 2. counts, then each wave's rank base per expert (earlier waves' counts),
+    // then the prefix scans of the counts and of the padded counts
+    for (int e = tid; e < E; e += kRouteThreads) {
+        int run = 0;
+        for (int w = 0; w < kRouteWaves; ++w) {
+            const int c = s_wcnt[w][e];
+            s_wcnt[w][e] = run;
+            run += c;
+        }
+        s_cnt[e] = run;
+        s_tiles[e] = (run + kBlockM - 1) / kBlockM;
+    }
     __syncthreads();
     if (wave == 0) wave_exclusive_scan256([&](int e) { return s_cnt[e]; }, s_off, E, lane);
     if (wave == 1) wave_exclusive_scan256([&](int e) { return s_tiles[e]; }, s_poff, E, lane);
@@ -139,21 +151,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     for (int64_t i = n_pad + tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
     for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
 
-    // 3. stable scatter, 1024 assignments per round.  Inside a wave, lanes with
-    // the same expert find each other with 9 ballots over the id bits; the rank
-    // of an assignment is the count of earlier rounds, of lower waves in this
-    // round, and of lower lanes in its own wave.
+    // 3. stable scatter: each wave walks its chunk 64 assignments at a time.
+    // Lanes with the same expert find each other with 9 ballots over the id
+    // bits; the rank of an assignment is its wave's running base for that
+    // expert plus the number of lower lanes with the same expert.  The
+    // lowest such lane then advances the base.  No workgroup barrier: the
+    // bases of a wave are its own.
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int next = (!in_lds && tid < N) ? a.ids[tid] : -1;
-    for (int base = 0; base < N; base += kRouteThreads) {
-        const int p = base + tid;
-        int id;
-        if (in_lds) {
-            id = p < N ? s_ids[p] : -1;
-        } else {
-            id = next;
-            next = p + kRouteThreads < N ? a.ids[p + kRouteThreads] : -1;  // next round's id, in flight
-        }
+    for (int base = c_lo; base < c_lo + chunk; base += 64) {
+        const int p = base + lane;
+        const int id = p < c_hi ? (in_lds ? s_ids[p] : a.ids[p]) : -1;
         const bool valid = (unsigned)id < (unsigned)E;
         const int key = valid ? id : 511;
         uint64_t m = ~0ull;
@@ -164,30 +171,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             m &= bit ? bal : ~bal;
         }
         const int wrank = __popcll(m & lt_mask);
-        if (valid && wrank == 0) s_wcnt[wave][id] = __popcll(m);
-        __syncthreads();
         if (valid) {
-            int r = s_base[id] + wrank;
-            for (int w = 0; w < wave; ++w) r += s_wcnt[w][id];
+            const int r = s_wcnt[wave][id] + wrank;
             a.pos[p] = s_off[id] + r;
             a.ppos[p] = s_poff[id] + r;
             a.sorted_p[s_off[id] + r] = p;
             a.row_src[s_poff[id] + r] = p;
-        } else if (p < N) {
+        } else if (p < c_hi) {
             a.pos[p] = -1;
             a.ppos[p] = -1;
         }
-        __syncthreads();
-        for (int e = tid; e < E; e += kRouteThreads) {
-            int s = 0;
-            for (int w = 0; w < kRouteWaves; ++w) {
-                s += s_wcnt[w][e];
-                s_wcnt[w][e] = 0;
-            }
-            s_base[e] += s;
-        }
-        __syncthreads();
+        // every lane has read its base above (the wave's LDS accesses stay in
+        // order); the first lane of each expert group advances it
+        if (valid && wrank == 0) s_wcnt[wave][id] += __popcll(m);
     }
+    __syncthreads();
 
     // 4. block map: expert and first padded row of each group block
     const int ntiles = n_pad / kBlockM;
