@@ -182,14 +182,13 @@ def main():
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
     cold_ms, _ = timed_steps(min(args.steps, 20), flush)
     del flush
-    # per-kernel durations: the stage-event variant records an event between
-    # the kernels (each event adds a few microseconds of launch gap, so these
-    # steps are not the ones the headline p50 comes from)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # per-kernel durations: the kernel-timing variant has each dispatch record
+    # its own start and end (what a kernel trace reports), in separate steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
     for i in range(args.steps):
         device.run(d, out=out, workspace=ws, stream=stream, events=ev[i])
     torch.cuda.synchronize()
-    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+    stage_ms = np.array([[e[2 * j].elapsed_time(e[2 * j + 1]) for j in range(4)] for e in ev])
     p50 = float(np.median(step_ms))
     flops = W.flops(w)
     alg_bytes = W.algorithmic_bytes(w)

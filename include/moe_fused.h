@@ -104,11 +104,12 @@ MOE_API int moe_fused_forward(const moe_dims* dims, const void* x, const int32_t
                       const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* moe_fused_forward with stage timing: records events[0..4] (hipEvent_t,
- * created by the caller) on `stream` before routing, before GEMM-1, before
- * GEMM-2, before the combine and after the combine, so the caller can time
- * each kernel with hipEventElapsedTime.  Same result and errors as
- * moe_fused_forward; MOE_ERR_INVALID_ARG if events or any of its 5 entries is
+/* moe_fused_forward with kernel timing: events[0..7] (hipEvent_t, created by
+ * the caller with timing enabled) receive the start and end of the routing,
+ * GEMM-1, GEMM-2 and combine kernels as their dispatches record them
+ * (events[2i] start, events[2i+1] end of kernel i), so hipEventElapsedTime on
+ * a pair gives that kernel's duration.  Same result and errors as
+ * moe_fused_forward; MOE_ERR_INVALID_ARG if events or any of its 8 entries is
  * NULL. */
 MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, const int32_t* topk_ids,
                                        const float* topk_w, const void* w1, const void* w2,

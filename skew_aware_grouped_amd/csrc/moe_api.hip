@@ -206,9 +206,8 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     int cus = 0, occ1 = 1, occ2 = 1;
     if (device_info(mode, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    auto mark = [&](int i) -> bool {
-        return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
-    };
+    // timing events of launch i (route, GEMM-1, GEMM-2, combine), or none
+    auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
     const int32_t E = dims->num_experts, k = dims->top_k, d_h = dims->d_hidden, d_e = dims->d_expert;
 
     RouteArgs r{};
@@ -233,7 +232,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.tasks1 = at<int4>(workspace, L.tasks1);
     r.tasks2 = at<int4>(workspace, L.tasks2);
     r.zero = at<unsigned char>(workspace, L.zero);
-    if (!mark(0) || launch_route(r, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_route(r, s, ev(0), ev(1)) != hipSuccess) return MOE_ERR_HIP;
     const void* xg = x;
     if (mode == MOE_MODE_F32ACT) {
         uint16_t* xb = at<uint16_t>(workspace, L.x_bf16);
@@ -256,7 +255,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.d_h = d_h;
     g1.d_e = d_e;
     const int64_t grid1 = std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1);
-    if (!mark(1) || launch_gemm1(mode, g1, (int)std::max<int64_t>(grid1, 1), s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm1(mode, g1, (int)std::max<int64_t>(grid1, 1), s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
 
     Gemm2Args g2{};
     g2.h = g1.h;
@@ -272,7 +271,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.d_h = d_h;
     g2.d_e = d_e;
     const int64_t grid2 = std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2);
-    if (!mark(2) || launch_gemm2(mode, g2, (int)std::max<int64_t>(grid2, 1), s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm2(mode, g2, (int)std::max<int64_t>(grid2, 1), s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
 
     CombineArgs c{};
     c.y = g2.y;
@@ -282,7 +281,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     c.k = k;
     c.E = E;
     c.d_h = d_h;
-    if (!mark(3) || launch_combine(mode, c, s) != hipSuccess || !mark(4)) return MOE_ERR_HIP;
+    if (launch_combine(mode, c, s, ev(6), ev(7)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
 
@@ -297,7 +296,7 @@ int moe_fused_forward_profiled(const moe_dims* dims, const void* x, const int32_
                                const void* w1, const void* w2, const moe_scales* scales, void* out,
                                void* workspace, size_t workspace_bytes, void* stream, void* const* events) {
     if (!events) return MOE_ERR_INVALID_ARG;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 8; ++i)
         if (!events[i]) return MOE_ERR_INVALID_ARG;
     return forward_impl(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,
                         events);

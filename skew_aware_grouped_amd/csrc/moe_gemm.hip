@@ -616,32 +616,32 @@ hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s) {
+hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (mode == MOE_MODE_FP8)
-        hipLaunchKernelGGL(gemm1_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else
-        hipLaunchKernelGGL(gemm1_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s) {
+hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     if (mode == MOE_MODE_FP8)
-        hipLaunchKernelGGL(gemm2_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_BF16)
-        hipLaunchKernelGGL(gemm2_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else
-        hipLaunchKernelGGL(gemm2_kernel<MOE_MODE_F32ACT>, dim3(grid), dim3(kGemmThreads), 0, s, a);
+        hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_F32ACT>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 
-hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s) {
+hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const int64_t n = (int64_t)a.T * (a.d_h / 8);
     const int blocks = (int)((n + 255) / 256);
     if (blocks == 0) return hipSuccess;
     if (mode == MOE_MODE_F32ACT)
-        hipLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL(combine_kernel<true>, dim3(blocks), dim3(256), 0, s, t0, t1, 0, a);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, a);
+        hipExtLaunchKernelGGL(combine_kernel<false>, dim3(blocks), dim3(256), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 

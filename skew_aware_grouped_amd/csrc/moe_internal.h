@@ -2,6 +2,7 @@
 // library (kernels and the C-ABI host code).  Not installed, not part of the ABI.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -106,12 +107,17 @@ struct CombineArgs {
     int32_t T, k, E, d_h;
 };
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Launchers.  With t0/t1 (timing events created by the caller) the kernel's
+// own start and end are recorded, as the dispatch sees them.
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // x fp32 -> bf16 (round to nearest even), n elements, multiple of 8
 hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s);
-hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s);
-hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s);
-hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s);
+hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
+hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
+hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
+                          hipEvent_t t1 = nullptr);
 // Resident workgroups per CU of the persistent GEMM kernels (occupancy query).
 hipError_t gemm_occupancy(int mode, int* g1_blocks_per_cu, int* g2_blocks_per_cu);
 

@@ -288,8 +288,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 
 }  // namespace
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, a);
+hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+    hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 

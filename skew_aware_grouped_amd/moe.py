@@ -110,7 +110,7 @@ def moe_fused_forward(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace,
 
 def moe_fused_forward_profiled(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,
                                events) -> int:
-    ev = (ctypes.c_void_p * 5)(*events) if events is not None else None
+    ev = (ctypes.c_void_p * 8)(*events) if events is not None else None
     return int(lib().moe_fused_forward_profiled(ctypes.byref(dims), x, topk_ids, topk_w, w1, w2,
                                                 ctypes.byref(scales) if scales is not None else None, out,
                                                 workspace, workspace_bytes, stream, ev))
@@ -186,7 +186,8 @@ def make_dims(x, topk_ids, w1, mode: Optional[int] = None) -> moe_dims:
 def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=None, w2_scale=None,
                   workspace=None, stream=None, events=None):
     """Run ``moe_fused_forward`` on torch device tensors; returns ``out``.  With
-    ``events`` (5 torch.cuda.Event objects) the stage-timing variant is used."""
+    ``events`` (8 torch.cuda.Event objects: start and end of the routing, GEMM-1,
+    GEMM-2 and combine kernels) the kernel-timing variant is used."""
     import torch
     dims = make_dims(x, topk_ids, w1)
     if out is None:
