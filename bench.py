@@ -9,7 +9,11 @@ time, TFLOP/s at that p50 (algorithmic FLOPs = 6*d_h*d_e per valid
 assignment), the dominant kernel's roofline fraction from its own event-timed
 duration, and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+The weights are rewritten once, before any timing, into the packed tile order
+(moe_pack_weights), as a deployment does when it loads them; ``--weights
+row-major`` times the layer on the weights as given instead.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--weights packed|row-major] [--no-cpu]
 """
 import argparse
 import json
@@ -54,7 +58,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, workload, weights):
     """HBM-side bytes per launch from the committed counter summary
     (profiles/, FETCH_SIZE + WRITE_SIZE scaled by a copy of known size), or
     None when no record exists or the kernel sources changed since it was taken."""
@@ -68,7 +72,7 @@ def measured_traffic(kernel, workload):
                     continue
                 rec = json.loads(line[len("traffic_record:"):])
                 if rec.get("kernel") == kernel and rec.get("workload") == workload and \
-                        rec.get("source_sha256_16") == src:
+                        rec.get("weights", "row-major") == weights and rec.get("source_sha256_16") == src:
                     return float(rec["traffic_bytes"])
     return None
 
@@ -121,6 +125,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--weights", choices=["packed", "row-major"], default="packed",
+                    help="weight layout the layer reads (packing happens once, outside the timed region)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (for scaling profiler byte counters)")
@@ -138,8 +144,8 @@ def main():
         copy_calibration(args.copy_calibration_mb)
         return
     w = W.config(args.config)
-    d = device.upload(w)
-    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
+    d = device.upload(w, packed=args.weights == "packed")
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], weight_layout=d["weight_layout"])
     ws = moe.workspace_for(dims, "cuda:0")
     odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
     out = torch.empty(w.T, w.d_h, dtype=odt, device="cuda:0")
@@ -209,7 +215,7 @@ def main():
     else:
         roof = {"kernel": "gemm1_kernel", "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": measured_traffic("gemm1_kernel", w.name), "alg_bytes_per_launch": g1_bytes,
+    roof.update({"traffic": measured_traffic("gemm1_kernel", w.name, args.weights), "alg_bytes_per_launch": g1_bytes,
                  "alg_flops_per_launch": g1_flops, "avg_launch_us": round(k_us, 2)})
     res = {
         "metric": METRIC,
@@ -226,7 +232,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": w.T, "experts": w.E, "top_k": w.k, "d_hidden": w.d_h,
                    "d_expert": w.d_e, "active_experts": w.active_experts(),
-                   "valid_assignments": w.valid_assignments(), "routing": str(w.meta.get("routing"))},
+                   "valid_assignments": w.valid_assignments(), "routing": str(w.meta.get("routing")),
+                   "weight_layout": args.weights},
         "p50_us": round(p50 * 1e3, 2),
         "p10_us": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
         "p90_us": round(float(np.percentile(step_ms, 90)) * 1e3, 2),

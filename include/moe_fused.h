@@ -52,16 +52,27 @@ extern "C" {
 #define MOE_MODE_BF16 1
 #define MOE_MODE_FP8 2
 
+/* Storage order of W1 and W2 (moe_dims.weight_layout):
+ *  MOE_WEIGHTS_ROW_MAJOR  w1 [E, 2*d_e, d_h], w2 [E, d_h, d_e] as described for
+ *                         moe_fused_forward.
+ *  MOE_WEIGHTS_PACKED     the tile order moe_pack_weights writes: the same
+ *                         bytes, permuted so that every weight tile a GEMM
+ *                         task streams is one contiguous block. */
+#define MOE_WEIGHTS_ROW_MAJOR 0
+#define MOE_WEIGHTS_PACKED 1
+
 /* Layer shape.  Supported envelope: 0 <= num_tokens, 1 <= num_experts <= 256,
  * 1 <= top_k <= 8, num_tokens*top_k < 2^31, d_hidden and d_expert positive
- * multiples of 128. */
+ * multiples of 128.  Zero-initialising weight_layout selects row-major
+ * weights. */
 typedef struct {
-    int32_t mode;        /* MOE_MODE_* */
-    int32_t num_tokens;  /* T */
-    int32_t num_experts; /* E */
-    int32_t top_k;       /* k */
-    int32_t d_hidden;    /* d_h */
-    int32_t d_expert;    /* d_e */
+    int32_t mode;          /* MOE_MODE_* */
+    int32_t num_tokens;    /* T */
+    int32_t num_experts;   /* E */
+    int32_t top_k;         /* k */
+    int32_t d_hidden;      /* d_h */
+    int32_t d_expert;      /* d_e */
+    int32_t weight_layout; /* MOE_WEIGHTS_* */
 } moe_dims;
 
 /* FP8 block scales (fp32, dequantised value = code * scale).  Required in
@@ -91,6 +102,7 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
  *  topk_w    [T, k] fp32         routing weights, used as given
  *  w1        [E, 2*d_e, d_h]     rows [0,d_e) gate, [d_e,2*d_e) up; K (d_h) contiguous
  *  w2        [E, d_h, d_e]       K (d_e) contiguous
+ *                                (with MOE_WEIGHTS_PACKED: the outputs of moe_pack_weights)
  *  scales    FP8 mode only (may be NULL otherwise)
  *  out       [T, d_h]            fp32 (F32ACT) or bf16; every row is written
  *  workspace device buffer of at least moe_workspace_bytes(dims) bytes, 256-byte aligned
@@ -115,6 +127,29 @@ MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, cons
                                        const float* topk_w, const void* w1, const void* w2,
                                        const moe_scales* scales, void* out, void* workspace,
                                        size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * Rewrite row-major W1 and W2 (bf16 or e4m3 as dims->mode says) into the
+ * packed tile order, once, when the weights are loaded; the forward call then
+ * streams each task's weight tile as one contiguous block instead of one
+ * 128-byte piece per weight row (dims->weight_layout is ignored here).  The
+ * permutation moves 16-byte chunks; block scales keep their layout.
+ *
+ * With eb bytes per element (2 for bf16, 1 for e4m3) and the column-block
+ * widths of moe_ws_layout (block_n1: 64 in the bf16 modes, 128 in FP8 mode;
+ * block_n2: 128), let R1 = d_h*eb/128 and R2 = d_e*eb/128 (128-byte K blocks
+ * per weight row), n1 = d_e/block_n1, n2 = d_h/128.  Then, for 0 <= s < 8:
+ *  w1_packed chunk (((e*n1 + c)*R1 + b)*2*block_n1 + r)*8 + s holds bytes
+ *    [128*b + 16*(s ^ (r & 7)), +16) of W1[e] row c*block_n1 + r (gate rows,
+ *    r < block_n1) or d_e + c*block_n1 + r - block_n1 (up rows);
+ *  w2_packed chunk (((e*n2 + c)*R2 + b)*128 + r)*8 + s holds bytes
+ *    [128*b + 16*(s ^ (r & 7)), +16) of W2[e] row c*128 + r.
+ * The packed buffers have the byte sizes of w1 and w2, are caller-owned,
+ * 16-byte aligned and must not overlap the inputs.  MOE_ERR_INVALID_ARG for
+ * invalid dims, a null or misaligned pointer, or overlapping buffers.
+ */
+MOE_API int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void* w1_packed,
+                             void* w2_packed, void* stream);
 
 /* Rows per group block: each expert's group of routed rows is padded to a
  * multiple of this (tilelang.dataflow README section 3.5, "padded offsets"). */

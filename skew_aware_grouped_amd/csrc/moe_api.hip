@@ -20,6 +20,7 @@ bool dims_ok(const moe_dims* d) {
     if (d->top_k < 1 || d->top_k > 8) return false;
     if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return false;
     if (d->d_hidden < 128 || d->d_hidden % 128 || d->d_expert < 128 || d->d_expert % 128) return false;
+    if (d->weight_layout != MOE_WEIGHTS_ROW_MAJOR && d->weight_layout != MOE_WEIGHTS_PACKED) return false;
     return true;
 }
 
@@ -186,7 +187,8 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!dims_ok(dims)) {
         // shape fields present but outside the envelope
         if (dims->mode < 0 || dims->mode > 2 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
-            dims->d_hidden <= 0 || dims->d_expert <= 0)
+            dims->d_hidden <= 0 || dims->d_expert <= 0 ||
+            (dims->weight_layout != MOE_WEIGHTS_ROW_MAJOR && dims->weight_layout != MOE_WEIGHTS_PACKED))
             return MOE_ERR_INVALID_ARG;
         return MOE_ERR_UNSUPPORTED;
     }
@@ -254,6 +256,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.k = k;
     g1.d_h = d_h;
     g1.d_e = d_e;
+    g1.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
     const int64_t grid1 = std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1);
     if (launch_gemm1(mode, g1, (int)std::max<int64_t>(grid1, 1), s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
 
@@ -270,6 +273,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.y = at<void>(workspace, L.y);
     g2.d_h = d_h;
     g2.d_e = d_e;
+    g2.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
     const int64_t grid2 = std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2);
     if (launch_gemm2(mode, g2, (int)std::max<int64_t>(grid2, 1), s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
 
@@ -282,6 +286,32 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     c.E = E;
     c.d_h = d_h;
     if (launch_combine(mode, c, s, ev(6), ev(7)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void* w1_packed, void* w2_packed,
+                     void* stream) {
+    if (!dims) return MOE_ERR_INVALID_ARG;
+    moe_dims d = *dims;
+    d.weight_layout = MOE_WEIGHTS_ROW_MAJOR;  // the packing itself ignores the field
+    if (!dims_ok(&d)) return MOE_ERR_INVALID_ARG;
+    if (!w1 || !w2 || !w1_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1_packed) || !aligned16(w2_packed)) return MOE_ERR_INVALID_ARG;
+    const int64_t eb = d.mode == MOE_MODE_FP8 ? 1 : 2;
+    const int64_t E = d.num_experts, d_h = d.d_hidden, d_e = d.d_expert;
+    const int64_t b1 = E * 2 * d_e * d_h * eb, b2 = E * d_h * d_e * eb;
+    auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+        const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+        return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+    };
+    if (overlap(w1_packed, b1, w1, b1) || overlap(w1_packed, b1, w2, b2) || overlap(w2_packed, b2, w1, b1) ||
+        overlap(w2_packed, b2, w2, b2) || overlap(w1_packed, b1, w2_packed, b2))
+        return MOE_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_pack(w1, w1_packed, E, d_e, d_h * eb, gemm1_block_n(d.mode), true, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_pack(w2, w2_packed, E, d_h, d_e * eb, gemm2_block_n(d.mode), false, s) != hipSuccess)
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -38,6 +38,8 @@
 // accumulator with (row scale of x or h) * (block scale of W): the block
 // dequantisation happens in registers.  The row and block scales of each K
 // block ride in the same LDS stage as the operands.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -212,8 +214,8 @@ struct Cfg {
 template <int MODE, bool GATED, int NSUB, int RING>
 __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_scale, const int32_t* row_src,
                                           int a_div, const void* wts, const float* w_scale, const unsigned char* zero,
-                                          int e, int row0, int cb, int K, int N_out, unsigned char* smem,
-                                          const Gemm1Args* g1, const Gemm2Args* g2) {
+                                          int e, int row0, int cb, int K, int N_out, bool packed,
+                                          unsigned char* smem, const Gemm1Args* g1, const Gemm2Args* g2) {
     using C = Cfg<MODE, GATED>;
     constexpr bool kFP8 = C::kFP8;
     constexpr int S = C::stages(NSUB, RING);
@@ -233,10 +235,20 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     const int n_a = w < kAInstr ? (kAInstr - 1 - w) / kGemmWaves + 1 : 0;
     const int loads_per_stage = C::kBInstr + n_a + ((kFP8 && (w < 2 || (w == 2 && NSUB > 4))) ? 1 : 0);
 
-    // ---- per-lane load sources (stage 0); a K block advances them by 128 bytes
+    // ---- per-lane load sources (stage 0); a K block advances the A sources by
+    // 128 bytes and the B sources by b_step: 128 bytes in row-major weights,
+    // a whole stage in packed ones, where the stages of task (e, cb) follow
+    // each other and each holds its rows already in the swizzled LDS order
     const unsigned char* bsrc[C::kBInstr];
+    const int64_t b_step = packed ? C::kStageB : kRowBytes;
 #pragma unroll
     for (int j = 0; j < C::kBInstr; ++j) {
+        if (packed) {
+            const int64_t tile = (int64_t)e * (N_out / C::kBN) + cb;
+            bsrc[j] = static_cast<const unsigned char*>(wts) + tile * nk * C::kStageB +
+                      ((w * C::kBInstr + j) * 64 + lane) * 16;
+            continue;
+        }
         const int r = (w * C::kBInstr + j) * 8 + (lane >> 3);  // tile row
         const int c = (lane & 7) ^ (r & 7);
         int64_t wrow;
@@ -298,8 +310,9 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     auto issue = [&](int kc) {
         const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
         const int64_t koff = (int64_t)kc * kRowBytes;
+        const int64_t boff = (int64_t)kc * b_step;
 #pragma unroll
-        for (int j = 0; j < C::kBInstr; ++j) g2l16(bsrc[j] + koff, st + (unsigned)((w * C::kBInstr + j) * 1024));
+        for (int j = 0; j < C::kBInstr; ++j) g2l16(bsrc[j] + boff, st + (unsigned)((w * C::kBInstr + j) * 1024));
 #pragma unroll
         for (int j = 0; j < kAMaxPerWave; ++j) {
             const int ai = w + kGemmWaves * j;
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
         const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
 #define MOE_G1(NS)                                                                                                \
     gemm_task<GM, true, NS, RING>(a.x, a.x_scale, a.row_src, a.k, a.w1, a.w1_scale, a.zero, e, row0, cb, a.d_h, a.d_e, \
-                                  smem, &a, nullptr)
+                                  a.packed != 0, smem, &a, nullptr)
         switch (nsub) {
             case 1: MOE_G1(1); break;
             case 2: MOE_G1(2); break;
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
         const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
 #define MOE_G2(NS)                                                                                                 \
     gemm_task<MODE, false, NS, RING>(a.h, a.h_scale, a.row_src, 1, a.w2, a.w2_scale, a.zero, e, row0, cb, a.d_e, a.d_h, \
-                                     smem, nullptr, &a)
+                                     a.packed != 0, smem, nullptr, &a)
         switch (nsub) {
             case 1: MOE_G2(1); break;
             case 2: MOE_G2(2); break;
@@ -607,7 +620,43 @@ __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float* x, uint16_t
     reinterpret_cast<uint4*>(xb)[i] = o;
 }
 
+// Packed tile order: output chunk q (16 bytes) = ((tile * kb + b) * rows + r) * 8 + s
+// for tile = e * (n_out / bn) + c, rows = bn (or 2 bn gated: gate rows, then
+// up rows), holding 16-byte chunk s ^ (r & 7) of K block b of the tile's row
+// r, i.e. exactly what the GEMM's direct-to-LDS loads place in slot s of LDS
+// row r.  A grid-stride loop over output chunks; a one-time rewrite, so plain
+// 64-bit index arithmetic.
+__global__ __launch_bounds__(256) void pack_kernel(const uint4* w, uint4* wp, int64_t nchunks, int64_t n_out,
+                                                   int64_t kb, int bn, int gated) {
+    const int64_t rows = gated ? 2 * (int64_t)bn : bn;
+    const int64_t ncb = n_out / bn;
+    const int64_t rows_per_e = gated ? 2 * n_out : n_out;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nchunks;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const int s = (int)(q & 7);
+        int64_t t = q >> 3;
+        const int r = (int)(t % rows);
+        t /= rows;
+        const int64_t b = t % kb;
+        t /= kb;
+        const int64_t c = t % ncb, e = t / ncb;
+        const int64_t row = !gated || r < bn ? c * bn + r : n_out + c * bn + (r - bn);
+        wp[q] = w[((e * rows_per_e + row) * kb + b) * 8 + (s ^ (r & 7))];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pack(const void* w, void* wp, int64_t E, int64_t n_out, int64_t k_bytes, int bn, bool gated,
+                       hipStream_t s) {
+    const int64_t nchunks = E * (gated ? 2 : 1) * n_out * (k_bytes / 16);
+    if (nchunks == 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((nchunks + 255) / 256, 65536);
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<const uint4*>(w), static_cast<uint4*>(wp), nchunks, n_out, k_bytes / 128, bn,
+                       gated ? 1 : 0);
+    return hipGetLastError();
+}
 
 hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s) {
     const int64_t n8 = n / 8;

@@ -84,6 +84,7 @@ struct Gemm1Args {
     void* h;
     float* h_scale;
     int32_t k, d_h, d_e;
+    int32_t packed;  // W1 in the packed tile order
 };
 
 struct Gemm2Args {
@@ -98,6 +99,7 @@ struct Gemm2Args {
     const unsigned char* zero;
     void* y;
     int32_t d_h, d_e;
+    int32_t packed;  // W2 in the packed tile order
 };
 
 struct CombineArgs {
@@ -112,6 +114,10 @@ struct CombineArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // x fp32 -> bf16 (round to nearest even), n elements, multiple of 8
 hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s);
+// W (row-major [E][rows][K bytes]) -> packed tile order for tasks of `bn`
+// output columns (gated: gate and up rows of a column block together)
+hipError_t launch_pack(const void* w, void* wp, int64_t E, int64_t n_out, int64_t k_bytes, int bn, bool gated,
+                       hipStream_t s);
 hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
 hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,

@@ -8,7 +8,9 @@ from . import moe
 from .workloads import MODE_BF16, MODE_F32ACT, MODE_FP8, MoEWorkload
 
 
-def upload(w: MoEWorkload, device="cuda:0") -> dict:
+def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
+    """Device copies of the workload's tensors; with ``packed`` the weights are
+    rewritten once into the packed tile order (moe_pack_weights)."""
     import torch
 
     def t(a, dt=None):
@@ -34,13 +36,17 @@ def upload(w: MoEWorkload, device="cuda:0") -> dict:
         d["x_scale"] = d["w1_scale"] = d["w2_scale"] = None
     d["topk_ids"] = t(w.topk_ids.astype(np.int32))
     d["topk_w"] = t(w.topk_w.astype(np.float32))
+    d["weight_layout"] = moe.MOE_WEIGHTS_ROW_MAJOR
+    if packed:
+        d["w1"], d["w2"] = moe.pack_weights(d["w1"], d["w2"])
+        d["weight_layout"] = moe.MOE_WEIGHTS_PACKED
     return d
 
 
 def run(d: dict, out=None, workspace=None, stream=None, events=None):
     return moe.fused_forward(d["x"], d["topk_ids"], d["topk_w"], d["w1"], d["w2"], out=out, x_scale=d["x_scale"],
                              w1_scale=d["w1_scale"], w2_scale=d["w2_scale"], workspace=workspace, stream=stream,
-                             events=events)
+                             events=events, weight_layout=d.get("weight_layout", moe.MOE_WEIGHTS_ROW_MAJOR))
 
 
 def out_to_f64(out) -> np.ndarray:

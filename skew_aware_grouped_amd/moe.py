@@ -27,10 +27,14 @@ MOE_MODE_F32ACT = 0
 MOE_MODE_BF16 = 1
 MOE_MODE_FP8 = 2
 
+MOE_WEIGHTS_ROW_MAJOR = 0
+MOE_WEIGHTS_PACKED = 1
+
 
 class moe_dims(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("num_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_expert", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_expert", ctypes.c_int32),
+                ("weight_layout", ctypes.c_int32)]
 
 
 class moe_scales(ctypes.Structure):
@@ -76,6 +80,8 @@ def lib():
     L.moe_fused_forward_profiled.restype = ctypes.c_int
     L.moe_fused_forward_profiled.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, P(moe_scales), vp, vp,
                                              ctypes.c_size_t, vp, P(vp)]
+    L.moe_pack_weights.restype = ctypes.c_int
+    L.moe_pack_weights.argtypes = [P(moe_dims), vp, vp, vp, vp, vp]
     L.moe_block_m.restype = ctypes.c_int32
     L.moe_block_m.argtypes = []
     L.moe_route_caps.restype = ctypes.c_int
@@ -114,6 +120,11 @@ def moe_fused_forward_profiled(dims, x, topk_ids, topk_w, w1, w2, scales, out, w
     return int(lib().moe_fused_forward_profiled(ctypes.byref(dims), x, topk_ids, topk_w, w1, w2,
                                                 ctypes.byref(scales) if scales is not None else None, out,
                                                 workspace, workspace_bytes, stream, ev))
+
+
+def moe_pack_weights(dims, w1, w2, w1_packed, w2_packed, stream) -> int:
+    return int(lib().moe_pack_weights(ctypes.byref(dims) if dims is not None else None, w1, w2, w1_packed,
+                                      w2_packed, stream))
 
 
 def moe_block_m() -> int:
@@ -175,21 +186,42 @@ def workspace_for(dims: moe_dims, device):
     return ws
 
 
-def make_dims(x, topk_ids, w1, mode: Optional[int] = None) -> moe_dims:
+def make_dims(x, topk_ids, w1, mode: Optional[int] = None, weight_layout: int = MOE_WEIGHTS_ROW_MAJOR) -> moe_dims:
     T, d_h = x.shape
     E, two_de, d_h2 = w1.shape
     assert d_h2 == d_h and two_de % 2 == 0, "w1 must be [E, 2*d_expert, d_hidden]"
     return moe_dims(mode=_mode_of(x, w1) if mode is None else mode, num_tokens=T, num_experts=E,
-                    top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2)
+                    top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2, weight_layout=weight_layout)
+
+
+def pack_weights(w1, w2, stream=None):
+    """``moe_pack_weights`` on torch device tensors: new tensors of the same
+    shapes and dtypes holding W1 and W2 in the packed tile order (pass them
+    to ``fused_forward`` with ``weight_layout=MOE_WEIGHTS_PACKED``)."""
+    import torch
+    E, two_de, d_h = w1.shape
+    mode = MOE_MODE_FP8 if w1.dtype in (torch.float8_e4m3fn, torch.uint8) else MOE_MODE_BF16
+    for name, t in (("w1", w1), ("w2", w2)):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if tuple(w2.shape) != (E, d_h, two_de // 2):
+        raise ValueError("w2 must be [E, d_hidden, d_expert]")
+    dims = moe_dims(mode=mode, num_tokens=0, num_experts=E, top_k=1, d_hidden=d_h, d_expert=two_de // 2)
+    p1, p2 = torch.empty_like(w1), torch.empty_like(w2)
+    rc = moe_pack_weights(dims, w1.data_ptr(), w2.data_ptr(), p1.data_ptr(), p2.data_ptr(), _stream_ptr(stream))
+    if rc:
+        raise MoEError(rc, "moe_pack_weights")
+    return p1, p2
 
 
 def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=None, w2_scale=None,
-                  workspace=None, stream=None, events=None):
+                  workspace=None, stream=None, events=None, weight_layout=MOE_WEIGHTS_ROW_MAJOR):
     """Run ``moe_fused_forward`` on torch device tensors; returns ``out``.  With
     ``events`` (8 torch.cuda.Event objects: start and end of the routing, GEMM-1,
-    GEMM-2 and combine kernels) the kernel-timing variant is used."""
+    GEMM-2 and combine kernels) the kernel-timing variant is used.  With
+    ``weight_layout=MOE_WEIGHTS_PACKED``, w1 and w2 are ``pack_weights`` outputs."""
     import torch
-    dims = make_dims(x, topk_ids, w1)
+    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout)
     if out is None:
         odt = torch.float32 if dims.mode == MOE_MODE_F32ACT else torch.bfloat16
         out = torch.empty(x.shape[0], x.shape[1], dtype=odt, device=x.device)

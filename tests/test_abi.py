@@ -23,8 +23,9 @@ def test_block_m_and_caps():
     assert moe.moe_route_caps(1, 2, 32) == (2 + 2 * 15, 2)
 
 
-def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048):
-    return moe.moe_dims(mode=mode, num_tokens=T, num_experts=E, top_k=k, d_hidden=d_h, d_expert=d_e)
+def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048, layout=moe.MOE_WEIGHTS_ROW_MAJOR):
+    return moe.moe_dims(mode=mode, num_tokens=T, num_experts=E, top_k=k, d_hidden=d_h, d_expert=d_e,
+                        weight_layout=layout)
 
 
 def test_workspace_layout_is_disjoint_and_aligned():
@@ -45,6 +46,8 @@ def test_invalid_dims_rejected():
     assert moe.moe_workspace_bytes(_dims(E=0)) == 0
     assert moe.moe_workspace_bytes(_dims(k=9)) == 0
     assert moe.moe_workspace_bytes(_dims(mode=3)) == 0
+    assert moe.moe_workspace_bytes(_dims(layout=2)) == 0
+    assert moe.moe_workspace_bytes(_dims(layout=moe.MOE_WEIGHTS_PACKED)) == moe.moe_workspace_bytes(_dims())
 
 
 def test_forward_argument_errors_without_gpu():
@@ -60,6 +63,7 @@ def test_forward_argument_errors_without_gpu():
 
     assert call(None) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(mode=5)) == moe.MOE_ERR_INVALID_ARG
+    assert call(_dims(layout=7)) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(d_h=100)) == moe.MOE_ERR_UNSUPPORTED
     assert call(_dims(E=300)) == moe.MOE_ERR_UNSUPPORTED
     assert call(_dims(T=0)) == moe.MOE_OK  # empty batch: nothing to do
@@ -78,3 +82,23 @@ def test_route_argument_errors_without_gpu():
     assert moe.moe_route(4, 2, 0, 1 << 20, out, None) == moe.MOE_ERR_INVALID_ARG
     assert moe.moe_route(4, 9, 4, 1 << 20, out, None) == moe.MOE_ERR_INVALID_ARG
     assert moe.moe_route(4, 2, 4, 1 << 20, out, None) == moe.MOE_ERR_INVALID_ARG  # null outputs
+
+
+def test_pack_weights_argument_errors_without_gpu():
+    E, d_h, d_e = 4, 256, 128
+    n1 = E * 2 * d_e * d_h * 2  # bf16 bytes of W1
+    n2 = E * d_h * d_e * 2
+    w1, w2 = 1 << 30, (1 << 30) + n1  # fake, aligned, disjoint; never dereferenced
+    p1, p2 = (1 << 31), (1 << 31) + n1
+    dims = _dims(mode=moe.MOE_MODE_BF16, T=0, E=E, d_h=d_h, d_e=d_e)
+
+    def call(d=dims, a=w1, b=w2, c=p1, e=p2):
+        return moe.moe_pack_weights(d, a, b, c, e, None)
+
+    assert call(d=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(d=_dims(mode=moe.MOE_MODE_BF16, E=E, d_h=100, d_e=d_e)) == moe.MOE_ERR_INVALID_ARG
+    for bad in (dict(a=None), dict(b=None), dict(c=None), dict(e=None), dict(c=p1 + 8), dict(a=w1 + 4)):
+        assert call(**bad) == moe.MOE_ERR_INVALID_ARG, bad
+    assert call(c=w1 + 256) == moe.MOE_ERR_INVALID_ARG  # w1_packed overlaps w1
+    assert call(e=w1) == moe.MOE_ERR_INVALID_ARG  # w2_packed overlaps w1
+    assert call(e=p1 + n1 - 16) == moe.MOE_ERR_INVALID_ARG  # the packed buffers overlap

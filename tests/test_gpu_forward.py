@@ -42,9 +42,9 @@ def _run(w, out=None):
     return d, o
 
 
-def _check(w, oracle, rows=None, label=""):
+def _check(w, oracle, rows=None, label="", packed=False):
     import torch
-    d = device.upload(w)
+    d = device.upload(w, packed=packed)
     odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
     out = torch.full((w.T, w.d_h), float("nan"), dtype=odt, device="cuda:0")  # sentinel: every row must be written
     dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
@@ -56,16 +56,18 @@ def _check(w, oracle, rows=None, label=""):
     acc, _ = oracle.forward(w, rows=rows)
     gs = g if rows is None else g[rows]
     err = normwise(gs, acc)
-    print(f"{label} mode={w.mode} T={w.T} E={w.E} k={w.k} {w.d_h}x{w.d_e}: normwise err {err:.3e}", flush=True)
+    print(f"{label} mode={w.mode} packed={packed} T={w.T} E={w.E} k={w.k} {w.d_h}x{w.d_e}: normwise err {err:.3e}",
+          flush=True)
     assert err <= TOL[w.mode], err
     return d, out, g
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8])
-def test_small_shapes_full_parity(oracle, mode):
+def test_small_shapes_full_parity(oracle, mode, packed):
     """Several tiles in every direction with ragged expert groups."""
     w = W.custom(200, 8, 3, 384, 256, mode, seed=21)
-    _check(w, oracle, label="small")
+    _check(w, oracle, label="small", packed=packed)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen_bf16"])
@@ -107,9 +109,10 @@ EDGE_CASES = {
 }
 
 
+@pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("case", sorted(EDGE_CASES))
 @pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8])
-def test_edge_cases(oracle, case, mode):
+def test_edge_cases(oracle, case, mode, packed):
     c = EDGE_CASES[case]
     rng = np.random.default_rng(9)
     T, E, k = c["T"], c["E"], c["k"]
@@ -121,7 +124,56 @@ def test_edge_cases(oracle, case, mode):
         ids[1::5, 1] = E + 3
         ids[7, :] = -2  # a token with no valid assignment -> zero row
     w = W.custom(T, E, k, 256, 128 if mode != W.MODE_FP8 else 256, mode, seed=13, topk_ids=ids)
-    _check(w, oracle, label=case)
+    _check(w, oracle, label=case, packed=packed)
+
+
+def _packed_reference(wt, gated, bn):
+    """The packed tile order as the header defines it, by numpy indexing: chunk
+    ((tile * R + b) * rows + r) * 8 + s holds chunk s ^ (r & 7) of K block b of
+    tile row r (gated tiles: gate rows c*bn.., then up rows d_e + c*bn..)."""
+    E, nrows, kbytes = wt.shape
+    n_out = nrows // 2 if gated else nrows
+    R = kbytes // 128
+    w5 = wt.reshape(E, nrows, R, 8, 16)
+    c = np.arange(n_out // bn)[:, None, None, None]
+    b = np.arange(R)[None, :, None, None]
+    r = np.arange(2 * bn if gated else bn)[None, None, :, None]
+    s = np.arange(8)[None, None, None, :]
+    row = np.where(r < bn, c * bn + r, n_out + c * bn + r - bn) if gated else c * bn + r
+    return w5[:, row, b, s ^ (r & 7)].reshape(-1)
+
+
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8])
+def test_pack_weights_is_the_stated_permutation(mode):
+    """moe_pack_weights output, byte for byte, against the header's formula."""
+    import torch
+    w = W.custom(8, 3, 2, 384, 256, mode, seed=3)
+    d = device.upload(w)
+    p1, p2 = moe.pack_weights(d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    L = moe.moe_workspace_layout(moe.make_dims(d["x"], d["topk_ids"], d["w1"]))
+    assert (L.block_n1, L.block_n2) == ((128, 128) if mode == W.MODE_FP8 else (64, 128))
+
+    def raw(t):
+        return t.view(torch.uint8).cpu().numpy().reshape(t.shape[0], t.shape[1], -1)
+
+    for src, got, gated, bn in ((d["w1"], p1, True, L.block_n1), (d["w2"], p2, False, L.block_n2)):
+        want = _packed_reference(raw(src), gated, bn)
+        assert np.array_equal(got.view(torch.uint8).cpu().numpy().reshape(-1), want)
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen_bf16", "qwen_fp8", "ds_fp8_128", "ds_fp8_1024", "ds_fp8_8192"])
+def test_packed_weights_bitwise_equal_row_major(name):
+    """The packed layout changes where the GEMMs read each weight tile from,
+    not what they compute: the output is bitwise the row-major one."""
+    import torch
+    print(f"generating {name}", flush=True)
+    w = W.config(name)
+    a = device.run(device.upload(w)).clone()
+    b = device.run(device.upload(w, packed=True)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16) if a.dtype != torch.float32 else a.view(torch.int32),
+                       b.view(torch.int16) if b.dtype != torch.float32 else b.view(torch.int32))
 
 
 def test_empty_batch_is_noop():
