@@ -192,7 +192,8 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
 
 /* Byte offsets of the workspace sections moe_fused_forward uses, for tests and
  * inspection after a call.  The routing arrays hold the layout described for
- * moe_route.  `stats` is a control block of int32 words: [0..4] = {dropped,
+ * moe_route; row_w (fp32 [n_pad_cap]) holds the routing weight of each padded
+ * row below padded_offsets[E] (0 on padding rows).  `stats` is a control block of int32 words: [0..4] = {dropped,
  * blocks, padded rows, GEMM-1 tasks, GEMM-2 tasks}; words [272..280] and
  * [288..296] hold the start of each of the 8 per-XCD segments (and the end of
  * the last) of the GEMM-1 and GEMM-2 task lists.  Tasks are int32 quadruples
@@ -201,7 +202,7 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
  * (expert, column block) sit in the same segment, next to each other.
  * Returns MOE_ERR_INVALID_ARG for invalid dims. */
 typedef struct {
-    size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, tile_expert, tile_row0, stats;
+    size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, row_w, tile_expert, tile_row0, stats;
     size_t tasks1, tasks2, h, h_scale, y, zero, x_bf16, total;
     int64_t n_pad_cap, tile_cap, task1_cap, task2_cap;
     int32_t block_n1, block_n2, max_row_blocks;

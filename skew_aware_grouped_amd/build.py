@@ -17,6 +17,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 ALU ops are switched off for every HIP translation unit.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE, "-I", CSRC]
+# The GEMM kernels' queue atomics run on one lane and their results are read
+# much later; the compiler's wave-level atomic aggregation would read the
+# result right after the atomic, making the wave wait for it there.
+SOURCE_FLAGS = {"moe_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def build(verbose: bool = False) -> str:
@@ -26,7 +30,7 @@ def build(verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))

@@ -59,6 +59,7 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     L->sorted_p = take(4 * N);
     L->ppos = take(4 * N);
     L->row_src = take(4 * L->n_pad_cap);
+    L->row_w = take(4 * L->n_pad_cap);
     L->tile_expert = take(4 * L->tile_cap);
     L->tile_row0 = take(4 * L->tile_cap);
     L->stats = take(4 * kCtlWords);
@@ -253,6 +254,8 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.zero = r.zero;
     g1.h = at<void>(workspace, L.h);
     g1.h_scale = mode == MOE_MODE_FP8 ? at<float>(workspace, L.h_scale) : nullptr;
+    g1.topk_w = topk_w;
+    g1.row_w = at<float>(workspace, L.row_w);
     g1.k = k;
     g1.d_h = d_h;
     g1.d_e = d_e;
@@ -266,7 +269,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.w2 = w2;
     g2.w2_scale = mode == MOE_MODE_FP8 ? scales->w2_scale : nullptr;
     g2.row_src = r.row_src;
-    g2.topk_w = topk_w;
+    g2.row_w = g1.row_w;
     g2.tasks = r.tasks2;
     g2.ctl = r.ctl;
     g2.zero = r.zero;

@@ -116,12 +116,15 @@ __device__ __forceinline__ void g2l4(const void* g, unsigned lds) {
 }
 __device__ __forceinline__ unsigned lds_offset(const void* p) { return (unsigned)(uintptr_t)p; }
 
-// stage hand-off: every wave has waited for its own loads of the stage; the
-// empty asm keeps the compiler from moving LDS accesses across the barrier
-__device__ __forceinline__ void stage_barrier() {
+// Workgroup barrier for LDS hand-offs (stages of the ring, the epilogue's
+// staging, the task queue state): this wave's LDS accesses are complete
+// (s_waitcnt lgkmcnt(0)) but its global stores and loads may still be in
+// flight, unlike __syncthreads, whose fence would wait for every store of
+// the epilogue to be acknowledged.  The workgroup shares nothing through
+// global memory.  The empty asm keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
-    // this wave's LDS reads of the previous stage are complete before any
-    // wave may overwrite that slot (s_waitcnt lgkmcnt(0), no vmcnt wait)
     __builtin_amdgcn_s_waitcnt(VmCnt<63>::imm & ~(0xF << 8));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -140,35 +143,115 @@ __device__ __forceinline__ v8i lds_frag32(const unsigned char* row, int g, int s
 // on it; any value in [0, 8) is correct.
 __device__ __forceinline__ int my_xcd() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcds - 1); }
 
-// Next task of this workgroup: from its own XCD's segment of the list first,
-// then from the other segments in turn (each segment keeps its own counter,
-// in its own cache line).  Returns -1 once every segment is exhausted.
-// s_seg holds the kXcds + 1 segment starts; s_mask the segments found empty.
-__device__ __forceinline__ int pull_task(int32_t* ctl, int counter_base, const int* s_seg, int xcd, int* s_slot,
-                                         unsigned* s_mask) {
-    if (threadIdx.x == 0) {
-        int slot = -1;
+// Task queue of a GEMM kernel: the list is split into kXcds segments, each
+// with its own counter in its own cache line; a workgroup takes tasks from
+// its own XCD's segment first, then from the others in turn.
+//
+// The last wave of the workgroup is also its scheduler.  It claims the next
+// task while the current one streams and, after its K loop, loads that
+// task's record and source rows (row_src, and for GEMM-2 the routing weight
+// of each row) into the other half of a double buffer in LDS.  So no queue
+// atomic, record load or row-index load sits between two tasks, and the
+// other waves never wait on a global load outside the stage ring.  The
+// record and rows go straight to LDS (direct-to-LDS loads, waited for by the
+// scheduler wave alone); the scheduler wave issues no global stores, so its
+// waits never wait on one.
+constexpr int kSchedWave = kGemmWaves - 1;
+constexpr int kClaimLead = 2;  // K blocks between the claim and the end of the task
+constexpr int kStoreThreads = 64 * kSchedWave;  // threads of the epilogue's store loops
+
+struct QueueLds {
+    int seg[kXcds + 1];  // segment starts (and the end of the last)
+    unsigned mask;       // segments found exhausted (scheduler lane 0)
+    int slot;            // the task of the next round, -1 when none is left
+    int4 task;           // its record {expert, first padded row, row blocks, column block}
+    int rec[64];         // landing area of the record load (16 copies)
+    int rows[2][kAMaxRows];    // row_src of the task's rows, by round parity
+    float roww[2][kAMaxRows];  // GEMM-2: routing weight of the task's rows
+};
+
+// scheduler lane 0: claim a task, waiting for each atomic (the first task,
+// and the fallback once the segment claimed from ahead has run out)
+__device__ __forceinline__ int claim_blocking(int32_t* ctl, int base, QueueLds* q, int xcd) {
+    for (int i = 0; i < kXcds; ++i) {
+        const int x = (xcd + i) & (kXcds - 1);
+        if ((q->mask >> x) & 1u) continue;
+        const int j = atomicAdd(&ctl[base + kQueueStride * x], 1);
+        if (q->seg[x] + j < q->seg[x + 1]) return q->seg[x] + j;
+        q->mask |= 1u << x;
+    }
+    return -1;
+}
+
+// Scheduler wave state of one round.
+struct Sched {
+    int32_t* ctl;
+    int base;
+    const int4* tasks;
+    const int32_t* row_src;
+    const float* row_w;  // GEMM-2 only
+    QueueLds* q;
+    int xcd;
+    int x = -1, raw = 0;  // lane 0: segment and result of the atomic sent ahead
+    int slot = -1;
+
+    // lane 0, during the current task's last K blocks; the result is read
+    // after the K loop, behind a full vmcnt wait of every wave
+    __device__ __forceinline__ void issue() {
         for (int i = 0; i < kXcds; ++i) {
-            const int x = (xcd + i) & (kXcds - 1);
-            if ((*s_mask >> x) & 1u) continue;
-            const int j = atomicAdd(&ctl[counter_base + kQueueStride * x], 1);
-            if (s_seg[x] + j < s_seg[x + 1]) {
-                slot = s_seg[x] + j;
+            const int y = (xcd + i) & (kXcds - 1);
+            if (!((q->mask >> y) & 1u)) {
+                x = y;
                 break;
             }
-            *s_mask |= 1u << x;
         }
-        *s_slot = slot;
+        if (x >= 0) raw = atomicAdd(&ctl[base + kQueueStride * x], 1);
     }
-    __syncthreads();
-    // readfirstlane: the slot is the same for every thread, and the compiler
-    // must know it, or it treats the task loop as divergent and may split a
-    // thread-0 region next to the loop's back-edge off the loop while the
-    // other lanes iterate on a stale slot
-    const int t = __builtin_amdgcn_readfirstlane(*s_slot);
-    __syncthreads();
-    return t;
-}
+    // whole scheduler wave: settle the claim (ahead: the atomic sent by
+    // issue(); else claim now), then load the record and, into rows[par] and
+    // roww[par], the task's source rows.  All 64 lanes take part in every
+    // direct-to-LDS load (lanes past the task's rows reread its first row).
+    __device__ __forceinline__ void fetch(bool ahead, int par) {
+        const int lane = threadIdx.x & 63;
+        int sl = -1;
+        if (lane == 0) {
+            if (!ahead) {
+                sl = claim_blocking(ctl, base, q, xcd);
+            } else if (x >= 0) {
+                if (q->seg[x] + raw < q->seg[x + 1]) {
+                    sl = q->seg[x] + raw;
+                } else {
+                    q->mask |= 1u << x;
+                    sl = claim_blocking(ctl, base, q, xcd);
+                }
+            }
+        }
+        slot = __shfl(sl, 0, 64);
+        if (slot < 0) return;
+        g2l4(reinterpret_cast<const int*>(tasks + slot) + (lane & 3), lds_offset(q->rec));
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        asm volatile("" ::: "memory");
+        const int row0 = __builtin_amdgcn_readfirstlane(q->rec[1]);
+        const int n = 16 * __builtin_amdgcn_readfirstlane(q->rec[2]);
+#pragma unroll
+        for (int j = 0; j < kAMaxRows / 64; ++j) {
+            if (64 * j >= n) break;
+            const int r = 64 * j + lane < n ? 64 * j + lane : 0;
+            g2l4(row_src + row0 + r, lds_offset(&q->rows[par][64 * j]));
+            if (row_w) g2l4(row_w + row0 + r, lds_offset(&q->roww[par][64 * j]));
+        }
+    }
+    // whole scheduler wave, before the round's last barrier: the rows have
+    // landed; publish the record
+    __device__ __forceinline__ void publish() {
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        asm volatile("" ::: "memory");
+        if ((threadIdx.x & 63) == 0) {
+            q->slot = slot;
+            if (slot >= 0) q->task = make_int4(q->rec[0], q->rec[1], q->rec[2], q->rec[3]);
+        }
+    }
+};
 
 // ------------------------------------------------------------------ configs
 // Stage of the ring for a task of NSUB group blocks: the K block of the
@@ -189,7 +272,7 @@ struct Cfg {
     // ring: FP8 GEMM-1 (256 weight rows per stage) takes a whole CU's LDS
     // (three stages of a 128-row task, four of a 16-row one); the others take
     // four stages of a one-block task, so two workgroups share a CU
-    static constexpr int kRing = (GATED && kFP8) ? 160 * 1024 - 256 : 4 * stage_bytes(1);
+    static constexpr int kRing = (GATED && kFP8) ? 160 * 1024 - 2560 : 4 * stage_bytes(1);
     // stages in a ring of `ring` bytes
     static constexpr int stages(int nsub, int ring) {
         return ring / stage_bytes(nsub) < 8 ? ring / stage_bytes(nsub) : 8;
@@ -215,7 +298,8 @@ template <int MODE, bool GATED, int NSUB, int RING>
 __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_scale, const int32_t* row_src,
                                           int a_div, const void* wts, const float* w_scale, const unsigned char* zero,
                                           int e, int row0, int cb, int K, int N_out, bool packed,
-                                          unsigned char* smem, const Gemm1Args* g1, const Gemm2Args* g2) {
+                                          unsigned char* smem, const Gemm1Args* g1, const Gemm2Args* g2,
+                                          Sched& sch, const int* rows, const float* roww, int par) {
     using C = Cfg<MODE, GATED>;
     constexpr bool kFP8 = C::kFP8;
     constexpr int S = C::stages(NSUB, RING);
@@ -271,7 +355,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         asrc[j] = zero;
         if (ai < kAInstr) {
             if constexpr (GATED) {
-                const int p = row_src[row0 + r];
+                const int p = rows[r];
                 apad[j] = p < 0;
                 asrc[j] = apad[j] ? zero + c * 16
                                   : static_cast<const unsigned char*>(a_base) + (int64_t)(p / a_div) * ld_bytes + c * 16;
@@ -290,7 +374,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         const int srow = (w == 2 ? 64 : 0) + lane;
         if ((w == 0 || w == 2) && srow < 16 * NSUB) {
             son = true;
-            const int p = row_src[row0 + srow];
+            const int p = rows[srow];
             if (GATED) {
                 spad = p < 0;
                 ssrc = spad ? reinterpret_cast<const float*>(zero) : a_scale + (int64_t)(p / a_div) * kq;
@@ -304,6 +388,22 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             const int64_t nrb = GATED ? 2 * (int64_t)N_out / kQ : (int64_t)N_out / kQ;
             const int64_t brow = GATED ? (lane == 0 ? cb : N_out / kQ + cb) : (int64_t)cb;
             ssrc = w_scale + ((int64_t)e * nrb + brow) * kq;
+        }
+    }
+
+    // Routing weight of each tile row: GEMM-1 tasks of column block 0 look it
+    // up (topk_w[row_src]) and store it by padded row for GEMM-2, whose
+    // scheduler wave loads it with the rows of its next task.  Row
+    // 64 * w + lane in waves 0 and 1; the load is issued ahead of the stage
+    // loads.
+    constexpr int kRows = 16 * NSUB;
+    const int w_row = 64 * w + lane;
+    const bool w_owner = GATED && cb == 0 && w < 2 && w_row < kRows;
+    float ep_w = 0.f;
+    if constexpr (GATED) {
+        if (w_owner) {
+            const int p = rows[w_row];
+            ep_w = p >= 0 ? g1->topk_w[p] : 0.f;
         }
     }
 
@@ -337,12 +437,17 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     const int swz = lr & 7;
     const int npro = nk < S - 1 ? nk : S - 1;
     for (int kc = 0; kc < npro; ++kc) issue(kc);
+    // the scheduler claims the next task kClaimLead K blocks before this one
+    // ends: late enough that tasks go to the workgroups that finish first,
+    // early enough that the atomic has returned when the K loop is done
+    const int claim_at = nk > kClaimLead ? nk - kClaimLead : 0;
     for (int kc = 0; kc < nk; ++kc) {
         // stage kc is complete once at most the younger stages' loads remain
         const int younger = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
         wait_vm_le(younger * loads_per_stage);
-        stage_barrier();
+        lds_barrier();
         if (kc + S - 1 < nk) issue(kc + S - 1);
+        if (kc == claim_at && threadIdx.x == 64 * kSchedWave) sch.issue();
         const unsigned char* st = smem + (kc % S) * kStage;
         const unsigned char* sb = st;
         const unsigned char* sa = st + C::kStageB;
@@ -403,11 +508,18 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         }
     }
 
+    // every wave: the stage loads are complete; this also settles, for the
+    // compiler's own bookkeeping, the scheduler's atomic and any load it
+    // issued before the ring (no store of the previous task is still young)
+    __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+    if (w == kSchedWave) sch.fetch(true, par ^ 1);
+
     // ---- epilogue: stage the output tile in LDS, then 16-byte row stores
-    __syncthreads();  // every wave is done with the ring
+    lds_barrier();  // every wave is done with the ring
     unsigned char* stage = smem;                                              // [16*NSUB][kEpiRow]
     float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * kAMaxRows);  // [waves][kAMaxRows]
     if constexpr (GATED) {
+        if (w_owner) g1->row_w[row0 + w_row] = ep_w;
         float hv[NSUB][C::kNFW][4];
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
@@ -428,7 +540,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
                     if (lr == 0) s_amax[w * kAMaxRows + 16 * s + 4 * lg + i] = m;
                 }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
 #pragma unroll
@@ -456,16 +568,17 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                             (unsigned short)f32_to_bf16(hv[s][f][i]);
                     }
         }
-        __syncthreads();
+        lds_barrier();
         // h[row0 + r][cb*kBN ...]: kEpiRow bytes per row
         constexpr int kChunks = C::kEpiRow / 16;
         unsigned char* h = static_cast<unsigned char*>(g1->h);
         const int64_t hrow_bytes = (int64_t)N_out * (kFP8 ? 1 : 2);
-        for (int i = threadIdx.x; i < 16 * NSUB * kChunks; i += kGemmThreads) {
-            const int r = i / kChunks, c = i - r * kChunks;
-            *reinterpret_cast<v4i*>(h + (int64_t)(row0 + r) * hrow_bytes + (int64_t)cb * C::kEpiRow + c * 16) =
-                *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
-        }
+        if (w != kSchedWave)
+            for (int i = threadIdx.x; i < 16 * NSUB * kChunks; i += kStoreThreads) {
+                const int r = i / kChunks, c = i - r * kChunks;
+                *reinterpret_cast<v4i*>(h + (int64_t)(row0 + r) * hrow_bytes + (int64_t)cb * C::kEpiRow + c * 16) =
+                    *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
+            }
     } else {
         constexpr bool kF32 = MODE == MOE_MODE_F32ACT;
 #pragma unroll
@@ -473,8 +586,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int rr = 16 * s + 4 * lg + i;
-                const int p = row_src[row0 + rr];
-                const float wt = p >= 0 ? g2->topk_w[p] : 0.f;
+                const float wt = roww[rr];  // 0 on padding rows
 #pragma unroll
                 for (int f = 0; f < C::kNFW; ++f) {
                     const float v = acc[s][f][0][i] * wt;
@@ -485,19 +597,21 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                         reinterpret_cast<unsigned short*>(stage + rr * C::kEpiRow)[col] = (unsigned short)f32_to_bf16(v);
                 }
             }
-        __syncthreads();
+        lds_barrier();
         constexpr int kChunks = C::kEpiRow / 16;
         unsigned char* y = static_cast<unsigned char*>(g2->y);
         const int64_t yrow_bytes = (int64_t)N_out * C::kOutBytes;
-        for (int i = threadIdx.x; i < 16 * NSUB * kChunks; i += kGemmThreads) {
-            const int r = i / kChunks, c = i - r * kChunks;
-            const int p = row_src[row0 + r];
-            if (p < 0) continue;
-            *reinterpret_cast<v4i*>(y + (int64_t)p * yrow_bytes + (int64_t)cb * C::kEpiRow + c * 16) =
-                *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
-        }
+        if (w != kSchedWave)
+            for (int i = threadIdx.x; i < 16 * NSUB * kChunks; i += kStoreThreads) {
+                const int r = i / kChunks, c = i - r * kChunks;
+                const int p = rows[r];
+                if (p < 0) continue;
+                *reinterpret_cast<v4i*>(y + (int64_t)p * yrow_bytes + (int64_t)cb * C::kEpiRow + c * 16) =
+                    *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
+            }
     }
-    __syncthreads();  // the ring is refilled by the next task
+    if (w == kSchedWave) sch.publish();
+    lds_barrier();  // the ring and the staging area are refilled by the next task
 }
 
 template <int MODE>
@@ -505,20 +619,30 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
     constexpr int GM = MODE == MOE_MODE_F32ACT ? MOE_MODE_BF16 : MODE;  // x arrives as bf16
     constexpr int RING = Cfg<GM, true>::kRing;
     __shared__ __attribute__((aligned(16))) unsigned char smem[RING];
-    __shared__ int s_slot, s_seg[kXcds + 1];
-    __shared__ unsigned s_mask;
-    if (threadIdx.x <= kXcds) s_seg[threadIdx.x] = a.ctl[kCtlSeg1 + threadIdx.x];
-    if (threadIdx.x == 0) s_mask = 0;
-    __syncthreads();
+    __shared__ QueueLds q;
     const int xcd = my_xcd();
-    for (;;) {
-        const int t = pull_task(a.ctl, kCtlQueue1, s_seg, xcd, &s_slot, &s_mask);
+    if (threadIdx.x <= kXcds) q.seg[threadIdx.x] = a.ctl[kCtlSeg1 + threadIdx.x];
+    if (threadIdx.x == 0) q.mask = 0;
+    lds_barrier();
+    if (threadIdx.x >= 64 * kSchedWave) {
+        Sched sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
+        sch.fetch(false, 0);
+        sch.publish();
+    }
+    lds_barrier();
+    for (int par = 0;; par ^= 1) {
+        // readfirstlane: the task is the same for every thread, and the
+        // compiler must know it, or it treats the task loop as divergent and
+        // may split a thread-0 region next to the loop's back-edge off the
+        // loop while the other lanes iterate on a stale task
+        const int t = __builtin_amdgcn_readfirstlane(q.slot);
         if (t < 0) break;
-        const int4 task = a.tasks[t];
-        const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
+        const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
+        const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
+        Sched sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
 #define MOE_G1(NS)                                                                                                \
     gemm_task<GM, true, NS, RING>(a.x, a.x_scale, a.row_src, a.k, a.w1, a.w1_scale, a.zero, e, row0, cb, a.d_h, a.d_e, \
-                                  a.packed != 0, smem, &a, nullptr)
+                                  a.packed != 0, smem, &a, nullptr, sch, q.rows[par], q.roww[par], par)
         switch (nsub) {
             case 1: MOE_G1(1); break;
             case 2: MOE_G1(2); break;
@@ -537,20 +661,26 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
     constexpr int RING = Cfg<MODE, false>::kRing;
     __shared__ __attribute__((aligned(16))) unsigned char smem[RING];
-    __shared__ int s_slot, s_seg[kXcds + 1];
-    __shared__ unsigned s_mask;
-    if (threadIdx.x <= kXcds) s_seg[threadIdx.x] = a.ctl[kCtlSeg2 + threadIdx.x];
-    if (threadIdx.x == 0) s_mask = 0;
-    __syncthreads();
+    __shared__ QueueLds q;
     const int xcd = my_xcd();
-    for (;;) {
-        const int t = pull_task(a.ctl, kCtlQueue2, s_seg, xcd, &s_slot, &s_mask);
+    if (threadIdx.x <= kXcds) q.seg[threadIdx.x] = a.ctl[kCtlSeg2 + threadIdx.x];
+    if (threadIdx.x == 0) q.mask = 0;
+    lds_barrier();
+    if (threadIdx.x >= 64 * kSchedWave) {
+        Sched sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
+        sch.fetch(false, 0);
+        sch.publish();
+    }
+    lds_barrier();
+    for (int par = 0;; par ^= 1) {
+        const int t = __builtin_amdgcn_readfirstlane(q.slot);  // uniform, as in gemm1_kernel
         if (t < 0) break;
-        const int4 task = a.tasks[t];
-        const int e = task.x, row0 = task.y, nsub = task.z, cb = task.w;
+        const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
+        const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
+        Sched sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
 #define MOE_G2(NS)                                                                                                 \
     gemm_task<MODE, false, NS, RING>(a.h, a.h_scale, a.row_src, 1, a.w2, a.w2_scale, a.zero, e, row0, cb, a.d_e, a.d_h, \
-                                     a.packed != 0, smem, nullptr, &a)
+                                     a.packed != 0, smem, nullptr, &a, sch, q.rows[par], q.roww[par], par)
         switch (nsub) {
             case 1: MOE_G2(1); break;
             case 2: MOE_G2(2); break;

@@ -83,6 +83,8 @@ struct Gemm1Args {
     const unsigned char* zero;
     void* h;
     float* h_scale;
+    const float* topk_w;  // [T*k] routing weights
+    float* row_w;         // [n_pad] routing weight of each padded row (0 on padding), written by column block 0
     int32_t k, d_h, d_e;
     int32_t packed;  // W1 in the packed tile order
 };
@@ -93,7 +95,7 @@ struct Gemm2Args {
     const void* w2;
     const float* w2_scale;
     const int32_t* row_src;
-    const float* topk_w;
+    const float* row_w;  // from GEMM-1
     const int4* tasks;
     int32_t* ctl;
     const unsigned char* zero;

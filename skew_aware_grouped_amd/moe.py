@@ -48,7 +48,8 @@ class moe_route_out(ctypes.Structure):
 
 class moe_ws_layout(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_size_t) for n in ("counts", "offsets", "padded_offsets", "pos", "sorted_p", "ppos",
-                                                 "row_src", "tile_expert", "tile_row0", "stats", "tasks1", "tasks2",
+                                                 "row_src", "row_w", "tile_expert", "tile_row0", "stats", "tasks1",
+                                                 "tasks2",
                                                  "h", "h_scale", "y", "zero", "x_bf16", "total")]
                 + [(n, ctypes.c_int64) for n in ("n_pad_cap", "tile_cap", "task1_cap", "task2_cap")]
                 + [(n, ctypes.c_int32) for n in ("block_n1", "block_n2", "max_row_blocks")])

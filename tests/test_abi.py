@@ -32,7 +32,7 @@ def test_workspace_layout_is_disjoint_and_aligned():
     for mode in (0, 1, 2):
         d = _dims(mode=mode)
         L = moe.moe_workspace_layout(d)
-        offs = [L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.tile_expert,
+        offs = [L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.row_w, L.tile_expert,
                 L.tile_row0, L.stats, L.tasks1, L.tasks2, L.h, L.h_scale, L.y, L.zero, L.x_bf16, L.total]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         N = 2048

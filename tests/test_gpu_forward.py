@@ -186,11 +186,12 @@ def test_empty_batch_is_noop():
     assert out.shape == (0, 256)
 
 
-def test_forward_routing_and_task_list(oracle):
+@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024"])
+def test_forward_routing_and_task_list(oracle, name):
     """The workspace after a forward call holds the oracle's routing metadata and
     task lists that cover every (group block, column block) pair exactly once."""
     import torch
-    w = W.config("qwen_fp8")
+    w = W.config(name)
     d = device.upload(w)
     dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
     ws = moe.workspace_for(dims, "cuda:0")
@@ -207,6 +208,11 @@ def test_forward_routing_and_task_list(oracle):
     assert np.array_equal(arr(L.counts, w.E), r["counts"])
     assert np.array_equal(arr(L.pos, N), r["pos"])
     assert np.array_equal(arr(L.row_src, L.n_pad_cap), r["row_src"])
+    # routing weight by padded row: a copy of topk_w, exact; 0 on padding rows
+    n_pad = int(r["padded_offsets"][-1])
+    src = r["row_src"][:n_pad]
+    want_w = np.where(src >= 0, w.topk_w.ravel().astype(np.float32)[np.maximum(src, 0)], np.float32(0))
+    assert np.array_equal(arr(L.row_w, n_pad, np.float32), want_w)
     ctl = arr(L.stats, 304)
     for lst, off, nb, segw in ((3, L.tasks1, w.d_e // L.block_n1, 272), (4, L.tasks2, w.d_h // L.block_n2, 288)):
         nt = int(ctl[lst])
