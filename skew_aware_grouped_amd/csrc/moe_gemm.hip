@@ -147,18 +147,22 @@ __device__ __forceinline__ int my_xcd() { return __builtin_amdgcn_s_getreg((3 <<
 // with its own counter in its own cache line; a workgroup takes tasks from
 // its own XCD's segment first, then from the others in turn.
 //
-// The last wave of the workgroup is also its scheduler.  It claims the next
-// task while the current one streams and, after its K loop, loads that
-// task's record and source rows (row_src, and for GEMM-2 the routing weight
-// of each row) into the other half of a double buffer in LDS.  So no queue
-// atomic, record load or row-index load sits between two tasks, and the
-// other waves never wait on a global load outside the stage ring.  The
-// record and rows go straight to LDS (direct-to-LDS loads, waited for by the
-// scheduler wave alone); the scheduler wave issues no global stores, so its
-// waits never wait on one.
+// The last wave of the workgroup is also its scheduler.  It issues none of
+// the stage loads (the other waves share them), so its vmcnt waits cover only
+// its own queue operations, and during the last K blocks of a task it claims
+// the next task, then loads that task's record and source rows (row_src, and
+// for GEMM-2 the routing weight of each row) into the other half of a double
+// buffer in LDS.  So no queue atomic, record load or row-index load sits
+// between two tasks or stalls the ring.  Record and rows go straight to LDS
+// (direct-to-LDS loads); the scheduler wave issues no global stores either.
 constexpr int kSchedWave = kGemmWaves - 1;
-constexpr int kClaimLead = 2;  // K blocks between the claim and the end of the task
+constexpr int kLoadWaves = kGemmWaves - 1;      // waves that issue the stage loads
 constexpr int kStoreThreads = 64 * kSchedWave;  // threads of the epilogue's store loops
+// K blocks before the end of a task at which the scheduler claims the next
+// task, settles the claim and loads the record, and loads the rows: one
+// step every two K blocks, about a memory round trip apart; late enough that
+// tasks go to the workgroups that finish first
+constexpr int kClaimLead = 6;
 
 struct QueueLds {
     int seg[kXcds + 1];  // segment starts (and the end of the last)
@@ -183,7 +187,8 @@ __device__ __forceinline__ int claim_blocking(int32_t* ctl, int base, QueueLds* 
     return -1;
 }
 
-// Scheduler wave state of one round.
+// Scheduler wave state of one round.  claim() runs on lane 0; the other
+// steps on the whole scheduler wave, in order.
 struct Sched {
     int32_t* ctl;
     int base;
@@ -195,9 +200,7 @@ struct Sched {
     int x = -1, raw = 0;  // lane 0: segment and result of the atomic sent ahead
     int slot = -1;
 
-    // lane 0, during the current task's last K blocks; the result is read
-    // after the K loop, behind a full vmcnt wait of every wave
-    __device__ __forceinline__ void issue() {
+    __device__ __forceinline__ void claim() {
         for (int i = 0; i < kXcds; ++i) {
             const int y = (xcd + i) & (kXcds - 1);
             if (!((q->mask >> y) & 1u)) {
@@ -207,11 +210,9 @@ struct Sched {
         }
         if (x >= 0) raw = atomicAdd(&ctl[base + kQueueStride * x], 1);
     }
-    // whole scheduler wave: settle the claim (ahead: the atomic sent by
-    // issue(); else claim now), then load the record and, into rows[par] and
-    // roww[par], the task's source rows.  All 64 lanes take part in every
-    // direct-to-LDS load (lanes past the task's rows reread its first row).
-    __device__ __forceinline__ void fetch(bool ahead, int par) {
+    // settle the claim (ahead: the atomic sent by claim(); else claim now and
+    // wait) and start loading the record
+    __device__ __forceinline__ void settle(bool ahead) {
         const int lane = threadIdx.x & 63;
         int sl = -1;
         if (lane == 0) {
@@ -227,8 +228,14 @@ struct Sched {
             }
         }
         slot = __shfl(sl, 0, 64);
+        if (slot >= 0) g2l4(reinterpret_cast<const int*>(tasks + slot) + (lane & 3), lds_offset(q->rec));
+    }
+    // once the record has landed: load the task's source rows into rows[par]
+    // and roww[par].  All 64 lanes take part in every direct-to-LDS load
+    // (lanes past the task's rows reread its first row).
+    __device__ __forceinline__ void load_rows(int par) {
         if (slot < 0) return;
-        g2l4(reinterpret_cast<const int*>(tasks + slot) + (lane & 3), lds_offset(q->rec));
+        const int lane = threadIdx.x & 63;
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
         asm volatile("" ::: "memory");
         const int row0 = __builtin_amdgcn_readfirstlane(q->rec[1]);
@@ -241,8 +248,7 @@ struct Sched {
             if (row_w) g2l4(row_w + row0 + r, lds_offset(&q->roww[par][64 * j]));
         }
     }
-    // whole scheduler wave, before the round's last barrier: the rows have
-    // landed; publish the record
+    // before the round's last barrier: the rows have landed; publish the record
     __device__ __forceinline__ void publish() {
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
         asm volatile("" ::: "memory");
@@ -264,7 +270,8 @@ struct Cfg {
     static constexpr int kNFW = (GATED && !kFP8) ? 1 : 2;  // 16-column fragments per wave
     static constexpr int kBN = 16 * kNFW * kGemmWaves;     // output columns per task
     static constexpr int kBRows = GATED ? 2 * kBN : kBN;   // weight rows per task
-    static constexpr int kBInstr = kBRows / 8 / kGemmWaves;  // B loads per wave per stage
+    static constexpr int kBAll = kBRows / 8;                            // B loads per stage (8 rows each)
+    static constexpr int kBMax = (kBAll + kLoadWaves - 1) / kLoadWaves;  // per loading wave, at most
     static constexpr int kStageB = kBRows * kRowBytes;
     // FP8: up to 128 row scales (waves 0 and 2), then the block scale(s) (wave 1)
     static constexpr int kStageS = kFP8 ? 1024 : 0;
@@ -313,27 +320,29 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     const int nk = K / (kFP8 ? 128 : 64);
     const unsigned smem_lds = lds_offset(smem);
     const int64_t ld_bytes = (int64_t)K * (kFP8 ? 1 : 2);  // bytes per operand row
-    // vector-memory loads this wave issues per stage: its B rows, its A rows
-    // (instructions w, w+4, ...) and, in FP8 mode, the row scales (wave 0) or
-    // the block scales (wave 1)
-    const int n_a = w < kAInstr ? (kAInstr - 1 - w) / kGemmWaves + 1 : 0;
-    const int loads_per_stage = C::kBInstr + n_a + ((kFP8 && (w < 2 || (w == 2 && NSUB > 4))) ? 1 : 0);
+    // vector-memory loads this wave issues per stage: B and A instructions
+    // w, w+3, ... (8 rows each) and, in FP8 mode, the row scales (waves 0
+    // and 2) or the block scales (wave 1); the scheduler wave issues none
+    const bool loader = w < kLoadWaves;
+    const int n_b = loader ? (C::kBAll - 1 - w) / kLoadWaves + 1 : 0;
+    const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / kLoadWaves + 1 : 0;
+    const int loads_per_stage = n_b + n_a + ((kFP8 && (w < 2 || (w == 2 && NSUB > 4))) ? 1 : 0);
 
     // ---- per-lane load sources (stage 0); a K block advances the A sources by
     // 128 bytes and the B sources by b_step: 128 bytes in row-major weights,
     // a whole stage in packed ones, where the stages of task (e, cb) follow
     // each other and each holds its rows already in the swizzled LDS order
-    const unsigned char* bsrc[C::kBInstr];
+    const unsigned char* bsrc[C::kBMax];
     const int64_t b_step = packed ? C::kStageB : kRowBytes;
 #pragma unroll
-    for (int j = 0; j < C::kBInstr; ++j) {
+    for (int j = 0; j < C::kBMax; ++j) {
+        const int b = w + kLoadWaves * j;  // B instruction: tile rows 8*b .. 8*b+7
         if (packed) {
             const int64_t tile = (int64_t)e * (N_out / C::kBN) + cb;
-            bsrc[j] = static_cast<const unsigned char*>(wts) + tile * nk * C::kStageB +
-                      ((w * C::kBInstr + j) * 64 + lane) * 16;
+            bsrc[j] = static_cast<const unsigned char*>(wts) + tile * nk * C::kStageB + (b * 64 + lane) * 16;
             continue;
         }
-        const int r = (w * C::kBInstr + j) * 8 + (lane >> 3);  // tile row
+        const int r = 8 * b + (lane >> 3);  // tile row (past the tile for unused b: never loaded)
         const int c = (lane & 7) ^ (r & 7);
         int64_t wrow;
         if constexpr (GATED)
@@ -343,17 +352,17 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         const int64_t rows_per_expert = GATED ? 2 * (int64_t)N_out : (int64_t)N_out;
         bsrc[j] = static_cast<const unsigned char*>(wts) + ((int64_t)e * rows_per_expert + wrow) * ld_bytes + c * 16;
     }
-    constexpr int kAMaxPerWave = (kAInstr + kGemmWaves - 1) / kGemmWaves;
+    constexpr int kAMaxPerWave = (kAInstr + kLoadWaves - 1) / kLoadWaves;
     const unsigned char* asrc[kAMaxPerWave];
     bool apad[kAMaxPerWave];
 #pragma unroll
     for (int j = 0; j < kAMaxPerWave; ++j) {
-        const int ai = w + kGemmWaves * j;  // A instruction: rows 8*ai .. 8*ai+7
+        const int ai = w + kLoadWaves * j;  // A instruction: rows 8*ai .. 8*ai+7
         const int r = 8 * ai + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
         apad[j] = false;
         asrc[j] = zero;
-        if (ai < kAInstr) {
+        if (loader && ai < kAInstr) {
             if constexpr (GATED) {
                 const int p = rows[r];
                 apad[j] = p < 0;
@@ -411,11 +420,15 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
         const int64_t koff = (int64_t)kc * kRowBytes;
         const int64_t boff = (int64_t)kc * b_step;
+        if (!loader) return;
 #pragma unroll
-        for (int j = 0; j < C::kBInstr; ++j) g2l16(bsrc[j] + boff, st + (unsigned)((w * C::kBInstr + j) * 1024));
+        for (int j = 0; j < C::kBMax; ++j) {
+            const int b = w + kLoadWaves * j;
+            if (b < C::kBAll) g2l16(bsrc[j] + boff, st + (unsigned)(b * 1024));
+        }
 #pragma unroll
         for (int j = 0; j < kAMaxPerWave; ++j) {
-            const int ai = w + kGemmWaves * j;
+            const int ai = w + kLoadWaves * j;
             if (ai < kAInstr) g2l16(apad[j] ? asrc[j] : asrc[j] + koff, st + (unsigned)(C::kStageB + ai * 1024));
         }
         if constexpr (kFP8) {
@@ -437,17 +450,23 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     const int swz = lr & 7;
     const int npro = nk < S - 1 ? nk : S - 1;
     for (int kc = 0; kc < npro; ++kc) issue(kc);
-    // the scheduler claims the next task kClaimLead K blocks before this one
-    // ends: late enough that tasks go to the workgroups that finish first,
-    // early enough that the atomic has returned when the K loop is done
     const int claim_at = nk > kClaimLead ? nk - kClaimLead : 0;
+    const int settle_at = nk > kClaimLead - 2 ? nk - (kClaimLead - 2) : 0;
+    const int rows_at = nk > kClaimLead - 4 ? nk - (kClaimLead - 4) : 0;
     for (int kc = 0; kc < nk; ++kc) {
         // stage kc is complete once at most the younger stages' loads remain
-        const int younger = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
-        wait_vm_le(younger * loads_per_stage);
+        // (each loading wave waits for its own; the barrier covers the rest)
+        if (loader) {
+            const int younger = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
+            wait_vm_le(younger * loads_per_stage);
+        }
         lds_barrier();
         if (kc + S - 1 < nk) issue(kc + S - 1);
-        if (kc == claim_at && threadIdx.x == 64 * kSchedWave) sch.issue();
+        if (w == kSchedWave) {
+            if (kc == claim_at && lane == 0) sch.claim();
+            if (kc == settle_at) sch.settle(true);
+            if (kc == rows_at) sch.load_rows(par ^ 1);
+        }
         const unsigned char* st = smem + (kc % S) * kStage;
         const unsigned char* sb = st;
         const unsigned char* sa = st + C::kStageB;
@@ -508,11 +527,11 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         }
     }
 
-    // every wave: the stage loads are complete; this also settles, for the
-    // compiler's own bookkeeping, the scheduler's atomic and any load it
-    // issued before the ring (no store of the previous task is still young)
+    // every wave: the stage loads are complete (and the scheduler's queue
+    // loads, issued two K blocks ago); this also settles, for the compiler's
+    // own bookkeeping, every load it saw (no store of the previous task is
+    // still young)
     __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-    if (w == kSchedWave) sch.fetch(true, par ^ 1);
 
     // ---- epilogue: stage the output tile in LDS, then 16-byte row stores
     lds_barrier();  // every wave is done with the ring
@@ -626,7 +645,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
     lds_barrier();
     if (threadIdx.x >= 64 * kSchedWave) {
         Sched sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
-        sch.fetch(false, 0);
+        sch.settle(false);
+        sch.load_rows(0);
         sch.publish();
     }
     lds_barrier();
@@ -668,7 +688,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
     lds_barrier();
     if (threadIdx.x >= 64 * kSchedWave) {
         Sched sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
-        sch.fetch(false, 0);
+        sch.settle(false);
+        sch.load_rows(0);
         sch.publish();
     }
     lds_barrier();
