@@ -99,7 +99,28 @@ __device__ __forceinline__ unsigned f32_to_e4m3(float f) {
     return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false) & 0xffu;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u, with the hardware reciprocal (v_rcp_f32, about 1 ulp) in
+// place of an IEEE division: the epilogue runs with one wave per SIMD, where
+// the division's long dependent sequence is not hidden
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
+// lane permutation within rows of 16 lanes (DPP; every lane reads a lane of
+// its own row, so no bound control is needed)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// max over the 16 lanes of a DPP row: swap neighbours, swap pairs (each lane
+// then holds its quad's max), mirror the 8-lane halves, mirror the row
+__device__ __forceinline__ float row16_max(float m) {
+    m = fmaxf(m, dpp<0xB1>(m));   // quad_perm [1,0,3,2]
+    m = fmaxf(m, dpp<0x4E>(m));   // quad_perm [2,3,0,1]
+    m = fmaxf(m, dpp<0x141>(m));  // row_half_mirror
+    m = fmaxf(m, dpp<0x140>(m));  // row_mirror
+    return m;
+}
 
 // Direct-to-LDS loads: lane l's 16 (or 4) bytes from its own global address
 // land at LDS byte offset lds + 16*l (or 4*l); lds must be wave-uniform (it
@@ -174,19 +195,6 @@ struct QueueLds {
     float roww[2][kAMaxRows];  // GEMM-2: routing weight of the task's rows
 };
 
-// scheduler lane 0: claim a task, waiting for each atomic (the first task,
-// and the fallback once the segment claimed from ahead has run out)
-__device__ __forceinline__ int claim_blocking(int32_t* ctl, int base, QueueLds* q, int xcd) {
-    for (int i = 0; i < kXcds; ++i) {
-        const int x = (xcd + i) & (kXcds - 1);
-        if ((q->mask >> x) & 1u) continue;
-        const int j = atomicAdd(&ctl[base + kQueueStride * x], 1);
-        if (q->seg[x] + j < q->seg[x + 1]) return q->seg[x] + j;
-        q->mask |= 1u << x;
-    }
-    return -1;
-}
-
 // Scheduler wave state of one round.  claim() runs on lane 0; the other
 // steps on the whole scheduler wave, in order.
 struct Sched {
@@ -200,6 +208,41 @@ struct Sched {
     int x = -1, raw = 0;  // lane 0: segment and result of the atomic sent ahead
     int slot = -1;
 
+    // whole scheduler wave, waiting: read every segment's counter at once
+    // (lanes 0..7, one round trip), then claim from the first segment in
+    // this XCD's order that still has tasks; repeat if another workgroup took
+    // the last one meanwhile.  -1 once every segment is exhausted.
+    __device__ __forceinline__ int claim_any() {
+        const int lane = threadIdx.x & 63;
+        for (int round = 0; round < kXcds; ++round) {
+            const int y = (xcd + lane) & (kXcds - 1);
+            bool avail = false;
+            if (lane < kXcds) {
+                const int c = __hip_atomic_load(&ctl[base + kQueueStride * y], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+                avail = q->seg[y] + c < q->seg[y + 1];
+            }
+            const uint64_t av = __ballot(avail);
+            const uint64_t gone = __ballot(lane < kXcds && !avail);
+            int got = -1;
+            if (lane == 0) {
+                for (int l = 0; l < kXcds; ++l)
+                    if ((gone >> l) & 1u) q->mask |= 1u << ((xcd + l) & (kXcds - 1));
+                if (av) {
+                    const int yy = (xcd + __builtin_ctzll(av)) & (kXcds - 1);
+                    const int j = atomicAdd(&ctl[base + kQueueStride * yy], 1);
+                    if (q->seg[yy] + j < q->seg[yy + 1])
+                        got = q->seg[yy] + j;
+                    else
+                        q->mask |= 1u << yy;
+                }
+            }
+            got = __shfl(got, 0, 64);
+            if (got >= 0 || av == 0) return got;
+        }
+        return -1;
+    }
+
     __device__ __forceinline__ void claim() {
         for (int i = 0; i < kXcds; ++i) {
             const int y = (xcd + i) & (kXcds - 1);
@@ -210,24 +253,28 @@ struct Sched {
         }
         if (x >= 0) raw = atomicAdd(&ctl[base + kQueueStride * x], 1);
     }
-    // settle the claim (ahead: the atomic sent by claim(); else claim now and
-    // wait) and start loading the record
+    // settle the claim (ahead: the atomic sent by claim(), and if its
+    // segment ran out, claim_any; else claim_any now) and start loading the
+    // record
     __device__ __forceinline__ void settle(bool ahead) {
         const int lane = threadIdx.x & 63;
+        bool search = !ahead;
         int sl = -1;
-        if (lane == 0) {
-            if (!ahead) {
-                sl = claim_blocking(ctl, base, q, xcd);
-            } else if (x >= 0) {
+        if (ahead) {
+            int got = -1, ran_out = 0;
+            if (lane == 0 && x >= 0) {
                 if (q->seg[x] + raw < q->seg[x + 1]) {
-                    sl = q->seg[x] + raw;
+                    got = q->seg[x] + raw;
                 } else {
                     q->mask |= 1u << x;
-                    sl = claim_blocking(ctl, base, q, xcd);
+                    ran_out = 1;
                 }
             }
+            sl = __shfl(got, 0, 64);
+            search = __shfl(ran_out, 0, 64) != 0;
         }
-        slot = __shfl(sl, 0, 64);
+        if (search) sl = claim_any();
+        slot = sl;
         if (slot >= 0) g2l4(reinterpret_cast<const int*>(tasks + slot) + (lane & 3), lds_offset(q->rec));
     }
     // once the record has landed: load the task's source rows into rows[par]
@@ -555,8 +602,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     float m = 0.f;
 #pragma unroll
                     for (int f = 0; f < C::kNFW; ++f) m = fmaxf(m, fabsf(hv[s][f][i]));
-#pragma unroll
-                    for (int d = 1; d < 16; d <<= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+                    m = row16_max(m);  // the 16 lanes of a row group hold one tile row
                     if (lr == 0) s_amax[w * kAMaxRows + 16 * s + 4 * lg + i] = m;
                 }
             lds_barrier();
@@ -568,11 +614,14 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     float amax = s_amax[rr];
 #pragma unroll
                     for (int ww = 1; ww < kGemmWaves; ++ww) amax = fmaxf(amax, s_amax[ww * kAMaxRows + rr]);
-                    const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+                    // scale amax/448; values are multiplied by its reciprocal
+                    // (|v| * 448/amax stays within rounding of 448, the e4m3 maximum)
+                    const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+                    const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
 #pragma unroll
                     for (int f = 0; f < C::kNFW; ++f)
                         stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] =
-                            (unsigned char)f32_to_e4m3(hv[s][f][i] / sc);
+                            (unsigned char)f32_to_e4m3(hv[s][f][i] * inv);
                     if (w == 0 && lr == 0) g1->h_scale[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
                 }
         } else {
