@@ -222,6 +222,11 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.nb1 = d_e / L.block_n1;
     r.nb2 = d_h / L.block_n2;
     r.min_tasks1 = cus * occ1;
+    // persistent grids: at most one workgroup per task, at most what fits on the chip
+    const int grid1 = (int)std::max<int64_t>(std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1), 1);
+    const int grid2 = (int)std::max<int64_t>(std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2), 1);
+    r.grid1 = grid1;
+    r.grid2 = grid2;
     r.counts = at<int32_t>(workspace, L.counts);
     r.offsets = at<int32_t>(workspace, L.offsets);
     r.padded_offsets = at<int32_t>(workspace, L.padded_offsets);
@@ -260,8 +265,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.d_h = d_h;
     g1.d_e = d_e;
     g1.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
-    const int64_t grid1 = std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1);
-    if (launch_gemm1(mode, g1, (int)std::max<int64_t>(grid1, 1), s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm1(mode, g1, grid1, s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
 
     Gemm2Args g2{};
     g2.h = g1.h;
@@ -277,8 +281,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.d_h = d_h;
     g2.d_e = d_e;
     g2.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
-    const int64_t grid2 = std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2);
-    if (launch_gemm2(mode, g2, (int)std::max<int64_t>(grid2, 1), s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm2(mode, g2, grid2, s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
 
     CombineArgs c{};
     c.y = g2.y;

@@ -253,6 +253,18 @@ struct Sched {
         }
         if (x >= 0) raw = atomicAdd(&ctl[base + kQueueStride * x], 1);
     }
+    // the workgroup's first task: the one assigned statically to it, if its
+    // segment has enough tasks, else one claimed from the queue; then start
+    // loading the record
+    __device__ __forceinline__ void first() {
+        const int xs = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+        if (j < static_tasks(gridDim.x, xs, q->seg[xs + 1] - q->seg[xs])) {
+            slot = q->seg[xs] + j;
+            g2l4(reinterpret_cast<const int*>(tasks + slot) + ((threadIdx.x & 63) & 3), lds_offset(q->rec));
+        } else {
+            settle(false);
+        }
+    }
     // settle the claim (ahead: the atomic sent by claim(), and if its
     // segment ran out, claim_any; else claim_any now) and start loading the
     // record
@@ -694,7 +706,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm1_kernel(Gemm1Args a) {
     lds_barrier();
     if (threadIdx.x >= 64 * kSchedWave) {
         Sched sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
-        sch.settle(false);
+        sch.first();
         sch.load_rows(0);
         sch.publish();
     }
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
     lds_barrier();
     if (threadIdx.x >= 64 * kSchedWave) {
         Sched sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
-        sch.settle(false);
+        sch.first();
         sch.load_rows(0);
         sch.publish();
     }

@@ -52,6 +52,16 @@ enum {
     kCtlWords = kCtlSeg2 + 16
 };
 
+// First task of GEMM workgroup g, assigned without the queue: workgroup g
+// takes task j = g / kXcds of segment x = g % kXcds if that segment has more
+// than j tasks (workgroups are dispatched to the XCDs in turn, so x is
+// normally the workgroup's own XCD).  Returns how many tasks of segment x are
+// taken that way, where the segment's queue counter starts.
+__host__ __device__ inline int static_tasks(int grid, int x, int seg_len) {
+    const int n = (grid - x + kXcds - 1) / kXcds;  // workgroups g < grid with g % kXcds == x
+    return n < seg_len ? n : seg_len;
+}
+
 // Output columns per GEMM task.  GEMM-1 FP8 needs 128 so that one task owns
 // a whole 128-column requantisation group of the intermediate and a single
 // block row of W1's scales; bf16 GEMM-1 uses 64; GEMM-2 uses 128 (one W2
@@ -65,6 +75,7 @@ struct RouteArgs {
     int64_t n_pad_cap, tile_cap;
     int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
     int32_t min_tasks1;  // GEMM-1 takes kMaxRowBlocks1-block M-tiles only if that leaves this many tasks
+    int32_t grid1, grid2;  // workgroups of the GEMM kernels (their first tasks are assigned statically)
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;
     int32_t* ctl;  // control block [kCtlWords]
     int4* tasks1;

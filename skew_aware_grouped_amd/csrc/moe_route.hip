@@ -279,7 +279,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
     }
     if (tid < 2) a.ctl[tid == 0 ? kStatTasks1 : kStatTasks2] = s_seg[tid][kXcds];
-    if (tid < 2 * kXcds) a.ctl[(tid < kXcds ? kCtlQueue1 : kCtlQueue2 - kXcds * kQueueStride) + kQueueStride * tid] = 0;
+    // queue counters start past the tasks the workgroups take statically
+    if (tid < 2 * kXcds) {
+        const int list = tid / kXcds, x = tid % kXcds;
+        a.ctl[(list == 0 ? kCtlQueue1 : kCtlQueue2) + kQueueStride * x] =
+            static_tasks(list == 0 ? a.grid1 : a.grid2, x, s_seg[list][x + 1] - s_seg[list][x]);
+    }
     if (tid < 2 * (kXcds + 1)) {
         const int list = tid / (kXcds + 1), x = tid % (kXcds + 1);
         a.ctl[(list == 0 ? kCtlSeg1 : kCtlSeg2) + x] = s_seg[list][x];
