@@ -18,12 +18,24 @@ namespace {
 
 constexpr int kLdsIds = 16384;
 
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int t = __shfl_up(v, d, 64);
-        if (lane >= d) v += t;
-    }
+// v + (the value of lane - k in the same row of 16 lanes, 0 where that lane
+// is outside the row), or with row_bcast the last lane of the previous row(s)
+// for the rows ROW_MASK selects (DPP: register-to-register, no LDS traffic)
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_add(int v) {
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Inclusive sum over lanes 0..lane of a wave64: shifts by 1, 2, 4 and 8
+// within each row of 16 lanes, then the row totals carried into rows 1 and 3
+// (row_bcast:15) and into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan(int v, int) {
+    v = dpp_add<0x111>(v);  // row_shr:1
+    v = dpp_add<0x112>(v);  // row_shr:2
+    v = dpp_add<0x114>(v);  // row_shr:4
+    v = dpp_add<0x118>(v);  // row_shr:8
+    v = dpp_add<0x142, 0xA>(v);  // row_bcast:15
+    v = dpp_add<0x143, 0xC>(v);  // row_bcast:31
     return v;
 }
 
@@ -93,7 +105,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int N = a.N;
     const bool in_lds = N <= kLdsIds;
 
-    for (int i = tid; i < kRouteWaves * kMaxExperts; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wcnt[i / E][i % E] = 0;
     if (tid == 0) s_dropped = 0;
     if (a.zero)
         for (int i = tid; i < kZeroBytes / 4; i += kRouteThreads) reinterpret_cast<int*>(a.zero)[i] = 0;
@@ -123,20 +135,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // 2. counts, then each wave's rank base per expert (earlier waves' counts),
     // then the prefix scans of the counts and of the padded counts
     for (int e = tid; e < E; e += kRouteThreads) {
+        int c[kRouteWaves];
+#pragma unroll
+        for (int w = 0; w < kRouteWaves; ++w) c[w] = s_wcnt[w][e];  // independent reads first
         int run = 0;
+#pragma unroll
         for (int w = 0; w < kRouteWaves; ++w) {
-            const int c = s_wcnt[w][e];
             s_wcnt[w][e] = run;
-            run += c;
+            run += c[w];
         }
         s_cnt[e] = run;
         s_tiles[e] = (run + kBlockM - 1) / kBlockM;
     }
     __syncthreads();
     if (wave == 0) wave_exclusive_scan256([&](int e) { return s_cnt[e]; }, s_off, E, lane);
-    if (wave == 1) wave_exclusive_scan256([&](int e) { return s_tiles[e]; }, s_poff, E, lane);
-    __syncthreads();
-    for (int e = tid; e <= E; e += kRouteThreads) s_poff[e] *= kBlockM;
+    if (wave == 1) wave_exclusive_scan256([&](int e) { return kBlockM * s_tiles[e]; }, s_poff, E, lane);
     __syncthreads();
     const int n_valid = s_off[E];
     const int n_pad = s_poff[E];
@@ -222,32 +235,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
         s_order[r] = e;
     }
-    __syncthreads();
     // GEMM-1 M-tiles: kMaxRowBlocks1 blocks (fewer weight re-reads) when that
     // still leaves min_tasks1 tasks, otherwise kMaxRowBlocks2 (more tasks to
-    // spread over the CUs)
-    if (wave == 0) {
+    // spread over the CUs); the last wave decides while the others rank
+    if (wave == kRouteWaves - 1) {
         int big = 0;
         for (int e = lane; e < E; e += 64) big += (s_tiles[e] + kMaxRowBlocks1 - 1) / kMaxRowBlocks1;
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) big += __shfl_xor(big, d, 64);
+        big = __builtin_amdgcn_readlane(wave_inclusive_scan(big, lane), 63);
         if (lane == 0) s_mb1 = big * a.nb1 >= a.min_tasks1 ? kMaxRowBlocks1 : kMaxRowBlocks2;
     }
     __syncthreads();
     const int mb1 = s_mb1;
-    for (int r = tid; r < E; r += kRouteThreads) {
-        s_mt[0][r] = (s_tiles[s_order[r]] + mb1 - 1) / mb1;
-        s_mt[1][r] = (s_tiles[s_order[r]] + kMaxRowBlocks2 - 1) / kMaxRowBlocks2;
-    }
-    __syncthreads();
+    // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2)
+    auto mtiles = [&](int list, int r) {
+        const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
+        return (s_tiles[s_order[r]] + mb - 1) / mb;
+    };
     {
         // waves 0..7: GEMM-1 list, XCD = wave; waves 8..15: GEMM-2 list
         const int list = wave / kXcds, x = wave % kXcds;
         const int nb = list == 0 ? a.nb1 : a.nb2;
-        wave_exclusive_scan256([&](int r) { return cbs_on(r, nb, x) * s_mt[list][r]; }, s_xpre[list][x], E,
+        wave_exclusive_scan256([&](int r) { return cbs_on(r, nb, x) * mtiles(list, r); }, s_xpre[list][x], E,
                                lane);
     }
-    if (wave < 2) wave_exclusive_scan256([&](int r) { return s_mt[wave][r]; }, s_mtoff[wave], E, lane);
+    if (wave < 2) {
+        wave_exclusive_scan256([&](int r) { return mtiles(wave, r); }, s_mtoff[wave], E, lane);
+        for (int r = lane; r < E; r += 64) s_mt[wave][r] = mtiles(wave, r);
+    }
     __syncthreads();
     if (tid < 2) {
         int run = 0;
