@@ -184,6 +184,9 @@ constexpr int kStoreThreads = 64 * kSchedWave;  // threads of the epilogue's sto
 // step every two K blocks, about a memory round trip apart; late enough that
 // tasks go to the workgroups that finish first
 constexpr int kClaimLead = 6;
+// rows of a task rounded up to whole 64-lane loads (the row-index loads fill
+// 64 entries per instruction)
+constexpr int kRowsLds = (kAMaxRows + 63) / 64 * 64;
 
 struct QueueLds {
     int seg[kXcds + 1];  // segment starts (and the end of the last)
@@ -191,8 +194,8 @@ struct QueueLds {
     int slot;            // the task of the next round, -1 when none is left
     int4 task;           // its record {expert, first padded row, row blocks, column block}
     int rec[64];         // landing area of the record load (16 copies)
-    int rows[2][kAMaxRows];    // row_src of the task's rows, by round parity
-    float roww[2][kAMaxRows];  // GEMM-2: routing weight of the task's rows
+    int rows[2][kRowsLds];    // row_src of the task's rows, by round parity
+    float roww[2][kRowsLds];  // GEMM-2: routing weight of the task's rows
 };
 
 // Scheduler wave state of one round.  claim() runs on lane 0; the other
@@ -300,7 +303,7 @@ struct Sched {
         const int row0 = __builtin_amdgcn_readfirstlane(q->rec[1]);
         const int n = 16 * __builtin_amdgcn_readfirstlane(q->rec[2]);
 #pragma unroll
-        for (int j = 0; j < kAMaxRows / 64; ++j) {
+        for (int j = 0; j < kRowsLds / 64; ++j) {
             if (64 * j >= n) break;
             const int r = 64 * j + lane < n ? 64 * j + lane : 0;
             g2l4(row_src + row0 + r, lds_offset(&q->rows[par][64 * j]));

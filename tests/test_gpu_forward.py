@@ -76,7 +76,7 @@ def test_workload_full_parity(oracle, name):
     _check(w, oracle, label=name)
 
 
-@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_128", "ds_fp8_1024", "ds_fp8_8192"])
+@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_128", "ds_fp8_256", "ds_fp8_512", "ds_fp8_1024", "ds_fp8_8192"])
 def test_workload_sampled_parity(oracle, name):
     print(f"generating {name}", flush=True)
     w = W.config(name)
