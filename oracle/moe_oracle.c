@@ -30,6 +30,15 @@
  * in FP8 mode the intermediate is requantised per row per 128 columns with
  * scale amax/448; ids outside [0,E) are dropped; the top-k sum runs in
  * ascending slot order from +0.0 with one final rounding.
+ *
+ * MXFP8 mode (the pages name MXFP8 as a variant of the Mixture-of-Kittens MoE
+ * kernels, PipeLink section 5.3, without defining it; the definition taken is
+ * the OCP Microscaling (MX) format): E4M3FN elements in blocks of 32
+ * consecutive values along the reduction dimension, each block with one
+ * E8M0 scale (value 2^(s-127), s = 255 is NaN); dequantised value = element *
+ * scale.  The intermediate is requantised per row per 32 columns with the
+ * shared exponent floor(log2(amax)) - 8 (8 = the largest E4M3 exponent) and
+ * saturating round-to-nearest-even elements.
  */
 #include <math.h>
 #include <stdint.h>
@@ -44,12 +53,14 @@
 #define ORACLE_MODE_F32ACT 0 /* x fp32, W bf16, out fp32 */
 #define ORACLE_MODE_BF16 1   /* x bf16, W bf16, out bf16 */
 #define ORACLE_MODE_FP8 2    /* x e4m3 + scales, W e4m3 + 128x128 block scales, out bf16 */
+#define ORACLE_MODE_MXFP8 3  /* x, W e4m3 with E8M0 scales per 32 along the reduction dimension, out bf16 */
 
 /* flags */
 #define ORACLE_MIRROR_H 1 /* round the intermediate where the method stores it */
 #define ORACLE_ACC64 2    /* evaluate in fp64 instead of fp32 */
 
 #define QBLK 128 /* block-scale granularity along every dimension */
+#define MXBLK 32 /* MX block: values along the reduction dimension sharing one scale */
 
 /* ------------------------------------------------------------------ codecs */
 
@@ -106,6 +117,9 @@ uint8_t oracle_e4m3_encode(double v) {
     return (uint8_t)(sign | best);
 }
 
+/* OCP E8M0 scale: an 8-bit biased exponent, value 2^(s-127); 255 is NaN. */
+double oracle_e8m0_decode(uint8_t s) { return s == 255 ? NAN : ldexp(1.0, (int)s - 127); }
+
 /* bfloat16: the upper 16 bits of an IEEE binary32.  Encoding rounds the
  * binary32 value to nearest with ties to even on the dropped 16 bits; NaN
  * stays a quiet NaN. */
@@ -146,34 +160,68 @@ void oracle_requant_chunk(double* a, int64_t n, int f64) {
     }
 }
 
-/* Dequantised element loaders. */
-static inline double ld_x(int mode, int f64, const void* x, const float* xs, int64_t d_h, int64_t t, int64_t c) {
-    if (mode == ORACLE_MODE_F32ACT) return ((const float*)x)[t * d_h + c];
-    if (mode == ORACLE_MODE_BF16) return oracle_bf16_decode(((const uint16_t*)x)[t * d_h + c]);
-    return R(e4m3_table[((const uint8_t*)x)[t * d_h + c]] * xs[t * (d_h / QBLK) + c / QBLK], f64);
+/* MX requantisation of one block of the intermediate (MXFP8 mode): shared
+ * exponent X = floor(log2(amax)) - 8, stored as the E8M0 byte X + 127 clamped
+ * to [0, 254] (byte 127 for an all-zero block); value -> decode(encode(v /
+ * 2^X)) * 2^X, the encode saturating at 448.  The division and product by a
+ * power of two are exact.  Writes the scale byte to *scale if non-NULL.
+ * Exported for the tests. */
+void oracle_mx_requant_block(double* a, int64_t n, uint8_t* scale) {
+    double amax = 0.0, sc;
+    int64_t i;
+    int ex = 0, b = 127;
+    oracle_init();
+    for (i = 0; i < n; ++i)
+        if (fabs(a[i]) > amax) amax = fabs(a[i]);
+    if (amax > 0.0) {
+        frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2(amax)) = ex - 1 */
+        b = ex - 1 - 8 + 127;
+        if (b < 0) b = 0;
+        if (b > 254) b = 254;
+    }
+    sc = ldexp(1.0, b - 127);
+    for (i = 0; i < n; ++i) a[i] = e4m3_table[oracle_e4m3_encode(a[i] / sc)] * sc;
+    if (scale) *scale = (uint8_t)b;
 }
 
-/* W is [E, rows, cols] row-major; scales are [E, rows/128, cols/128]. */
-static inline double ld_w(int mode, int f64, const void* w, const float* ws, int64_t rows, int64_t cols,
+/* Dequantised element loaders.  Scales are fp32 (FP8 mode) or E8M0 bytes
+ * (MXFP8 mode), passed untyped. */
+static inline double ld_x(int mode, int f64, const void* x, const void* xs, int64_t d_h, int64_t t, int64_t c) {
+    if (mode == ORACLE_MODE_F32ACT) return ((const float*)x)[t * d_h + c];
+    if (mode == ORACLE_MODE_BF16) return oracle_bf16_decode(((const uint16_t*)x)[t * d_h + c]);
+    if (mode == ORACLE_MODE_MXFP8)  /* x_scale [T, d_h/32] */
+        return e4m3_table[((const uint8_t*)x)[t * d_h + c]] *
+               oracle_e8m0_decode(((const uint8_t*)xs)[t * (d_h / MXBLK) + c / MXBLK]);
+    return R(e4m3_table[((const uint8_t*)x)[t * d_h + c]] * ((const float*)xs)[t * (d_h / QBLK) + c / QBLK], f64);
+}
+
+/* W is [E, rows, cols] row-major (cols = the reduction dimension); FP8 scales
+ * are [E, rows/128, cols/128], MXFP8 scales [E, rows, cols/32]. */
+static inline double ld_w(int mode, int f64, const void* w, const void* ws, int64_t rows, int64_t cols,
                           int64_t e, int64_t r, int64_t c) {
     int64_t i = (e * rows + r) * cols + c;
+    if (mode == ORACLE_MODE_MXFP8)
+        return e4m3_table[((const uint8_t*)w)[i]] *
+               oracle_e8m0_decode(((const uint8_t*)ws)[(e * rows + r) * (cols / MXBLK) + c / MXBLK]);
     if (mode != ORACLE_MODE_FP8) return oracle_bf16_decode(((const uint16_t*)w)[i]);
-    return R(e4m3_table[((const uint8_t*)w)[i]] * ws[(e * (rows / QBLK) + r / QBLK) * (cols / QBLK) + c / QBLK],
+    return R(e4m3_table[((const uint8_t*)w)[i]] *
+                 ((const float*)ws)[(e * (rows / QBLK) + r / QBLK) * (cols / QBLK) + c / QBLK],
              f64);
 }
 
 static int check_dims(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_e) {
     if (T < 0 || E < 1 || k < 1 || d_h < 1 || d_e < 1) return 0;
-    if (mode < 0 || mode > 2) return 0;
+    if (mode < 0 || mode > 3) return 0;
     if (mode == ORACLE_MODE_FP8 && (d_h % QBLK || d_e % QBLK)) return 0;
+    if (mode == ORACLE_MODE_MXFP8 && (d_h % MXBLK || d_e % MXBLK)) return 0;
     return 1;
 }
 
 /* Expert FFN of one assignment: y = W2[e] . (silu(g) * u), g and u from
  * W1[e] rows [0,d_e) and [d_e,2 d_e).  Accumulations run in ascending index
  * order.  a is scratch of d_e doubles, y receives d_h values. */
-static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void* x, const float* xs, int64_t t,
-                       const void* w1, const float* w1s, const void* w2, const float* w2s, int64_t e, double* a,
+static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void* x, const void* xs, int64_t t,
+                       const void* w1, const void* w1s, const void* w2, const void* w2s, int64_t e, double* a,
                        double* y) {
     int f64 = (flags & ORACLE_ACC64) != 0;
     int64_t r, c, n;
@@ -191,6 +239,8 @@ static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void
     if (flags & ORACLE_MIRROR_H) {
         if (mode == ORACLE_MODE_FP8) {
             for (r = 0; r < d_e; r += QBLK) oracle_requant_chunk(a + r, QBLK, f64);
+        } else if (mode == ORACLE_MODE_MXFP8) {
+            for (r = 0; r < d_e; r += MXBLK) oracle_mx_requant_block(a + r, MXBLK, NULL);
         } else {
             for (r = 0; r < d_e; ++r) a[r] = oracle_bf16_decode(oracle_bf16_encode((float)a[r]));
         }
@@ -209,15 +259,16 @@ static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void
  * mode's output dtype (fp32 in F32ACT mode, bf16 bits otherwise).
  */
 int moe_oracle_forward(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_e, const void* x,
-                       const float* x_scale, const int32_t* topk_ids, const float* topk_w, const void* w1,
-                       const float* w1_scale, const void* w2, const float* w2_scale, int flags,
+                       const void* x_scale, const int32_t* topk_ids, const float* topk_w, const void* w1,
+                       const void* w1_scale, const void* w2, const void* w2_scale, int flags,
                        const int64_t* rows, int64_t nrows, double* out_acc, void* out) {
     int64_t i;
     int f64 = (flags & ORACLE_ACC64) != 0;
     int failed = 0;
     if (!check_dims(mode, T, E, k, d_h, d_e)) return ORACLE_EINVAL;
     if (!x || !topk_ids || !topk_w || !w1 || !w2 || !out_acc) return ORACLE_EINVAL;
-    if (mode == ORACLE_MODE_FP8 && (!x_scale || !w1_scale || !w2_scale)) return ORACLE_EINVAL;
+    if ((mode == ORACLE_MODE_FP8 || mode == ORACLE_MODE_MXFP8) && (!x_scale || !w1_scale || !w2_scale))
+        return ORACLE_EINVAL;
     if (!rows) nrows = T;
     oracle_init();
 #pragma omp parallel for schedule(dynamic, 1)

@@ -22,6 +22,7 @@ _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 MODE_F32ACT = 0
 MODE_BF16 = 1
 MODE_FP8 = 2
+MODE_MXFP8 = 3
 MIRROR_H = 1
 ACC64 = 2
 
@@ -62,6 +63,10 @@ def _load():
     lib.oracle_bf16_decode.argtypes = [ctypes.c_uint16]
     lib.oracle_requant_chunk.restype = None
     lib.oracle_requant_chunk.argtypes = [vp, i64, i32]
+    lib.oracle_e8m0_decode.restype = ctypes.c_double
+    lib.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_mx_requant_block.restype = None
+    lib.oracle_mx_requant_block.argtypes = [vp, i64, vp]
     lib.moe_oracle_forward.restype = i32
     lib.moe_oracle_forward.argtypes = [i32, i64, i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                        vp, i64, vp, vp]
@@ -106,6 +111,21 @@ def requant_chunk(values, acc64: bool = False) -> np.ndarray:
     a = np.ascontiguousarray(np.asarray(values, dtype=np.float64).copy())
     lib.oracle_requant_chunk(_ptr(a), a.size, 1 if acc64 else 0)
     return a
+
+
+def e8m0_decode(scales) -> np.ndarray:
+    lib = _load()
+    s = np.asarray(scales, dtype=np.uint8)
+    return np.array([lib.oracle_e8m0_decode(int(v)) for v in s.ravel()], dtype=np.float64).reshape(s.shape)
+
+
+def mx_requant_block(values):
+    """MX requantisation of one block of the intermediate: (dequantised values, E8M0 scale byte)."""
+    lib = _load()
+    a = np.ascontiguousarray(np.asarray(values, dtype=np.float64).copy())
+    sc = np.zeros(1, np.uint8)
+    lib.oracle_mx_requant_block(_ptr(a), a.size, _ptr(sc))
+    return a, int(sc[0])
 
 
 # ----------------------------------------------------------------- routing
@@ -164,16 +184,17 @@ def forward(inp, rows=None, mirror: bool = True, acc64: bool = False):
     def c(a, dt):
         return None if a is None else np.ascontiguousarray(a, dtype=dt)
 
-    xdt = {MODE_F32ACT: np.float32, MODE_BF16: np.uint16, MODE_FP8: np.uint8}[mode]
-    wdt = np.uint8 if mode == MODE_FP8 else np.uint16
+    xdt = {MODE_F32ACT: np.float32, MODE_BF16: np.uint16, MODE_FP8: np.uint8, MODE_MXFP8: np.uint8}[mode]
+    wdt = np.uint8 if mode in (MODE_FP8, MODE_MXFP8) else np.uint16
+    sdt = np.uint8 if mode == MODE_MXFP8 else np.float32  # E8M0 bytes or fp32 scales
     x = c(inp.x, xdt)
-    xs = c(inp.x_scale, np.float32)
+    xs = c(inp.x_scale, sdt)
     ids = c(inp.topk_ids, np.int32)
     tw = c(inp.topk_w, np.float32)
     w1 = c(inp.w1, wdt)
-    w1s = c(inp.w1_scale, np.float32)
+    w1s = c(inp.w1_scale, sdt)
     w2 = c(inp.w2, wdt)
-    w2s = c(inp.w2_scale, np.float32)
+    w2s = c(inp.w2_scale, sdt)
     flags = (MIRROR_H if mirror else 0) | (ACC64 if acc64 else 0)
     rc = lib.moe_oracle_forward(mode, int(inp.T), int(inp.E), int(inp.k), int(inp.d_h), int(inp.d_e),
                                 _ptr(x), _ptr(xs), _ptr(ids), _ptr(tw), _ptr(w1), _ptr(w1s), _ptr(w2), _ptr(w2s),

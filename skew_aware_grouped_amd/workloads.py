@@ -20,11 +20,18 @@ and skewed routing with hot and empty experts:
                  28 share the rest by Zipf(1.0) (largest remainder, at least 1).
 * ``ds_fp8_8192`` 8192 tokens, 7168/2048, FP8; two experts get 30% each, 16
                  experts none, 14 share the rest by Zipf(1.0).
+* ``qwen_mxfp8``, ``ds_mxfp8_<T>`` (T in {1024, 8192}): the same recipes in MXFP8
+                 (the MX variant the pages name for the MoE kernels of PipeLink
+                 section 5.3): e4m3 codes with one E8M0 scale per 32 values along
+                 the reduction dimension.
 
 Weights are N(0, 1/fan_in); activations N(0, 1).  FP8 tensors are e4m3 codes
 (OCP E4M3FN) with fp32 scales s = amax/448 per 128x128 weight block and per
 token per 128 activation columns; the cast to e4m3 is torch's.  Combine
-weights are the softmax of N(0,1) logits over the k chosen experts.
+weights are the softmax of N(0,1) logits over the k chosen experts.  MXFP8
+tensors: per 32 values along the reduction dimension, shared exponent
+X = floor(log2(amax)) - 8, scale byte X + 127, codes = e4m3(v / 2^X) with the
+quotient clamped to +-448 before torch's cast.
 Randomness: ``numpy.random.default_rng([1000 + config_index, stream])`` with
 streams 0 (x), 1 (W1), 2 (W2), 3 (routing), 4 (logits).
 """
@@ -39,7 +46,9 @@ import numpy as np
 MODE_F32ACT = 0
 MODE_BF16 = 1
 MODE_FP8 = 2
+MODE_MXFP8 = 3
 QBLK = 128
+MXBLK = 32
 
 STREAM_X, STREAM_W1, STREAM_W2, STREAM_ROUTE, STREAM_LOGITS = range(5)
 
@@ -114,6 +123,17 @@ def quantize_blocks(a: np.ndarray):
     return q, s
 
 
+def quantize_mx(a: np.ndarray):
+    """[R, C] float -> e4m3 codes [R, C], E8M0 scale bytes [R, C/32] (per row per 32 columns)."""
+    R, C = a.shape
+    blk = a.reshape(R, C // MXBLK, MXBLK).astype(np.float64)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))  # amax = f 2^ex, f in [0.5, 1)
+    b = np.where(amax > 0, np.clip(ex - 1 - 8 + 127, 0, 254), 127).astype(np.int64)
+    q = np.clip(blk / np.ldexp(1.0, b - 127)[:, :, None], -448.0, 448.0)
+    return _to_e4m3_codes(q.reshape(R, C).astype(np.float32)), b.astype(np.uint8)
+
+
 # ---------------------------------------------------------------- routing
 def route_uniform(rng, T, E, k):
     return np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -176,6 +196,9 @@ for _T in (128, 256, 512, 1024):
                                    routing=("exact", (int(round(0.4 * _T * 2)),), 3, 1.0))
 CONFIGS["ds_fp8_8192"] = dict(index=4, T=8192, E=32, k=2, d_h=7168, d_e=2048, mode=MODE_FP8,
                               routing=("exact", (4915, 4915), 16, 1.0))
+CONFIGS["qwen_mxfp8"] = dict(CONFIGS["qwen_fp8"], index=5, mode=MODE_MXFP8)
+CONFIGS["ds_mxfp8_1024"] = dict(CONFIGS["ds_fp8_1024"], index=6, mode=MODE_MXFP8)
+CONFIGS["ds_mxfp8_8192"] = dict(CONFIGS["ds_fp8_8192"], index=7, mode=MODE_MXFP8)
 
 
 def make_routing(index, T, E, k, routing):
@@ -205,13 +228,23 @@ def _weights(index, E, d_h, d_e, mode):
         for e in range(E):
             w2[e], w2_scale[e] = quantize_blocks(r2.standard_normal((d_h, d_e), dtype=np.float32) * s2)
         return w1, w2, w1_scale, w2_scale
+    if mode == MODE_MXFP8:
+        w1 = np.empty((E, 2 * d_e, d_h), np.uint8)
+        w2 = np.empty((E, d_h, d_e), np.uint8)
+        w1_scale = np.empty((E, 2 * d_e, d_h // MXBLK), np.uint8)
+        w2_scale = np.empty((E, d_h, d_e // MXBLK), np.uint8)
+        for e in range(E):
+            w1[e], w1_scale[e] = quantize_mx(r1.standard_normal((2 * d_e, d_h), dtype=np.float32) * s1)
+        for e in range(E):
+            w2[e], w2_scale[e] = quantize_mx(r2.standard_normal((d_h, d_e), dtype=np.float32) * s2)
+        return w1, w2, w1_scale, w2_scale
     w1 = np.stack([to_bf16_bits(r1.standard_normal((2 * d_e, d_h), dtype=np.float32) * s1) for _ in range(E)])
     w2 = np.stack([to_bf16_bits(r2.standard_normal((d_h, d_e), dtype=np.float32) * s2) for _ in range(E)])
     return w1, w2, None, None
 
 
 def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) -> MoEWorkload:
-    if mode == MODE_FP8:
+    if mode in (MODE_FP8, MODE_MXFP8):
         assert d_h % QBLK == 0 and d_e % QBLK == 0
     ids = make_routing(index, T, E, k, routing) if topk_ids is None else np.asarray(topk_ids, np.int32)
     lg = _rng(index, STREAM_LOGITS).standard_normal((T, k))
@@ -222,6 +255,8 @@ def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) 
     x_scale = None
     if mode == MODE_FP8:
         x, x_scale = quantize_rows(xf)
+    elif mode == MODE_MXFP8:
+        x, x_scale = quantize_mx(xf)
     else:
         x = xf if mode == MODE_F32ACT else to_bf16_bits(xf)
     return MoEWorkload(name=name, mode=mode, T=T, E=E, k=k, d_h=d_h, d_e=d_e, x=x, topk_ids=ids, topk_w=tw,
@@ -250,11 +285,15 @@ def algorithmic_bytes(w: MoEWorkload) -> float:
     """Bytes the layer must move once: the active experts' weights (+scales), x (+scales),
     out, and the routing ids and weights."""
     a = w.active_experts()
-    wb = 1 if w.mode == MODE_FP8 else 2
+    wb = 1 if w.mode in (MODE_FP8, MODE_MXFP8) else 2
     per_expert = 3 * w.d_h * w.d_e * wb
     if w.mode == MODE_FP8:
         per_expert += 4 * (2 * w.d_e // QBLK) * (w.d_h // QBLK) + 4 * (w.d_h // QBLK) * (w.d_e // QBLK)
-    xb = {MODE_F32ACT: 4, MODE_BF16: 2, MODE_FP8: 1}[w.mode]
+    if w.mode == MODE_MXFP8:
+        per_expert += 3 * w.d_h * w.d_e // MXBLK
+    xb = {MODE_F32ACT: 4, MODE_BF16: 2, MODE_FP8: 1, MODE_MXFP8: 1}[w.mode]
     x_bytes = w.T * w.d_h * xb + (w.T * (w.d_h // QBLK) * 4 if w.mode == MODE_FP8 else 0)
+    if w.mode == MODE_MXFP8:
+        x_bytes += w.T * (w.d_h // MXBLK)
     out_bytes = w.T * w.d_h * (4 if w.mode == MODE_F32ACT else 2)
     return float(a * per_expert + x_bytes + out_bytes + w.T * w.k * 8)

@@ -4,6 +4,7 @@ The FP8 format is OCP E4M3FN (one reading of the pages, which say only "FP8");
 bf16 is the upper half of binary32 with round-to-nearest-even.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -115,3 +116,54 @@ def test_requant_chunk_matches_torch_pipeline(oracle):
 
 def test_requant_chunk_all_zero(oracle):
     assert np.array_equal(oracle.requant_chunk(np.zeros(128)), np.zeros(128))
+
+
+# ----------------------------------------------------------------- MXFP8
+def test_e8m0_decode_all_bytes(oracle):
+    """E8M0 byte s is the biased exponent of 2^(s-127) (the binary32 with exponent
+    field s and zero mantissa for s in 1..254; s = 0 is 2^-127, s = 255 is NaN)."""
+    s = np.arange(256, dtype=np.uint32)
+    got = oracle.e8m0_decode(s.astype(np.uint8))
+    ref = (s[1:255] << 23).view(np.float32).astype(np.float64)
+    assert np.array_equal(got[1:255], ref)
+    assert got[0] == 2.0 ** -127 and np.isnan(got[255])
+
+
+def _torch_mx_block(v):
+    """MX quantise-dequantise of one block, from the format's definition, by torch:
+    X = floor(log2(amax)) - 8; e4m3 cast of v / 2^X clamped to +-448; times 2^X."""
+    import torch
+    t = torch.tensor(v, dtype=torch.float64)
+    amax = float(t.abs().max())
+    if amax == 0:
+        return t.numpy(), 127
+    x = math.floor(math.log2(amax)) - 8
+    q = torch.clamp(t / 2.0 ** x, -448, 448).float().to(torch.float8_e4m3fn).double()
+    return (q * 2.0 ** x).numpy(), x + 127
+
+
+def test_mx_requant_block_matches_definition(oracle):
+    rng = np.random.default_rng(4)
+    cases = [rng.standard_normal(32) * 10.0 ** rng.uniform(-6, 6) for _ in range(200)]
+    cases += [np.zeros(32), np.full(32, 2.0 ** 5), np.linspace(-1, 1, 32) * 1.9 * 2.0 ** 3,
+              np.r_[448.0 * 2 ** -8, np.zeros(31)], rng.standard_normal(32) * 1e-30]
+    for v in cases:
+        got, b = oracle.mx_requant_block(v)
+        ref, rb = _torch_mx_block(v)
+        assert b == rb
+        assert np.array_equal(got, ref)
+
+
+def test_mx_requant_saturates_and_brackets_amax(oracle):
+    """The shared exponent puts amax in [2^(X+8), 2^(X+9)); quotients above 448 clamp."""
+    v = np.zeros(32)
+    v[0] = 1.99 * 2 ** 4   # amax: X = 4 - 8 = -4, quotient 1.99 * 2^8 = 509.4 -> 448
+    v[1] = -0.75
+    got, b = oracle.mx_requant_block(v)
+    assert b == 127 - 4
+    assert got[0] == 448.0 * 2.0 ** -4 and got[1] == -0.75
+    for _ in range(50):
+        w = np.random.default_rng(_).standard_normal(32) * 3.0
+        _, b = oracle.mx_requant_block(w)
+        amax = np.abs(w).max()
+        assert 2.0 ** (b - 127 + 8) <= amax < 2.0 ** (b - 127 + 9)

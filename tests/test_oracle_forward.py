@@ -34,11 +34,17 @@ def _deq_x(w):
     if w.mode == W.MODE_BF16:
         return torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).double()
     q = torch.from_numpy(w.x).view(torch.float8_e4m3fn).double()
+    if w.mode == W.MODE_MXFP8:  # E8M0 byte b per token per 32 columns: 2^(b - 127)
+        e = torch.from_numpy(w.x_scale.astype(np.int64) - 127).repeat_interleave(32, dim=1)
+        return torch.ldexp(q, e)
     s = torch.from_numpy(w.x_scale).double().repeat_interleave(128, dim=1)
     return q * s
 
 
 def _deq_w(w, a, s):
+    if w.mode == W.MODE_MXFP8:  # [E, rows, cols/32] bytes, one per row per 32 along K
+        q = torch.from_numpy(a).view(torch.float8_e4m3fn).double()
+        return torch.ldexp(q, torch.from_numpy(s.astype(np.int64) - 127).repeat_interleave(32, dim=2))
     if w.mode != W.MODE_FP8:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).double()
     q = torch.from_numpy(a).view(torch.float8_e4m3fn).double()
@@ -49,6 +55,16 @@ def _deq_w(w, a, s):
 def _torch_h_round(a, mode):
     if mode in (W.MODE_F32ACT, W.MODE_BF16):
         return a.float().to(torch.bfloat16).double()
+    if mode == W.MODE_MXFP8:
+        # per row per 32: X = floor(log2(amax)) - 8 (from frexp's exponent), values / 2^X
+        # clamped to the e4m3 range and cast by torch, times 2^X
+        T, D = a.shape
+        blk = a.reshape(T, D // 32, 32)
+        amax = blk.abs().amax(dim=2, keepdim=True)
+        _, ex = torch.frexp(torch.where(amax > 0, amax, torch.ones_like(amax)))
+        x = torch.where(amax > 0, ex - 1 - 8, torch.zeros_like(ex)).clamp(-127, 127)
+        q = torch.ldexp(blk, -x).clamp(-448, 448).float().to(torch.float8_e4m3fn).double()
+        return torch.ldexp(q, x).reshape(T, D)
     T, D = a.shape
     blk = a.float().reshape(T, D // 128, 128)
     amax = blk.abs().amax(dim=2, keepdim=True)
@@ -82,7 +98,7 @@ def _small(mode, T=24, E=5, k=3, d_h=256, d_e=256, seed=3, ids=None):
     return W.custom(T, E, k, d_h, d_e, mode, seed=seed, routing=routing, topk_ids=ids)
 
 
-MODES = [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8]
+MODES = [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -138,7 +154,10 @@ def test_rounding_point_of_intermediate(oracle, mode):
     ref_m = dense_moe(w, h_round=True)
     assert normwise(acc_m, ref_m) < 2e-3
     gap = normwise(acc_p, acc_m)
-    assert 5e-3 > gap > 1e-4 if mode != W.MODE_FP8 else 3e-2 > gap > 1e-3
+    # MX requantisation saturates the largest values of a block (the shared
+    # exponent leaves them in [256, 512) against an e4m3 maximum of 448)
+    lo_hi = {W.MODE_FP8: (1e-3, 3e-2), W.MODE_MXFP8: (1e-3, 6e-2)}.get(mode, (1e-4, 5e-3))
+    assert lo_hi[1] > gap > lo_hi[0]
 
 
 @pytest.mark.parametrize("name", ["tiny"])
@@ -225,3 +244,27 @@ def test_all_dropped_token_is_zero(oracle):
     w.topk_ids = ids
     acc, out = oracle.forward(w)
     assert np.all(acc[2] == 0) and np.all(out[2] == 0)
+
+
+def test_mxfp8_with_power_of_two_blocks_equals_fp8(oracle):
+    """MXFP8 whose scale bytes are constant over each 128x128 weight block and each
+    128 activation columns is the FP8 block-scaled layer with scales 2^(b-127):
+    both modes of the oracle must agree exactly (pins the MX scale indexing,
+    per row and per 32 along the reduction dimension, to the pinned FP8 path)."""
+    rng = np.random.default_rng(11)
+    T, E, k, d_h, d_e = 12, 3, 2, 256, 256
+    w = _small(W.MODE_FP8, T=T, E=E, k=k, d_h=d_h, d_e=d_e, seed=5)
+    ex1 = rng.integers(-3, 4, size=w.w1_scale.shape)
+    ex2 = rng.integers(-3, 4, size=w.w2_scale.shape)
+    exx = rng.integers(-3, 4, size=w.x_scale.shape)
+    w.w1_scale = np.ldexp(1.0, ex1).astype(np.float32)
+    w.w2_scale = np.ldexp(1.0, ex2).astype(np.float32)
+    w.x_scale = np.ldexp(1.0, exx).astype(np.float32)
+    acc_fp8, _ = oracle.forward(w, mirror=False)
+    m = W.custom(T, E, k, d_h, d_e, W.MODE_MXFP8, seed=5)
+    m.x, m.w1, m.w2, m.topk_ids, m.topk_w = w.x, w.w1, w.w2, w.topk_ids, w.topk_w
+    m.x_scale = (exx + 127).astype(np.uint8).repeat(4, axis=1)                      # [T, d_h/32]
+    m.w1_scale = (ex1 + 127).astype(np.uint8).repeat(128, axis=1).repeat(4, axis=2)  # [E, 2 d_e, d_h/32]
+    m.w2_scale = (ex2 + 127).astype(np.uint8).repeat(128, axis=1).repeat(4, axis=2)  # [E, d_h, d_e/32]
+    acc_mx, _ = oracle.forward(m, mirror=False)
+    assert np.array_equal(acc_fp8, acc_mx)
