@@ -2,7 +2,7 @@
 
 Each case edits one plausible mistake into a copy of the oracle's C source
 (dropped term, wrong sign, wrong index, transposed operand, broken rounding,
-broken stability), builds it, and runs the CPU pin tests against it in a
+broken stability, a wrong MX scale index, exponent or bias), builds it, and runs the CPU pin tests against it in a
 subprocess; the run must fail.  The product path is not involved.
 """
 import os
@@ -25,8 +25,12 @@ MUTATIONS = {
     "bf16_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
     "e4m3_bias_8": ("ex - 7)", "ex - 8)"),
     "first_slot_skipped": ("for (j = 0; j < k; ++j)", "for (j = 1; j < k; ++j)"),
-    "x_scale_block_ignored": ("xs[t * (d_h / QBLK) + c / QBLK]", "xs[t * (d_h / QBLK)]"),
+    "x_scale_block_ignored": ("xs)[t * (d_h / QBLK) + c / QBLK]", "xs)[t * (d_h / QBLK)]"),
     "w_scale_col_block_ignored": ("* (cols / QBLK) + c / QBLK]", "* (cols / QBLK)]"),
+    "mx_x_scale_block_ignored": ("xs)[t * (d_h / MXBLK) + c / MXBLK]", "xs)[t * (d_h / MXBLK)]"),
+    "mx_w_scale_row_ignored": ("[(e * rows + r) * (cols / MXBLK) + c / MXBLK]", "[(e * rows) * (cols / MXBLK) + c / MXBLK]"),
+    "mx_shared_exponent_off_by_one": ("b = ex - 1 - 8 + 127;", "b = ex - 8 + 127;"),
+    "e8m0_bias_128": ("ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
 }
 
 PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_routing.py", "tests/test_oracle_forward.py"]
