@@ -28,21 +28,24 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused MoE layer p50 µs + TFLOP/s (% MFMA/HBM roofline), 1 MI355X"
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 5000.0}  # dense MFMA: bf16 (F32ACT runs bf16 MFMA), fp8
-DTYPE = {0: "bf16", 1: "bf16", 2: "fp8_e4m3"}
+PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 5000.0, 3: 5000.0}  # dense MFMA: bf16 (F32ACT runs bf16 MFMA), fp8
+DTYPE = {0: "bf16", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp8_e4m3"}
 DEFAULT_CONFIG = "qwen_bf16"
 
 
 def gemm1_alg_bytes(w):
-    """Bytes GEMM-1 must move once: active experts' W1 (+ block scales), x (+ scales), h (+ scales)."""
+    """Bytes GEMM-1 must move once: active experts' W1 (+ scales), x (+ scales), h (+ scales)."""
     from skew_aware_grouped_amd import workloads as W
     a = w.active_experts()
-    wb = 1 if w.mode == W.MODE_FP8 else 2
-    xb = {W.MODE_F32ACT: 4, W.MODE_BF16: 2, W.MODE_FP8: 1}[w.mode]
+    fp8 = w.mode in (W.MODE_FP8, W.MODE_MXFP8)
+    wb = 1 if fp8 else 2
+    xb = 1 if fp8 else {W.MODE_F32ACT: 4, W.MODE_BF16: 2}[w.mode]
     nv = w.valid_assignments()
     b = a * 2 * w.d_e * w.d_h * wb + w.T * w.d_h * xb + nv * w.d_e * wb
-    if w.mode == W.MODE_FP8:
+    if w.mode == W.MODE_FP8:  # fp32 scales per 128x128 block (W1), per row per 128 (x, h)
         b += a * (2 * w.d_e // 128) * (w.d_h // 128) * 4 + w.T * (w.d_h // 128) * 4 + nv * (w.d_e // 128) * 4
+    if w.mode == W.MODE_MXFP8:  # one E8M0 byte per row per 32 values
+        b += a * 2 * w.d_e * (w.d_h // 32) + w.T * (w.d_h // 32) + nv * (w.d_e // 32)
     return float(b)
 
 
@@ -145,7 +148,7 @@ def main():
         return
     w = W.config(args.config)
     d = device.upload(w, packed=args.weights == "packed")
-    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], weight_layout=d["weight_layout"])
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], weight_layout=d["weight_layout"], x_scale=d["x_scale"])
     ws = moe.workspace_for(dims, "cuda:0")
     odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
     out = torch.empty(w.T, w.d_h, dtype=odt, device="cuda:0")
@@ -158,7 +161,7 @@ def main():
     acc, _ = moe_oracle.forward(w, rows=rows)
     got = device.out_to_f64(out)[rows]
     gate_err = float(np.abs(got - acc).max() / np.abs(acc).max())
-    tol = 3e-2 if w.mode == W.MODE_FP8 else 1e-2
+    tol = 3e-2 if w.mode in (W.MODE_FP8, W.MODE_MXFP8) else 1e-2
     if not gate_err <= tol:
         print(f"bench.py: correctness gate failed (normwise err {gate_err:.3e} > {tol})", file=sys.stderr)
         sys.exit(1)

@@ -8,7 +8,10 @@
  * GEMM-2 applies the down projection, scales each row by its routing weight and
  * the per-token rows are summed.  The activation is SwiGLU, silu(gate) * up,
  * taken on the unrounded fp32 accumulator (PipeLink, section 5.5 "Fused GEMM
- * and Activation").  FP8 is OCP E4M3FN with fp32 block scales.
+ * and Activation").  FP8 is OCP E4M3FN with fp32 block scales.  MXFP8, which
+ * the pages name as a variant of the Mixture-of-Kittens MoE kernels (PipeLink,
+ * section 5.3) without defining it, is taken as the OCP Microscaling format:
+ * E4M3FN values with one E8M0 scale per 32 consecutive values along K.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers (HIP global memory) of the current
@@ -47,10 +50,17 @@ extern "C" {
  *  MOE_MODE_F32ACT  x fp32 [T,d_h]; W1, W2 bf16; out fp32.  The GEMMs run on
  *                   bf16 MFMA, so x is rounded to bf16 (nearest-even) on load.
  *  MOE_MODE_BF16    x, W1, W2, out bf16.
- *  MOE_MODE_FP8     x, W1, W2 e4m3 codes with fp32 scales; out bf16. */
+ *  MOE_MODE_FP8     x, W1, W2 e4m3 codes with fp32 128x128 block scales; out
+ *                   bf16.  The intermediate is requantised per row per 128
+ *                   columns (scale amax/448).
+ *  MOE_MODE_MXFP8   x, W1, W2 e4m3 codes with E8M0 scales per 32 values along
+ *                   K; out bf16.  The intermediate is requantised per row per
+ *                   32 columns (shared exponent floor(log2 amax) - 8, elements
+ *                   saturated to +-448). */
 #define MOE_MODE_F32ACT 0
 #define MOE_MODE_BF16 1
 #define MOE_MODE_FP8 2
+#define MOE_MODE_MXFP8 3
 
 /* Storage order of W1 and W2 (moe_dims.weight_layout):
  *  MOE_WEIGHTS_ROW_MAJOR  w1 [E, 2*d_e, d_h], w2 [E, d_h, d_e] as described for
@@ -75,15 +85,21 @@ typedef struct {
     int32_t weight_layout; /* MOE_WEIGHTS_* */
 } moe_dims;
 
-/* FP8 block scales (fp32, dequantised value = code * scale).  Required in
- * MOE_MODE_FP8, ignored otherwise.
+/* Scales of the quantised modes (dequantised value = code * scale).  Required
+ * in MOE_MODE_FP8 and MOE_MODE_MXFP8, ignored otherwise.
+ * MOE_MODE_FP8, fp32:
  *  x_scale   [T, d_h/128]                 one scale per token per 128 columns
  *  w1_scale  [E, 2*d_e/128, d_h/128]      one scale per 128x128 block of W1
- *  w2_scale  [E, d_h/128, d_e/128]        one scale per 128x128 block of W2 */
+ *  w2_scale  [E, d_h/128, d_e/128]        one scale per 128x128 block of W2
+ * MOE_MODE_MXFP8, uint8 E8M0 (byte s means 2^(s-127); s = 255 is NaN and
+ * makes the rows it scales NaN):
+ *  x_scale   [T, d_h/32]                  one byte per token per 32 columns
+ *  w1_scale  [E, 2*d_e, d_h/32]           one byte per W1 row per 32 columns
+ *  w2_scale  [E, d_h, d_e/32]             one byte per W2 row per 32 columns */
 typedef struct {
-    const float* x_scale;
-    const float* w1_scale;
-    const float* w2_scale;
+    const void* x_scale;
+    const void* w1_scale;
+    const void* w2_scale;
 } moe_scales;
 
 /* Bytes of device workspace moe_fused_forward needs for these dims (routing
@@ -103,7 +119,7 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
  *  w1        [E, 2*d_e, d_h]     rows [0,d_e) gate, [d_e,2*d_e) up; K (d_h) contiguous
  *  w2        [E, d_h, d_e]       K (d_e) contiguous
  *                                (with MOE_WEIGHTS_PACKED: the outputs of moe_pack_weights)
- *  scales    FP8 mode only (may be NULL otherwise)
+ *  scales    FP8 and MXFP8 modes only (may be NULL otherwise)
  *  out       [T, d_h]            fp32 (F32ACT) or bf16; every row is written
  *  workspace device buffer of at least moe_workspace_bytes(dims) bytes, 256-byte aligned
  *
@@ -136,7 +152,8 @@ MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, cons
  * permutation moves 16-byte chunks; block scales keep their layout.
  *
  * With eb bytes per element (2 for bf16, 1 for e4m3) and the column-block
- * widths of moe_ws_layout (block_n1: 64 in the bf16 modes, 128 in FP8 mode;
+ * widths of moe_ws_layout (block_n1: 64 in the bf16 modes, 128 in the FP8 and
+ * MXFP8 modes;
  * block_n2: 128), let R1 = d_h*eb/128 and R2 = d_e*eb/128 (128-byte K blocks
  * per weight row), n1 = d_e/block_n1, n2 = d_h/128.  Then, for 0 <= s < 8:
  *  w1_packed chunk (((e*n1 + c)*R1 + b)*2*block_n1 + r)*8 + s holds bytes

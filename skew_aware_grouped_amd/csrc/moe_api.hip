@@ -15,7 +15,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool dims_ok(const moe_dims* d) {
     if (!d) return false;
-    if (d->mode < MOE_MODE_F32ACT || d->mode > MOE_MODE_FP8) return false;
+    if (d->mode < MOE_MODE_F32ACT || d->mode > MOE_MODE_MXFP8) return false;
     if (d->num_tokens < 0 || d->num_experts < 1 || d->num_experts > kMaxExperts) return false;
     if (d->top_k < 1 || d->top_k > 8) return false;
     if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return false;
@@ -44,7 +44,7 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     L->max_row_blocks = kMaxRowBlocks1;
     L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
     L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
-    const size_t hb = d->mode == MOE_MODE_FP8 ? 1 : 2;
+    const size_t hb = mode_fp8(d->mode) ? 1 : 2;
     const size_t yb = d->mode == MOE_MODE_F32ACT ? 4 : 2;
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -66,7 +66,10 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     L->tasks1 = take(16 * L->task1_cap);
     L->tasks2 = take(16 * L->task2_cap);
     L->h = take(hb * L->n_pad_cap * d->d_expert);
-    L->h_scale = take(d->mode == MOE_MODE_FP8 ? 4 * L->n_pad_cap * (d->d_expert / kQ) : 0);
+    // FP8: fp32 per row per 128 columns; MXFP8: one E8M0 byte per row per 32 columns
+    L->h_scale = take(d->mode == MOE_MODE_FP8     ? 4 * L->n_pad_cap * (d->d_expert / kQ)
+                      : d->mode == MOE_MODE_MXFP8 ? L->n_pad_cap * (d->d_expert / 32)
+                                                  : 0);
     L->y = take(yb * N * d->d_hidden);
     L->zero = take(kZeroBytes);
     // F32ACT: x rounded to bf16 once, then the bf16 GEMMs run on it
@@ -78,8 +81,8 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int occ1[3] = {0, 0, 0};
-    int occ2[3] = {0, 0, 0};
+    int occ1[4] = {0, 0, 0, 0};
+    int occ2[4] = {0, 0, 0, 0};
 };
 std::mutex g_mu;
 DeviceInfo g_dev[64];
@@ -94,7 +97,7 @@ hipError_t device_info(int mode, int* cus, int* occ1, int* occ2) {
     if (!di.ready) {
         err = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        for (int m = 0; m < 3; ++m) {
+        for (int m = 0; m < 4; ++m) {
             err = gemm_occupancy(m, &di.occ1[m], &di.occ2[m]);
             if (err != hipSuccess) return err;
             if (di.occ1[m] < 1) di.occ1[m] = 1;
@@ -187,7 +190,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!dims) return MOE_ERR_INVALID_ARG;
     if (!dims_ok(dims)) {
         // shape fields present but outside the envelope
-        if (dims->mode < 0 || dims->mode > 2 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
+        if (dims->mode < 0 || dims->mode > MOE_MODE_MXFP8 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
             dims->d_hidden <= 0 || dims->d_expert <= 0 ||
             (dims->weight_layout != MOE_WEIGHTS_ROW_MAJOR && dims->weight_layout != MOE_WEIGHTS_PACKED))
             return MOE_ERR_INVALID_ARG;
@@ -200,7 +203,10 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out) || !aligned16(topk_ids) ||
         !aligned16(topk_w))
         return MOE_ERR_INVALID_ARG;
-    if (mode == MOE_MODE_FP8 && (!scales || !scales->x_scale || !scales->w1_scale || !scales->w2_scale))
+    if (mode_fp8(mode) && (!scales || !scales->x_scale || !scales->w1_scale || !scales->w2_scale))
+        return MOE_ERR_INVALID_ARG;
+    // MXFP8 scale rows are loaded 4 bytes at a time
+    if (mode == MOE_MODE_MXFP8 && (((uintptr_t)scales->x_scale | (uintptr_t)scales->w1_scale | (uintptr_t)scales->w2_scale) & 3))
         return MOE_ERR_INVALID_ARG;
     moe_ws_layout L;
     layout_of(dims, &L);
@@ -250,15 +256,15 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
 
     Gemm1Args g1{};
     g1.x = xg;
-    g1.x_scale = mode == MOE_MODE_FP8 ? scales->x_scale : nullptr;
+    g1.x_scale = mode_fp8(mode) ? scales->x_scale : nullptr;
     g1.w1 = w1;
-    g1.w1_scale = mode == MOE_MODE_FP8 ? scales->w1_scale : nullptr;
+    g1.w1_scale = mode_fp8(mode) ? scales->w1_scale : nullptr;
     g1.row_src = r.row_src;
     g1.tasks = r.tasks1;
     g1.ctl = r.ctl;
     g1.zero = r.zero;
     g1.h = at<void>(workspace, L.h);
-    g1.h_scale = mode == MOE_MODE_FP8 ? at<float>(workspace, L.h_scale) : nullptr;
+    g1.h_scale = mode_fp8(mode) ? at<unsigned char>(workspace, L.h_scale) : nullptr;
     g1.topk_w = topk_w;
     g1.row_w = at<float>(workspace, L.row_w);
     g1.k = k;
@@ -271,7 +277,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.h = g1.h;
     g2.h_scale = g1.h_scale;
     g2.w2 = w2;
-    g2.w2_scale = mode == MOE_MODE_FP8 ? scales->w2_scale : nullptr;
+    g2.w2_scale = mode_fp8(mode) ? scales->w2_scale : nullptr;
     g2.row_src = r.row_src;
     g2.row_w = g1.row_w;
     g2.tasks = r.tasks2;
@@ -303,7 +309,7 @@ int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void*
     if (!dims_ok(&d)) return MOE_ERR_INVALID_ARG;
     if (!w1 || !w2 || !w1_packed || !w2_packed) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w1) || !aligned16(w2) || !aligned16(w1_packed) || !aligned16(w2_packed)) return MOE_ERR_INVALID_ARG;
-    const int64_t eb = d.mode == MOE_MODE_FP8 ? 1 : 2;
+    const int64_t eb = mode_fp8(d.mode) ? 1 : 2;
     const int64_t E = d.num_experts, d_h = d.d_hidden, d_e = d.d_expert;
     const int64_t b1 = E * 2 * d_e * d_h * eb, b2 = E * d_h * d_e * eb;
     auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {

@@ -38,6 +38,14 @@
 // accumulator with (row scale of x or h) * (block scale of W): the block
 // dequantisation happens in registers.  The row and block scales of each K
 // block ride in the same LDS stage as the operands.
+//
+// MXFP8 (E4M3 with one E8M0 scale per 32 values along K): the MFMA applies
+// the scales itself and accumulates straight into the accumulator with no
+// promotion.  Its operand layout (measured): lane group g = lane/16 holds K
+// [16g, 16g+16) in its first 16 bytes and K [64+16g, +16) in the last 16 (the
+// {g, g+4} chunks the FP8 path loads), and the lane (r, g) supplies the
+// E8M0 byte of row (or column) r for K values [32g, 32g+32), whichever lanes
+// hold them.  Each stage carries the 4 scale bytes of every A and B row.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -80,6 +88,12 @@ __device__ __forceinline__ void wait_vm_le(int n) { wait_vm_le_tree<0, 63>(n < 6
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
     // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0 (no MX scaling)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// scale_a / scale_b: E8M0 byte (low 8 bits) that lane (r, g) supplies for row
+// r of A / column r of B and K values [32g, 32g+32); format 0 = E4M3 for both
+__device__ __forceinline__ v4f mfma_mx(const v8i& a, const v8i& b, const v4f& c, int scale_a, int scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
 
 __device__ __forceinline__ v4f mfma_bf16(const v4i& a, const v4i& b, const v4f& c) {
@@ -153,12 +167,14 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ v4i lds16(const unsigned char* p) { return *reinterpret_cast<const v4i*>(p); }
 
-// the 32-byte K slice {chunk g, chunk g+4} of a swizzled 128-byte row
+// the 32-byte K slice {chunk g, chunk g+4} of a swizzled 128-byte row: the
+// K values lane group g of the 16x16x128 8-bit MFMA takes, in its order
 __device__ __forceinline__ v8i lds_frag32(const unsigned char* row, int g, int swz) {
     const v4i lo = lds16(row + ((g ^ swz) << 4));
     const v4i hi = lds16(row + (((g + 4) ^ swz) << 4));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
 
 // XCD of the calling wave (HW_REG_XCC_ID).  Only the task placement depends
 // on it; any value in [0, 8) is correct.
@@ -328,15 +344,18 @@ struct Sched {
 // fewer rows get more stages in flight.
 template <int MODE, bool GATED>
 struct Cfg {
-    static constexpr bool kFP8 = MODE == MOE_MODE_FP8;
+    static constexpr bool kBS = MODE == MOE_MODE_FP8;     // fp32 block scales, promoted per K block
+    static constexpr bool kMX = MODE == MOE_MODE_MXFP8;   // E8M0 scales per 32, applied by the MFMA
+    static constexpr bool kFP8 = kBS || kMX;              // one-byte e4m3 operands
     static constexpr int kNFW = (GATED && !kFP8) ? 1 : 2;  // 16-column fragments per wave
     static constexpr int kBN = 16 * kNFW * kGemmWaves;     // output columns per task
     static constexpr int kBRows = GATED ? 2 * kBN : kBN;   // weight rows per task
     static constexpr int kBAll = kBRows / 8;                            // B loads per stage (8 rows each)
     static constexpr int kBMax = (kBAll + kLoadWaves - 1) / kLoadWaves;  // per loading wave, at most
     static constexpr int kStageB = kBRows * kRowBytes;
-    // FP8: up to 128 row scales (waves 0 and 2), then the block scale(s) (wave 1)
-    static constexpr int kStageS = kFP8 ? 1024 : 0;
+    // FP8: up to 128 row scales (waves 0 and 2), then the block scale(s) (wave 1);
+    // MXFP8: the 4 scale bytes of this K block for every A row, then every B row
+    static constexpr int kStageS = kBS ? 1024 : kMX ? 4 * (kAMaxRows + kBRows) : 0;
     static constexpr int stage_bytes(int nsub) { return kStageB + 16 * nsub * kRowBytes + kStageS; }
     // ring: FP8 GEMM-1 (256 weight rows per stage) takes a whole CU's LDS
     // (three stages of a 128-row task, four of a 16-row one); the others take
@@ -364,13 +383,15 @@ struct Cfg {
 //     epilogue scales by topk_w[row_src[r]] and writes y[row_src[r]][cb*kBN ..].
 // K is the contraction length (d_h or d_e); N_out is d_e (GATED) or d_h.
 template <int MODE, bool GATED, int NSUB, int RING>
-__device__ __forceinline__ void gemm_task(const void* a_base, const float* a_scale, const int32_t* row_src,
-                                          int a_div, const void* wts, const float* w_scale, const unsigned char* zero,
+__device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scale_v, const int32_t* row_src,
+                                          int a_div, const void* wts, const void* w_scale_v, const unsigned char* zero,
                                           int e, int row0, int cb, int K, int N_out, bool packed,
                                           unsigned char* smem, const Gemm1Args* g1, const Gemm2Args* g2,
                                           Sched& sch, const int* rows, const float* roww, int par) {
     using C = Cfg<MODE, GATED>;
-    constexpr bool kFP8 = C::kFP8;
+    constexpr bool kFP8 = C::kFP8, kBS = C::kBS, kMX = C::kMX;
+    const float* a_scale = static_cast<const float*>(a_scale_v);  // FP8 mode
+    const float* w_scale = static_cast<const float*>(w_scale_v);
     constexpr int S = C::stages(NSUB, RING);
     static_assert(RING >= C::kRing, "ring smaller than this GEMM's");
     constexpr int kStage = C::stage_bytes(NSUB);
@@ -388,7 +409,10 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     const bool loader = w < kLoadWaves;
     const int n_b = loader ? (C::kBAll - 1 - w) / kLoadWaves + 1 : 0;
     const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / kLoadWaves + 1 : 0;
-    const int loads_per_stage = n_b + n_a + ((kFP8 && (w < 2 || (w == 2 && NSUB > 4))) ? 1 : 0);
+    int n_s = 0;
+    if constexpr (kBS) n_s = (w < 2 || (w == 2 && NSUB > 4)) ? 1 : 0;
+    if constexpr (kMX) n_s = w == 0 ? 2 : w == 1 ? (GATED ? 2 : 1) : w == 2 ? (NSUB > 4) + (GATED ? 1 : 0) : 0;
+    const int loads_per_stage = n_b + n_a + n_s;
 
     // ---- per-lane load sources (stage 0); a K block advances the A sources by
     // 128 bytes and the B sources by b_step: 128 bytes in row-major weights,
@@ -440,7 +464,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
     // -> row 64 + r; wave 1 lane 0 (and 1) -> block scale(s) of W for this K block
     const float* ssrc = nullptr;
     bool son = false, spad = false;
-    if constexpr (kFP8) {
+    if constexpr (kBS) {
         const int kq = K / kQ;
         const int srow = (w == 2 ? 64 : 0) + lane;
         if ((w == 0 || w == 2) && srow < 16 * NSUB) {
@@ -459,6 +483,54 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             const int64_t nrb = GATED ? 2 * (int64_t)N_out / kQ : (int64_t)N_out / kQ;
             const int64_t brow = GATED ? (lane == 0 ? cb : N_out / kQ + cb) : (int64_t)cb;
             ssrc = w_scale + ((int64_t)e * nrb + brow) * kq;
+        }
+    }
+    // MXFP8 scale sources: lane l of a slot reads the 4 bytes (K block kc's
+    // four E8M0 scales) of one row, rows stored [rows][K/32]:
+    //   wave 0: A rows 0..63 and B rows 0..63; wave 1: B rows 64..127 (and
+    //   128..191 in GEMM-1); wave 2: A rows 64..127 (more than 4 row blocks)
+    //   and, in GEMM-1, B rows 192..255.  LDS: A row r at 4*r, B row r at
+    //   4*(128 + r); mdst is the wave's base (lane l writes mdst + 4*l).
+    const unsigned char* msrc[2] = {zero, zero};
+    bool mon[2] = {false, false}, mfix[2] = {true, true};  // mfix: padding row, source not advanced
+    unsigned mdst[2] = {0u, 0u};
+    if constexpr (kMX) {
+        const unsigned char* as8 = static_cast<const unsigned char*>(a_scale_v);
+        const unsigned char* ws8 = static_cast<const unsigned char*>(w_scale_v);
+        const int64_t kq = K / 32;  // scale bytes per row
+        auto a_row = [&](int slot, int r) {
+            mon[slot] = true;
+            mdst[slot] = 4u * (r - lane);
+            if (r >= 16 * NSUB) return;  // past the task's rows: zeros, never read
+            if constexpr (GATED) {
+                const int p = rows[r];
+                if (p < 0) return;  // padding row: zero codes, zero scale bytes
+                msrc[slot] = as8 + (int64_t)(p / a_div) * kq;
+            } else {
+                msrc[slot] = as8 + (int64_t)(row0 + r) * kq;
+            }
+            mfix[slot] = false;
+        };
+        auto b_row = [&](int slot, int r) {
+            mon[slot] = true;
+            mdst[slot] = 4u * (kAMaxRows + r - lane);
+            int64_t wrow;
+            if constexpr (GATED)
+                wrow = r < C::kBN ? (int64_t)cb * C::kBN + r : (int64_t)N_out + (int64_t)cb * C::kBN + (r - C::kBN);
+            else
+                wrow = (int64_t)cb * C::kBN + r;
+            msrc[slot] = ws8 + ((int64_t)e * (GATED ? 2 : 1) * N_out + wrow) * kq;
+            mfix[slot] = false;
+        };
+        if (w == 0) {
+            a_row(0, lane);
+            b_row(1, lane);
+        } else if (w == 1) {
+            b_row(0, 64 + lane);
+            if (GATED) b_row(1, 128 + lane);
+        } else if (w == 2) {
+            if (NSUB > 4) a_row(0, 64 + lane);
+            if (GATED) b_row(NSUB > 4 ? 1 : 0, 192 + lane);
         }
     }
 
@@ -493,10 +565,16 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             const int ai = w + kLoadWaves * j;
             if (ai < kAInstr) g2l16(apad[j] ? asrc[j] : asrc[j] + koff, st + (unsigned)(C::kStageB + ai * 1024));
         }
-        if constexpr (kFP8) {
+        if constexpr (kBS) {
             // wave 0 reads the row scales, wave 1 the weights' block scales
             const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
             if (son) g2l4(spad ? ssrc : ssrc + kc, ss + (unsigned)(w == 1 ? 512 : w * 128));
+        }
+        if constexpr (kMX) {
+            const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                if (mon[m]) g2l4(mfix[m] ? msrc[m] : msrc[m] + 4 * kc, ss + mdst[m]);
         }
     };
 
@@ -532,7 +610,35 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
         const unsigned char* st = smem + (kc % S) * kStage;
         const unsigned char* sb = st;
         const unsigned char* sa = st + C::kStageB;
-        if constexpr (kFP8) {
+        if constexpr (kMX) {
+            // lane (lr, lg): chunks lg and lg + 4 of row lr of each fragment, and
+            // the scale byte of row lr for K values [32 lg, 32 lg + 32) (row r's
+            // four bytes at 4 r + 0..3)
+            const unsigned char* sc = st + C::kStageB + kStageA;
+            v8i A[NSUB];
+            int sxa[NSUB];
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                A[s] = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
+                sxa[s] = sc[4 * (16 * s + lr) + lg];
+            }
+            const unsigned char* scb = sc + 4 * kAMaxRows;
+#pragma unroll
+            for (int f = 0; f < C::kNFW; ++f) {
+                const int brow = 16 * (C::kNFW * w + f) + lr;
+                const v8i Bg = lds_frag32(sb + brow * kRowBytes, lg, swz);
+                const int sbg = scb[4 * brow + lg];
+#pragma unroll
+                for (int s = 0; s < NSUB; ++s) acc[s][f][0] = mfma_mx(A[s], Bg, acc[s][f][0], sxa[s], sbg);
+                if constexpr (GATED) {
+                    const v8i Bu = lds_frag32(sb + (C::kBN + brow) * kRowBytes, lg, swz);
+                    const int sbu = scb[4 * (C::kBN + brow) + lg];
+#pragma unroll
+                    for (int s = 0; s < NSUB; ++s)
+                        acc[s][f][GATED ? 1 : 0] = mfma_mx(A[s], Bu, acc[s][f][GATED ? 1 : 0], sxa[s], sbu);
+                }
+            }
+        } else if constexpr (kBS) {
             const float* sc = reinterpret_cast<const float*>(st + C::kStageB + kStageA);
             v8i A[NSUB];
 #pragma unroll
@@ -608,7 +714,34 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
             for (int f = 0; f < C::kNFW; ++f)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) hv[s][f][i] = silu_mul(acc[s][f][0][i], acc[s][f][1][i]);
-        if constexpr (kFP8) {
+        if constexpr (kMX) {
+            // per-row-per-32 requantisation: this wave's two fragments are
+            // columns [32 w, 32 w + 32) of the task, one MX block.  Shared
+            // exponent: floor(log2 amax) - 8 (the e4m3 maximum is 1.75 * 2^8),
+            // stored biased by 127 and clamped to [0, 254]; an all-zero block
+            // stores 127.  Elements: v * 2^-exponent, saturated to +-448.
+            uint8_t* hs = static_cast<uint8_t*>(g1->h_scale);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int rr = 16 * s + 4 * lg + i;
+                    float m = 0.f;
+#pragma unroll
+                    for (int f = 0; f < C::kNFW; ++f) m = fmaxf(m, fabsf(hv[s][f][i]));
+                    m = row16_max(m);
+                    // frexp: m = f * 2^x with f in [0.5, 1), so floor(log2 m) = x - 1
+                    int b = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 1 - 8 + 127 : 127;
+                    b = b < 0 ? 0 : (b > 254 ? 254 : b);
+#pragma unroll
+                    for (int f = 0; f < C::kNFW; ++f) {
+                        float v = __builtin_amdgcn_ldexpf(hv[s][f][i], 127 - b);
+                        v = fminf(fmaxf(v, -448.0f), 448.0f);
+                        stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] = (unsigned char)f32_to_e4m3(v);
+                    }
+                    if (lr == 0) hs[(int64_t)(row0 + rr) * (N_out / 32) + cb * kGemmWaves + w] = (uint8_t)b;
+                }
+        } else if constexpr (kBS) {
             // per-row-per-128 requantisation: amax over the task's 128 columns
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
@@ -637,7 +770,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const float* a_sca
                     for (int f = 0; f < C::kNFW; ++f)
                         stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] =
                             (unsigned char)f32_to_e4m3(hv[s][f][i] * inv);
-                    if (w == 0 && lr == 0) g1->h_scale[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
+                    if (w == 0 && lr == 0) static_cast<float*>(g1->h_scale)[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
                 }
         } else {
 #pragma unroll
@@ -881,7 +1014,9 @@ hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t
 }
 
 hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    if (mode == MOE_MODE_FP8)
+    if (mode == MOE_MODE_MXFP8)
+        hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_MXFP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
+    else if (mode == MOE_MODE_FP8)
         hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else
         hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
@@ -889,7 +1024,9 @@ hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, h
 }
 
 hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    if (mode == MOE_MODE_FP8)
+    if (mode == MOE_MODE_MXFP8)
+        hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_MXFP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
+    else if (mode == MOE_MODE_FP8)
         hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_BF16)
         hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_BF16>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
@@ -911,7 +1048,10 @@ hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEven
 
 hipError_t gemm_occupancy(int mode, int* g1, int* g2) {
     hipError_t e1, e2;
-    if (mode == MOE_MODE_FP8) {
+    if (mode == MOE_MODE_MXFP8) {
+        e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
+        e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
+    } else if (mode == MOE_MODE_FP8) {
         e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
     } else if (mode == MOE_MODE_BF16) {

@@ -66,7 +66,8 @@ __host__ __device__ inline int static_tasks(int grid, int x, int seg_len) {
 // a whole 128-column requantisation group of the intermediate and a single
 // block row of W1's scales; bf16 GEMM-1 uses 64; GEMM-2 uses 128 (one W2
 // scale block row).
-inline int gemm1_block_n(int mode) { return mode == MOE_MODE_FP8 ? 128 : 64; }
+inline bool mode_fp8(int mode) { return mode == MOE_MODE_FP8 || mode == MOE_MODE_MXFP8; }  // e4m3 operands
+inline int gemm1_block_n(int mode) { return mode_fp8(mode) ? 128 : 64; }
 inline int gemm2_block_n(int) { return 128; }
 
 struct RouteArgs {
@@ -85,15 +86,15 @@ struct RouteArgs {
 
 struct Gemm1Args {
     const void* x;  // e4m3 codes or bf16 [T, d_h]
-    const float* x_scale;
+    const void* x_scale;  // FP8: fp32 [T, d_h/128]; MXFP8: E8M0 bytes [T, d_h/32]
     const void* w1;
-    const float* w1_scale;
+    const void* w1_scale;  // FP8: fp32 128x128 block scales; MXFP8: E8M0 bytes per row per 32
     const int32_t* row_src;
     const int4* tasks;
     int32_t* ctl;
     const unsigned char* zero;
     void* h;
-    float* h_scale;
+    void* h_scale;  // FP8: fp32 [n_pad, d_e/128]; MXFP8: E8M0 bytes [n_pad, d_e/32]
     const float* topk_w;  // [T*k] routing weights
     float* row_w;         // [n_pad] routing weight of each padded row (0 on padding), written by column block 0
     int32_t k, d_h, d_e;
@@ -102,9 +103,9 @@ struct Gemm1Args {
 
 struct Gemm2Args {
     const void* h;
-    const float* h_scale;
+    const void* h_scale;
     const void* w2;
-    const float* w2_scale;
+    const void* w2_scale;
     const int32_t* row_src;
     const float* row_w;  // from GEMM-1
     const int4* tasks;

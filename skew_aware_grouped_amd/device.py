@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import moe
-from .workloads import MODE_BF16, MODE_F32ACT, MODE_FP8, MoEWorkload
+from .workloads import MODE_BF16, MODE_F32ACT, MODE_FP8, MODE_MXFP8, MoEWorkload
 
 
 def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
@@ -24,7 +24,7 @@ def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
         d["x"] = t(w.x.view(np.int16), torch.bfloat16)
     else:
         d["x"] = t(w.x, torch.float8_e4m3fn)
-    if w.mode == MODE_FP8:
+    if w.mode in (MODE_FP8, MODE_MXFP8):  # fp32 block scales or uint8 E8M0 scales
         d["w1"] = t(w.w1, torch.float8_e4m3fn)
         d["w2"] = t(w.w2, torch.float8_e4m3fn)
         d["x_scale"] = t(w.x_scale)

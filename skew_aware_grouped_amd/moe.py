@@ -26,6 +26,7 @@ MOE_ERR_HIP = 4
 MOE_MODE_F32ACT = 0
 MOE_MODE_BF16 = 1
 MOE_MODE_FP8 = 2
+MOE_MODE_MXFP8 = 3
 
 MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_PACKED = 1
@@ -163,10 +164,11 @@ def _stream_ptr(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _mode_of(x, w1):
+def _mode_of(x, w1, x_scale=None):
+    """e4m3 weights: MXFP8 when the scales are E8M0 bytes (uint8), else FP8."""
     import torch
     if w1.dtype in (torch.float8_e4m3fn, torch.uint8):
-        return MOE_MODE_FP8
+        return MOE_MODE_MXFP8 if x_scale is not None and x_scale.dtype == torch.uint8 else MOE_MODE_FP8
     if x.dtype == torch.float32:
         return MOE_MODE_F32ACT
     return MOE_MODE_BF16
@@ -187,11 +189,12 @@ def workspace_for(dims: moe_dims, device):
     return ws
 
 
-def make_dims(x, topk_ids, w1, mode: Optional[int] = None, weight_layout: int = MOE_WEIGHTS_ROW_MAJOR) -> moe_dims:
+def make_dims(x, topk_ids, w1, mode: Optional[int] = None, weight_layout: int = MOE_WEIGHTS_ROW_MAJOR,
+              x_scale=None) -> moe_dims:
     T, d_h = x.shape
     E, two_de, d_h2 = w1.shape
     assert d_h2 == d_h and two_de % 2 == 0, "w1 must be [E, 2*d_expert, d_hidden]"
-    return moe_dims(mode=_mode_of(x, w1) if mode is None else mode, num_tokens=T, num_experts=E,
+    return moe_dims(mode=_mode_of(x, w1, x_scale) if mode is None else mode, num_tokens=T, num_experts=E,
                     top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2, weight_layout=weight_layout)
 
 
@@ -220,9 +223,11 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     """Run ``moe_fused_forward`` on torch device tensors; returns ``out``.  With
     ``events`` (8 torch.cuda.Event objects: start and end of the routing, GEMM-1,
     GEMM-2 and combine kernels) the kernel-timing variant is used.  With
-    ``weight_layout=MOE_WEIGHTS_PACKED``, w1 and w2 are ``pack_weights`` outputs."""
+    ``weight_layout=MOE_WEIGHTS_PACKED``, w1 and w2 are ``pack_weights`` outputs.
+    e4m3 weights take fp32 block scales (FP8 mode) or uint8 E8M0 scales per 32
+    values (MXFP8 mode); the dtype of ``x_scale`` selects the mode."""
     import torch
-    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout)
+    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout, x_scale=x_scale)
     if out is None:
         odt = torch.float32 if dims.mode == MOE_MODE_F32ACT else torch.bfloat16
         out = torch.empty(x.shape[0], x.shape[1], dtype=odt, device=x.device)
@@ -232,7 +237,11 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     if topk_ids.dtype != torch.int32 or topk_w.dtype != torch.float32:
         raise ValueError("topk_ids must be int32 and topk_w float32")
     scales = None
-    if dims.mode == MOE_MODE_FP8:
+    if dims.mode in (MOE_MODE_FP8, MOE_MODE_MXFP8):
+        sdt = torch.uint8 if dims.mode == MOE_MODE_MXFP8 else torch.float32
+        for name, t in (("x_scale", x_scale), ("w1_scale", w1_scale), ("w2_scale", w2_scale)):
+            if t is None or not (t.is_cuda and t.is_contiguous()) or t.dtype != sdt:
+                raise ValueError(f"{name} must be a contiguous {sdt} device tensor")
         scales = moe_scales(x_scale.data_ptr(), w1_scale.data_ptr(), w2_scale.data_ptr())
     ws = workspace if workspace is not None else workspace_for(dims, x.device)
     args = (dims, x.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w1.data_ptr(), w2.data_ptr(), scales,

@@ -29,7 +29,7 @@ def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048, layout=m
 
 
 def test_workspace_layout_is_disjoint_and_aligned():
-    for mode in (0, 1, 2):
+    for mode in (0, 1, 2, 3):
         d = _dims(mode=mode)
         L = moe.moe_workspace_layout(d)
         offs = [L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.row_w, L.tile_expert,
@@ -45,7 +45,8 @@ def test_invalid_dims_rejected():
     assert moe.moe_workspace_bytes(_dims(d_h=100)) == 0
     assert moe.moe_workspace_bytes(_dims(E=0)) == 0
     assert moe.moe_workspace_bytes(_dims(k=9)) == 0
-    assert moe.moe_workspace_bytes(_dims(mode=3)) == 0
+    assert moe.moe_workspace_bytes(_dims(mode=4)) == 0
+    assert moe.moe_workspace_bytes(_dims(mode=-1)) == 0
     assert moe.moe_workspace_bytes(_dims(layout=2)) == 0
     assert moe.moe_workspace_bytes(_dims(layout=moe.MOE_WEIGHTS_PACKED)) == moe.moe_workspace_bytes(_dims())
 
@@ -70,6 +71,10 @@ def test_forward_argument_errors_without_gpu():
     assert call(_dims(), x=None) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(), x=p + 4) == moe.MOE_ERR_INVALID_ARG  # misaligned
     assert call(_dims(), scales=None) == moe.MOE_ERR_INVALID_ARG  # FP8 needs scales
+    mx = _dims(mode=moe.MOE_MODE_MXFP8)
+    assert call(mx, scales=None) == moe.MOE_ERR_INVALID_ARG  # so does MXFP8
+    assert call(mx, scales=moe.moe_scales(p, p + 2, p)) == moe.MOE_ERR_INVALID_ARG  # E8M0 rows: 4-byte aligned
+    assert call(mx, scales=moe.moe_scales(p, p, 0)) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(), ws_bytes=16) == moe.MOE_ERR_WORKSPACE
     assert call(_dims(), workspace=None) == moe.MOE_ERR_WORKSPACE
     assert call(_dims(), workspace=p + 64) == moe.MOE_ERR_WORKSPACE  # workspace must be 256-aligned

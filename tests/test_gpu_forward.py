@@ -2,7 +2,7 @@
 the CPU oracle.
 
 Tolerance: norm-wise max relative error max|g - r| / max|r| over the compared
-rows, 1e-2 in the bf16 modes and 3e-2 in FP8 mode.  At full workload sizes
+rows, 1e-2 in the bf16 modes and 3e-2 in the FP8 and MXFP8 modes.  At full workload sizes
 the oracle computes a sample of token rows; the full output is then checked
 for properties that hold at any size (every row written, finite, bitwise
 identical across launches)."""
@@ -13,7 +13,8 @@ from skew_aware_grouped_amd import device, moe, workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {W.MODE_F32ACT: 1e-2, W.MODE_BF16: 1e-2, W.MODE_FP8: 3e-2}
+TOL = {W.MODE_F32ACT: 1e-2, W.MODE_BF16: 1e-2, W.MODE_FP8: 3e-2, W.MODE_MXFP8: 3e-2}
+FP8_MODES = (W.MODE_FP8, W.MODE_MXFP8)
 
 
 def normwise(got, ref):
@@ -47,7 +48,7 @@ def _check(w, oracle, rows=None, label="", packed=False):
     d = device.upload(w, packed=packed)
     odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
     out = torch.full((w.T, w.d_h), float("nan"), dtype=odt, device="cuda:0")  # sentinel: every row must be written
-    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], x_scale=d["x_scale"])
     ws = moe.workspace_for(dims, "cuda:0")
     device.run(d, out=out, workspace=ws)
     torch.cuda.synchronize()
@@ -63,7 +64,7 @@ def _check(w, oracle, rows=None, label="", packed=False):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
 def test_small_shapes_full_parity(oracle, mode, packed):
     """Several tiles in every direction with ragged expert groups."""
     w = W.custom(200, 8, 3, 384, 256, mode, seed=21)
@@ -76,14 +77,15 @@ def test_workload_full_parity(oracle, name):
     _check(w, oracle, label=name)
 
 
-@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_128", "ds_fp8_256", "ds_fp8_512", "ds_fp8_1024", "ds_fp8_8192"])
+@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_128", "ds_fp8_256", "ds_fp8_512", "ds_fp8_1024", "ds_fp8_8192",
+                                  "qwen_mxfp8", "ds_mxfp8_1024", "ds_mxfp8_8192"])
 def test_workload_sampled_parity(oracle, name):
     print(f"generating {name}", flush=True)
     w = W.config(name)
     _check(w, oracle, rows=_sample_rows(w), label=name)
 
 
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8])
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
 def test_determinism_two_launches_and_streams(mode):
     import torch
     w = W.custom(300, 16, 2, 512, 256, mode, seed=5, routing=("zipf", 1.2, 3))
@@ -111,7 +113,7 @@ EDGE_CASES = {
 
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("case", sorted(EDGE_CASES))
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8])
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
 def test_edge_cases(oracle, case, mode, packed):
     c = EDGE_CASES[case]
     rng = np.random.default_rng(9)
@@ -123,7 +125,7 @@ def test_edge_cases(oracle, case, mode, packed):
         ids[::3, 0] = -1
         ids[1::5, 1] = E + 3
         ids[7, :] = -2  # a token with no valid assignment -> zero row
-    w = W.custom(T, E, k, 256, 128 if mode != W.MODE_FP8 else 256, mode, seed=13, topk_ids=ids)
+    w = W.custom(T, E, k, 256, 256 if mode in FP8_MODES else 128, mode, seed=13, topk_ids=ids)
     _check(w, oracle, label=case, packed=packed)
 
 
@@ -143,7 +145,7 @@ def _packed_reference(wt, gated, bn):
     return w5[:, row, b, s ^ (r & 7)].reshape(-1)
 
 
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8])
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
 def test_pack_weights_is_the_stated_permutation(mode):
     """moe_pack_weights output, byte for byte, against the header's formula."""
     import torch
@@ -151,8 +153,8 @@ def test_pack_weights_is_the_stated_permutation(mode):
     d = device.upload(w)
     p1, p2 = moe.pack_weights(d["w1"], d["w2"])
     torch.cuda.synchronize()
-    L = moe.moe_workspace_layout(moe.make_dims(d["x"], d["topk_ids"], d["w1"]))
-    assert (L.block_n1, L.block_n2) == ((128, 128) if mode == W.MODE_FP8 else (64, 128))
+    L = moe.moe_workspace_layout(moe.make_dims(d["x"], d["topk_ids"], d["w1"], x_scale=d["x_scale"]))
+    assert (L.block_n1, L.block_n2) == ((128, 128) if mode in FP8_MODES else (64, 128))
 
     def raw(t):
         return t.view(torch.uint8).cpu().numpy().reshape(t.shape[0], t.shape[1], -1)
@@ -162,7 +164,8 @@ def test_pack_weights_is_the_stated_permutation(mode):
         assert np.array_equal(got.view(torch.uint8).cpu().numpy().reshape(-1), want)
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_bf16", "qwen_fp8", "ds_fp8_128", "ds_fp8_1024", "ds_fp8_8192"])
+@pytest.mark.parametrize("name", ["tiny", "qwen_bf16", "qwen_fp8", "ds_fp8_128", "ds_fp8_1024", "ds_fp8_8192",
+                                  "qwen_mxfp8", "ds_mxfp8_1024"])
 def test_packed_weights_bitwise_equal_row_major(name):
     """The packed layout changes where the GEMMs read each weight tile from,
     not what they compute: the output is bitwise the row-major one."""
@@ -174,6 +177,27 @@ def test_packed_weights_bitwise_equal_row_major(name):
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16) if a.dtype != torch.float32 else a.view(torch.int32),
                        b.view(torch.int16) if b.dtype != torch.float32 else b.view(torch.int32))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_mxfp8_scales_vary_across_k(oracle, packed):
+    """MXFP8 with scale bytes that differ by up to 2^7 between neighbouring
+    32-value blocks of K, for x, W1 and W2 alike (still valid MX inputs): the
+    output is right only if every 32-value slice of K meets its own scale in
+    both operands.  Shifts are kept small enough that no product under- or
+    overflows fp32."""
+    import dataclasses
+    w = W.custom(150, 6, 2, 512, 256, W.MODE_MXFP8, seed=31, routing=("zipf", 1.1, 2))
+    rng = np.random.default_rng(4)
+
+    def shifted(sc, lo, hi):
+        d = rng.integers(lo, hi + 1, size=sc.shape[-1])  # one shift per K block
+        d = d + rng.integers(-1, 2, size=sc.shape[:-1])[..., None]  # and a small one per row
+        return np.clip(sc.astype(np.int32) + d, 1, 254).astype(np.uint8)
+
+    w = dataclasses.replace(w, x_scale=shifted(w.x_scale, -4, 3), w1_scale=shifted(w.w1_scale, -3, 4),
+                            w2_scale=shifted(w.w2_scale, -4, 3))
+    _check(w, oracle, label="mx_scale_shifts", packed=packed)
 
 
 def test_empty_batch_is_noop():
@@ -193,7 +217,7 @@ def test_forward_routing_and_task_list(oracle, name):
     import torch
     w = W.config(name)
     d = device.upload(w)
-    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], x_scale=d["x_scale"])
     ws = moe.workspace_for(dims, "cuda:0")
     device.run(d, workspace=ws)
     torch.cuda.synchronize()
