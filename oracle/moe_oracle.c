@@ -39,6 +39,12 @@
  * scale.  The intermediate is requantised per row per 32 columns with the
  * shared exponent floor(log2(amax)) - 8 (8 = the largest E4M3 exponent) and
  * saturating round-to-nearest-even elements.
+ *
+ * Clamped activation (flag ORACLE_ACT_CLAMPED; the pages name the GPT-OSS
+ * variant of SwiGLU as an independent activation owner, PipeLink section 5.3,
+ * without defining it; the definition taken is the published GPT-OSS one):
+ * the gate is clamped above at 7, the up value to [-7, 7], and
+ *     h = gate * sigmoid(1.702 * gate) * (up + 1).
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +64,9 @@
 /* flags */
 #define ORACLE_MIRROR_H 1 /* round the intermediate where the method stores it */
 #define ORACLE_ACC64 2    /* evaluate in fp64 instead of fp32 */
+#define ORACLE_ACT_CLAMPED 4 /* clamped activation (GPT-OSS variant) in place of SwiGLU */
+#define ACT_LIMIT 7.0        /* clamp bound of the clamped activation */
+#define ACT_ALPHA 1.702f     /* sigmoid slope of the clamped activation (an fp32 constant) */
 
 #define QBLK 128 /* block-scale granularity along every dimension */
 #define MXBLK 32 /* MX block: values along the reduction dimension sharing one scale */
@@ -218,7 +227,8 @@ static int check_dims(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_
 }
 
 /* Expert FFN of one assignment: y = W2[e] . (silu(g) * u), g and u from
- * W1[e] rows [0,d_e) and [d_e,2 d_e).  Accumulations run in ascending index
+ * W1[e] rows [0,d_e) and [d_e,2 d_e) (with ORACLE_ACT_CLAMPED the clamped
+ * activation of g and u instead).  Accumulations run in ascending index
  * order.  a is scratch of d_e doubles, y receives d_h values. */
 static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void* x, const void* xs, int64_t t,
                        const void* w1, const void* w1s, const void* w2, const void* w2s, int64_t e, double* a,
@@ -232,9 +242,21 @@ static void expert_ffn(int mode, int flags, int64_t d_h, int64_t d_e, const void
             g = R(g + R(ld_w(mode, f64, w1, w1s, 2 * d_e, d_h, e, r, c) * xv, f64), f64);
             u = R(u + R(ld_w(mode, f64, w1, w1s, 2 * d_e, d_h, e, d_e + r, c) * xv, f64), f64);
         }
-        /* SiLU(g) = g / (1 + exp(-g)) */
-        sg = f64 ? g / (1.0 + exp(-g)) : R(g / R(1.0 + (double)expf((float)-g), 0), 0);
-        a[r] = R(sg * u, f64);
+        if (flags & ORACLE_ACT_CLAMPED) {
+            /* g <- min(g, 7), u <- clamp(u, -7, 7): exact; then
+             * g * sigmoid(alpha g) * (u + 1), sigmoid(z) = 1 / (1 + exp(-z)) */
+            double z;
+            if (g > ACT_LIMIT) g = ACT_LIMIT;
+            if (u > ACT_LIMIT) u = ACT_LIMIT;
+            if (u < -ACT_LIMIT) u = -ACT_LIMIT;
+            z = R((double)ACT_ALPHA * g, f64);
+            sg = f64 ? g / (1.0 + exp(-z)) : R(g * R(1.0 / R(1.0 + (double)expf((float)-z), 0), 0), 0);
+            a[r] = R(sg * R(u + 1.0, f64), f64);
+        } else {
+            /* SiLU(g) = g / (1 + exp(-g)) */
+            sg = f64 ? g / (1.0 + exp(-g)) : R(g / R(1.0 + (double)expf((float)-g), 0), 0);
+            a[r] = R(sg * u, f64);
+        }
     }
     if (flags & ORACLE_MIRROR_H) {
         if (mode == ORACLE_MODE_FP8) {

@@ -25,6 +25,8 @@ MODE_FP8 = 2
 MODE_MXFP8 = 3
 MIRROR_H = 1
 ACC64 = 2
+ACT_CLAMPED = 4  # clamped activation (GPT-OSS variant of SwiGLU)
+ACT_SWIGLU, ACT_SWIGLU_CLAMPED = 0, 1  # values of a workload's ``activation``
 
 _lib = None
 
@@ -196,6 +198,8 @@ def forward(inp, rows=None, mirror: bool = True, acc64: bool = False):
     w2 = c(inp.w2, wdt)
     w2s = c(inp.w2_scale, sdt)
     flags = (MIRROR_H if mirror else 0) | (ACC64 if acc64 else 0)
+    if getattr(inp, "activation", ACT_SWIGLU) == ACT_SWIGLU_CLAMPED:
+        flags |= ACT_CLAMPED
     rc = lib.moe_oracle_forward(mode, int(inp.T), int(inp.E), int(inp.k), int(inp.d_h), int(inp.d_e),
                                 _ptr(x), _ptr(xs), _ptr(ids), _ptr(tw), _ptr(w1), _ptr(w1s), _ptr(w2), _ptr(w2s),
                                 flags, _ptr(rows_arr), nrows, _ptr(acc), _ptr(out))

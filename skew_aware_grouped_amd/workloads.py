@@ -47,6 +47,8 @@ MODE_F32ACT = 0
 MODE_BF16 = 1
 MODE_FP8 = 2
 MODE_MXFP8 = 3
+ACT_SWIGLU = 0          # silu(gate) * up
+ACT_SWIGLU_CLAMPED = 1  # clamped gate/up, gate * sigmoid(1.702 gate) * (up + 1)
 QBLK = 128
 MXBLK = 32
 
@@ -70,6 +72,7 @@ class MoEWorkload:
     x_scale: Optional[np.ndarray] = None
     w1_scale: Optional[np.ndarray] = None
     w2_scale: Optional[np.ndarray] = None
+    activation: int = 0  # ACT_SWIGLU or ACT_SWIGLU_CLAMPED
     meta: dict = field(default_factory=dict)
 
     @property
@@ -243,7 +246,8 @@ def _weights(index, E, d_h, d_e, mode):
     return w1, w2, None, None
 
 
-def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) -> MoEWorkload:
+def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None, activation=0,
+                  x_gain=1.0) -> MoEWorkload:
     if mode in (MODE_FP8, MODE_MXFP8):
         assert d_h % QBLK == 0 and d_e % QBLK == 0
     ids = make_routing(index, T, E, k, routing) if topk_ids is None else np.asarray(topk_ids, np.int32)
@@ -251,6 +255,8 @@ def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) 
     ex = np.exp(lg - lg.max(axis=1, keepdims=True))
     tw = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
     xf = _rng(index, STREAM_X).standard_normal((T, d_h), dtype=np.float32)
+    if x_gain != 1.0:  # wider pre-activations (reach the clamp of the clamped activation)
+        xf = xf * np.float32(x_gain)
     w1, w2, w1_scale, w2_scale = _weights(index, E, d_h, d_e, mode)
     x_scale = None
     if mode == MODE_FP8:
@@ -261,7 +267,7 @@ def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None) 
         x = xf if mode == MODE_F32ACT else to_bf16_bits(xf)
     return MoEWorkload(name=name, mode=mode, T=T, E=E, k=k, d_h=d_h, d_e=d_e, x=x, topk_ids=ids, topk_w=tw,
                        w1=w1, w2=w2, x_scale=x_scale, w1_scale=w1_scale, w2_scale=w2_scale,
-                       meta={"index": index, "routing": routing})
+                       activation=activation, meta={"index": index, "routing": routing, "x_gain": x_gain})
 
 
 @functools.lru_cache(maxsize=2)
@@ -270,10 +276,12 @@ def config(name: str) -> MoEWorkload:
     return make_workload(name=name, **c)
 
 
-def custom(T, E, k, d_h, d_e, mode, seed=7, routing=("uniform",), topk_ids=None) -> MoEWorkload:
+def custom(T, E, k, d_h, d_e, mode, seed=7, routing=("uniform",), topk_ids=None, activation=0,
+           x_gain=1.0) -> MoEWorkload:
     """Any shape, for parity sweeps and edge cases (seed selects the streams)."""
-    return make_workload(name=f"custom_T{T}_E{E}_k{k}_{d_h}x{d_e}_m{mode}_s{seed}", index=seed, T=T, E=E, k=k,
-                         d_h=d_h, d_e=d_e, mode=mode, routing=routing, topk_ids=topk_ids)
+    return make_workload(name=f"custom_T{T}_E{E}_k{k}_{d_h}x{d_e}_m{mode}_s{seed}_a{activation}_g{x_gain}",
+                         index=seed, T=T, E=E, k=k, d_h=d_h, d_e=d_e, mode=mode, routing=routing,
+                         topk_ids=topk_ids, activation=activation, x_gain=x_gain)
 
 
 def flops(w: MoEWorkload) -> float:

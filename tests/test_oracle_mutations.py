@@ -2,7 +2,8 @@
 
 Each case edits one plausible mistake into a copy of the oracle's C source
 (dropped term, wrong sign, wrong index, transposed operand, broken rounding,
-broken stability, a wrong MX scale index, exponent or bias), builds it, and runs the CPU pin tests against it in a
+broken stability, a wrong MX scale index, exponent or bias, a dropped clamp,
+term or slope of the clamped activation), builds it, and runs the CPU pin tests against it in a
 subprocess; the run must fail.  The product path is not involved.
 """
 import os
@@ -31,9 +32,14 @@ MUTATIONS = {
     "mx_w_scale_row_ignored": ("[(e * rows + r) * (cols / MXBLK) + c / MXBLK]", "[(e * rows) * (cols / MXBLK) + c / MXBLK]"),
     "mx_shared_exponent_off_by_one": ("b = ex - 1 - 8 + 127;", "b = ex - 8 + 127;"),
     "e8m0_bias_128": ("ldexp(1.0, (int)s - 127)", "ldexp(1.0, (int)s - 128)"),
+    "act_gate_clamp_dropped": ("if (g > ACT_LIMIT) g = ACT_LIMIT;", ""),
+    "act_up_lower_clamp_dropped": ("if (u < -ACT_LIMIT) u = -ACT_LIMIT;", ""),
+    "act_plus_one_dropped": ("R(u + 1.0, f64)", "u"),
+    "act_alpha_one": ("R((double)ACT_ALPHA * g, f64)", "g"),
 }
 
-PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_routing.py", "tests/test_oracle_forward.py"]
+PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_routing.py", "tests/test_oracle_forward.py",
+             "tests/test_oracle_activation.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
