@@ -12,6 +12,9 @@
  * the pages name as a variant of the Mixture-of-Kittens MoE kernels (PipeLink,
  * section 5.3) without defining it, is taken as the OCP Microscaling format:
  * E4M3FN values with one E8M0 scale per 32 consecutive values along K.
+ * The clamped activation (moe_dims.activation) is the GPT-OSS variant of
+ * SwiGLU, which the same page names as an independent activation owner; its
+ * published definition is taken.
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers (HIP global memory) of the current
@@ -71,10 +74,18 @@ extern "C" {
 #define MOE_WEIGHTS_ROW_MAJOR 0
 #define MOE_WEIGHTS_PACKED 1
 
+/* Activation of GEMM-1's gate and up values g, u (moe_dims.activation), taken
+ * on the fp32 accumulators:
+ *  MOE_ACT_SWIGLU          h = silu(g) * u
+ *  MOE_ACT_SWIGLU_CLAMPED  g' = min(g, 7), u' = clamp(u, -7, 7),
+ *                          h = g' * sigmoid(1.702 * g') * (u' + 1) */
+#define MOE_ACT_SWIGLU 0
+#define MOE_ACT_SWIGLU_CLAMPED 1
+
 /* Layer shape.  Supported envelope: 0 <= num_tokens, 1 <= num_experts <= 256,
  * 1 <= top_k <= 8, num_tokens*top_k < 2^31, d_hidden and d_expert positive
- * multiples of 128.  Zero-initialising weight_layout selects row-major
- * weights. */
+ * multiples of 128.  Zero-initialising weight_layout and activation selects
+ * row-major weights and SwiGLU. */
 typedef struct {
     int32_t mode;          /* MOE_MODE_* */
     int32_t num_tokens;    /* T */
@@ -83,6 +94,7 @@ typedef struct {
     int32_t d_hidden;      /* d_h */
     int32_t d_expert;      /* d_e */
     int32_t weight_layout; /* MOE_WEIGHTS_* */
+    int32_t activation;    /* MOE_ACT_* */
 } moe_dims;
 
 /* Scales of the quantised modes (dequantised value = code * scale).  Required
@@ -110,7 +122,7 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
 /*
  * Fused MoE forward:
  *   out[t] = sum_{j<k} topk_w[t,j] * W2[e] . ( silu(W1[e][0:d_e] . x[t]) * (W1[e][d_e:2d_e] . x[t]) ),
- *   e = topk_ids[t,j].
+ *   e = topk_ids[t,j]  (or the clamped activation in place of silu(g) * u).
  *
  *  x         [T, d_h]            fp32 / bf16 / e4m3 per mode
  *  topk_ids  [T, k] int32        expert of each assignment p = t*k + j; ids

@@ -21,6 +21,7 @@ bool dims_ok(const moe_dims* d) {
     if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return false;
     if (d->d_hidden < 128 || d->d_hidden % 128 || d->d_expert < 128 || d->d_expert % 128) return false;
     if (d->weight_layout != MOE_WEIGHTS_ROW_MAJOR && d->weight_layout != MOE_WEIGHTS_PACKED) return false;
+    if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_CLAMPED) return false;
     return true;
 }
 
@@ -192,7 +193,8 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
         // shape fields present but outside the envelope
         if (dims->mode < 0 || dims->mode > MOE_MODE_MXFP8 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
             dims->d_hidden <= 0 || dims->d_expert <= 0 ||
-            (dims->weight_layout != MOE_WEIGHTS_ROW_MAJOR && dims->weight_layout != MOE_WEIGHTS_PACKED))
+            (dims->weight_layout != MOE_WEIGHTS_ROW_MAJOR && dims->weight_layout != MOE_WEIGHTS_PACKED) ||
+            (dims->activation != MOE_ACT_SWIGLU && dims->activation != MOE_ACT_SWIGLU_CLAMPED))
             return MOE_ERR_INVALID_ARG;
         return MOE_ERR_UNSUPPORTED;
     }
@@ -271,6 +273,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.d_h = d_h;
     g1.d_e = d_e;
     g1.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
+    g1.act = dims->activation;
     if (launch_gemm1(mode, g1, grid1, s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
 
     Gemm2Args g2{};

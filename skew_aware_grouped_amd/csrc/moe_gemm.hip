@@ -120,6 +120,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
     return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// clamped variant: g' = min(g, 7), u' = clamp(u, -7, 7),
+// g' * sigmoid(1.702 g') * (u' + 1), with the same reciprocal
+__device__ __forceinline__ float clamped_act(float g, float u) {
+    g = fminf(g, 7.0f);
+    u = fminf(fmaxf(u, -7.0f), 7.0f);
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * g)) * (u + 1.0f);
+}
+
 // lane permutation within rows of 16 lanes (DPP; every lane reads a lane of
 // its own row, so no bound control is needed)
 template <int CTRL>
@@ -708,12 +716,21 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
     if constexpr (GATED) {
         if (w_owner) g1->row_w[row0 + w_row] = ep_w;
         float hv[NSUB][C::kNFW][4];
+        if (g1->act == MOE_ACT_SWIGLU_CLAMPED) {
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s)
+            for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-            for (int f = 0; f < C::kNFW; ++f)
+                for (int f = 0; f < C::kNFW; ++f)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) hv[s][f][i] = silu_mul(acc[s][f][0][i], acc[s][f][1][i]);
+                    for (int i = 0; i < 4; ++i) hv[s][f][i] = clamped_act(acc[s][f][0][i], acc[s][f][1][i]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+                for (int f = 0; f < C::kNFW; ++f)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) hv[s][f][i] = silu_mul(acc[s][f][0][i], acc[s][f][1][i]);
+        }
         if constexpr (kMX) {
             // per-row-per-32 requantisation: this wave's two fragments are
             // columns [32 w, 32 w + 32) of the task, one MX block.  Shared

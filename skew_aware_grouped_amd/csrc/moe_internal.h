@@ -99,6 +99,7 @@ struct Gemm1Args {
     float* row_w;         // [n_pad] routing weight of each padded row (0 on padding), written by column block 0
     int32_t k, d_h, d_e;
     int32_t packed;  // W1 in the packed tile order
+    int32_t act;     // MOE_ACT_*
 };
 
 struct Gemm2Args {

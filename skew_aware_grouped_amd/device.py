@@ -37,6 +37,7 @@ def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
     d["topk_ids"] = t(w.topk_ids.astype(np.int32))
     d["topk_w"] = t(w.topk_w.astype(np.float32))
     d["weight_layout"] = moe.MOE_WEIGHTS_ROW_MAJOR
+    d["activation"] = int(w.activation)
     if packed:
         d["w1"], d["w2"] = moe.pack_weights(d["w1"], d["w2"])
         d["weight_layout"] = moe.MOE_WEIGHTS_PACKED
@@ -46,7 +47,8 @@ def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
 def run(d: dict, out=None, workspace=None, stream=None, events=None):
     return moe.fused_forward(d["x"], d["topk_ids"], d["topk_w"], d["w1"], d["w2"], out=out, x_scale=d["x_scale"],
                              w1_scale=d["w1_scale"], w2_scale=d["w2_scale"], workspace=workspace, stream=stream,
-                             events=events, weight_layout=d.get("weight_layout", moe.MOE_WEIGHTS_ROW_MAJOR))
+                             events=events, weight_layout=d.get("weight_layout", moe.MOE_WEIGHTS_ROW_MAJOR),
+                             activation=d.get("activation", moe.MOE_ACT_SWIGLU))
 
 
 def out_to_f64(out) -> np.ndarray:

@@ -31,11 +31,14 @@ MOE_MODE_MXFP8 = 3
 MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_PACKED = 1
 
+MOE_ACT_SWIGLU = 0
+MOE_ACT_SWIGLU_CLAMPED = 1
+
 
 class moe_dims(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_expert", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("activation", ctypes.c_int32)]
 
 
 class moe_scales(ctypes.Structure):
@@ -190,12 +193,13 @@ def workspace_for(dims: moe_dims, device):
 
 
 def make_dims(x, topk_ids, w1, mode: Optional[int] = None, weight_layout: int = MOE_WEIGHTS_ROW_MAJOR,
-              x_scale=None) -> moe_dims:
+              x_scale=None, activation: int = MOE_ACT_SWIGLU) -> moe_dims:
     T, d_h = x.shape
     E, two_de, d_h2 = w1.shape
     assert d_h2 == d_h and two_de % 2 == 0, "w1 must be [E, 2*d_expert, d_hidden]"
     return moe_dims(mode=_mode_of(x, w1, x_scale) if mode is None else mode, num_tokens=T, num_experts=E,
-                    top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2, weight_layout=weight_layout)
+                    top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2, weight_layout=weight_layout,
+                    activation=activation)
 
 
 def pack_weights(w1, w2, stream=None):
@@ -219,7 +223,8 @@ def pack_weights(w1, w2, stream=None):
 
 
 def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=None, w2_scale=None,
-                  workspace=None, stream=None, events=None, weight_layout=MOE_WEIGHTS_ROW_MAJOR):
+                  workspace=None, stream=None, events=None, weight_layout=MOE_WEIGHTS_ROW_MAJOR,
+                  activation=MOE_ACT_SWIGLU):
     """Run ``moe_fused_forward`` on torch device tensors; returns ``out``.  With
     ``events`` (8 torch.cuda.Event objects: start and end of the routing, GEMM-1,
     GEMM-2 and combine kernels) the kernel-timing variant is used.  With
@@ -227,7 +232,7 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     e4m3 weights take fp32 block scales (FP8 mode) or uint8 E8M0 scales per 32
     values (MXFP8 mode); the dtype of ``x_scale`` selects the mode."""
     import torch
-    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout, x_scale=x_scale)
+    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout, x_scale=x_scale, activation=activation)
     if out is None:
         odt = torch.float32 if dims.mode == MOE_MODE_F32ACT else torch.bfloat16
         out = torch.empty(x.shape[0], x.shape[1], dtype=odt, device=x.device)

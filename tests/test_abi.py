@@ -23,9 +23,10 @@ def test_block_m_and_caps():
     assert moe.moe_route_caps(1, 2, 32) == (2 + 2 * 15, 2)
 
 
-def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048, layout=moe.MOE_WEIGHTS_ROW_MAJOR):
+def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048, layout=moe.MOE_WEIGHTS_ROW_MAJOR,
+          act=moe.MOE_ACT_SWIGLU):
     return moe.moe_dims(mode=mode, num_tokens=T, num_experts=E, top_k=k, d_hidden=d_h, d_expert=d_e,
-                        weight_layout=layout)
+                        weight_layout=layout, activation=act)
 
 
 def test_workspace_layout_is_disjoint_and_aligned():
@@ -49,6 +50,8 @@ def test_invalid_dims_rejected():
     assert moe.moe_workspace_bytes(_dims(mode=-1)) == 0
     assert moe.moe_workspace_bytes(_dims(layout=2)) == 0
     assert moe.moe_workspace_bytes(_dims(layout=moe.MOE_WEIGHTS_PACKED)) == moe.moe_workspace_bytes(_dims())
+    assert moe.moe_workspace_bytes(_dims(act=2)) == 0
+    assert moe.moe_workspace_bytes(_dims(act=moe.MOE_ACT_SWIGLU_CLAMPED)) == moe.moe_workspace_bytes(_dims())
 
 
 def test_forward_argument_errors_without_gpu():
@@ -65,6 +68,7 @@ def test_forward_argument_errors_without_gpu():
     assert call(None) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(mode=5)) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(layout=7)) == moe.MOE_ERR_INVALID_ARG
+    assert call(_dims(act=-1)) == moe.MOE_ERR_INVALID_ARG
     assert call(_dims(d_h=100)) == moe.MOE_ERR_UNSUPPORTED
     assert call(_dims(E=300)) == moe.MOE_ERR_UNSUPPORTED
     assert call(_dims(T=0)) == moe.MOE_OK  # empty batch: nothing to do

@@ -57,7 +57,7 @@ def _check(w, oracle, rows=None, label="", packed=False):
     acc, _ = oracle.forward(w, rows=rows)
     gs = g if rows is None else g[rows]
     err = normwise(gs, acc)
-    print(f"{label} mode={w.mode} packed={packed} T={w.T} E={w.E} k={w.k} {w.d_h}x{w.d_e}: normwise err {err:.3e}",
+    print(f"{label} mode={w.mode} act={w.activation} packed={packed} T={w.T} E={w.E} k={w.k} {w.d_h}x{w.d_e}: normwise err {err:.3e}",
           flush=True)
     assert err <= TOL[w.mode], err
     return d, out, g
@@ -69,6 +69,22 @@ def test_small_shapes_full_parity(oracle, mode, packed):
     """Several tiles in every direction with ragged expert groups."""
     w = W.custom(200, 8, 3, 384, 256, mode, seed=21)
     _check(w, oracle, label="small", packed=packed)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+def test_clamped_activation_small_shapes(oracle, mode, packed):
+    """The clamped activation on widened inputs (x scaled by 4: about a tenth
+    of the gate and up values lie beyond the clamp), ragged expert groups."""
+    w = W.custom(200, 8, 3, 384, 256, mode, seed=22, activation=W.ACT_SWIGLU_CLAMPED, x_gain=4.0)
+    _check(w, oracle, label="clamped", packed=packed)
+
+
+@pytest.mark.parametrize("name", ["qwen_bf16", "ds_fp8_1024", "ds_mxfp8_1024"])
+def test_clamped_activation_sampled(oracle, name):
+    import dataclasses
+    w = dataclasses.replace(W.config(name), activation=W.ACT_SWIGLU_CLAMPED)
+    _check(w, oracle, rows=_sample_rows(w), label=name + "_clamped", packed=True)
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen_bf16"])
