@@ -20,7 +20,10 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hi
 # The GEMM kernels' queue atomics run on one lane and their results are read
 # much later; the compiler's wave-level atomic aggregation would read the
 # result right after the atomic, making the wave wait for it there.
-SOURCE_FLAGS = {"moe_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+# MFMA results go to VGPRs: the FP8 promotion reads them with VALU
+# instructions, and from AGPRs each read would cost an extra move.
+SOURCE_FLAGS = {"moe_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-mllvm",
+                                 "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def build(verbose: bool = False) -> str:

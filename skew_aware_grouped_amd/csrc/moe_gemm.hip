@@ -647,37 +647,58 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
                 }
             }
         } else if constexpr (kBS) {
+            // software-pipelined by one row block: the MFMAs of row block s
+            // are issued, and the LDS reads of row block s + 1 started, before
+            // the promotion of row block s - 1 reads its results, so neither
+            // an MFMA result nor an LDS read is waited for right after issue
             const float* sc = reinterpret_cast<const float*>(st + C::kStageB + kStageA);
-            v8i A[NSUB];
-#pragma unroll
-            for (int s = 0; s < NSUB; ++s) A[s] = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
-            float sx[NSUB][4];
-#pragma unroll
-            for (int s = 0; s < NSUB; ++s)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sx[s][i] = sc[16 * s + 4 * lg + i];
             const float swg = sc[128];  // written by lane 0 (and 1) of wave 1
             const float swu = GATED ? sc[129] : 0.f;
+            constexpr int kG = GATED ? 2 : 1;
+            constexpr int kT = C::kNFW * kG;  // MFMAs per row block
+            v8i Bf[C::kNFW][kG];
 #pragma unroll
             for (int f = 0; f < C::kNFW; ++f) {
                 const int brow = 16 * (C::kNFW * w + f) + lr;
-                const v8i Bg = lds_frag32(sb + brow * kRowBytes, lg, swz);
-#pragma unroll
-                for (int s = 0; s < NSUB; ++s) {
-                    const v4f t = mfma_fp8(A[s], Bg, zero4);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[s][f][0][i] += t[i] * (sx[s][i] * swg);
-                }
-                if constexpr (GATED) {
-                    const v8i Bu = lds_frag32(sb + (C::kBN + brow) * kRowBytes, lg, swz);
-#pragma unroll
-                    for (int s = 0; s < NSUB; ++s) {
-                        const v4f t = mfma_fp8(A[s], Bu, zero4);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[s][f][GATED ? 1 : 0][i] += t[i] * (sx[s][i] * swu);
-                    }
-                }
+                Bf[f][0] = lds_frag32(sb + brow * kRowBytes, lg, swz);
+                if constexpr (GATED) Bf[f][kG - 1] = lds_frag32(sb + (C::kBN + brow) * kRowBytes, lg, swz);
             }
+            v4f tp[kT];
+            float pp[kG][4];
+            auto promote = [&](int s) {
+#pragma unroll
+                for (int f = 0; f < C::kNFW; ++f)
+#pragma unroll
+                    for (int g = 0; g < kG; ++g)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[s][f][g][i] += tp[f * kG + g][i] * pp[g][i];
+            };
+            v8i A = lds_frag32(sa + lr * kRowBytes, lg, swz);
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                v4f tq[kT];
+#pragma unroll
+                for (int f = 0; f < C::kNFW; ++f)
+#pragma unroll
+                    for (int g = 0; g < kG; ++g) tq[f * kG + g] = mfma_fp8(A, Bf[f][g], zero4);
+                v8i An = A;
+                if (s + 1 < NSUB) An = lds_frag32(sa + (16 * (s + 1) + lr) * kRowBytes, lg, swz);
+                float sx[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sx[i] = sc[16 * s + 4 * lg + i];
+                __builtin_amdgcn_sched_barrier(0);
+                if (s > 0) promote(s - 1);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < kT; ++j) tp[j] = tq[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pp[0][i] = sx[i] * swg;
+                    if constexpr (GATED) pp[kG - 1][i] = sx[i] * swu;
+                }
+                A = An;
+            }
+            promote(NSUB - 1);
         } else {
             // two 16x16x32 bf16 MFMAs per K block: chunk g, then chunk g+4
 #pragma unroll
