@@ -792,22 +792,39 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
                     if (lr == 0) s_amax[w * kAMaxRows + 16 * s + 4 * lg + i] = m;
                 }
             lds_barrier();
+            // every partial amax of this lane's rows (rows 16 s + 4 lg + i,
+            // i = 0..3, are four consecutive floats per wave) is read before
+            // the first staging write, so the reads go out back to back and
+            // are waited for once
+            static_assert(C::kNFW == 2, "two 16-column fragments per wave");
+            float amax[NSUB][4];
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) {
+                float4 m = *reinterpret_cast<const float4*>(&s_amax[16 * s + 4 * lg]);
+#pragma unroll
+                for (int ww = 1; ww < kGemmWaves; ++ww) {
+                    const float4 o = *reinterpret_cast<const float4*>(&s_amax[ww * kAMaxRows + 16 * s + 4 * lg]);
+                    m = make_float4(fmaxf(m.x, o.x), fmaxf(m.y, o.y), fmaxf(m.z, o.z), fmaxf(m.w, o.w));
+                }
+                amax[s][0] = m.x;
+                amax[s][1] = m.y;
+                amax[s][2] = m.z;
+                amax[s][3] = m.w;
+            }
 #pragma unroll
             for (int s = 0; s < NSUB; ++s)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int rr = 16 * s + 4 * lg + i;
-                    float amax = s_amax[rr];
-#pragma unroll
-                    for (int ww = 1; ww < kGemmWaves; ++ww) amax = fmaxf(amax, s_amax[ww * kAMaxRows + rr]);
+                    const float am = amax[s][i];
                     // scale amax/448; values are multiplied by its reciprocal
                     // (|v| * 448/amax stays within rounding of 448, the e4m3 maximum)
-                    const float sc = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-                    const float inv = amax > 0.f ? 448.0f * __builtin_amdgcn_rcpf(amax) : 1.0f;
-#pragma unroll
-                    for (int f = 0; f < C::kNFW; ++f)
-                        stage[rr * C::kEpiRow + 16 * (C::kNFW * w + f) + lr] =
-                            (unsigned char)f32_to_e4m3(hv[s][f][i] * inv);
+                    const float sc = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
+                    const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
+                    // both fragments' codes from one converter instruction
+                    const unsigned q2 = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(hv[s][0][i] * inv, hv[s][1][i] * inv, 0, false);
+                    stage[rr * C::kEpiRow + 16 * (C::kNFW * w) + lr] = (unsigned char)(q2 & 0xffu);
+                    stage[rr * C::kEpiRow + 16 * (C::kNFW * w + 1) + lr] = (unsigned char)((q2 >> 8) & 0xffu);
                     if (w == 0 && lr == 0) static_cast<float*>(g1->h_scale)[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
                 }
         } else {
