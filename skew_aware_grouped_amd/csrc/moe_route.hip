@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ int s_poff[kMaxExperts + 1];
     __shared__ int s_wcnt[kRouteWaves][kMaxExperts];
     __shared__ int s_order[kMaxExperts];
+    __shared__ int s_rtiles[kMaxExperts];        // group blocks of the expert of each rank
     __shared__ int s_mt[2][kMaxExperts];         // M-tiles per expert rank, per list
     __shared__ int s_mtoff[2][kMaxExperts + 1];
     __shared__ int s_xpre[2][kXcds][kMaxExperts + 1];  // per list and XCD: tasks of lower ranks
@@ -226,18 +227,38 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // (rank r, column block cb) -- every M-tile of one weight block -- goes to
     // XCD (r*nb + cb) mod 8, so the M-tiles that read the same weights run
     // side by side on one L2; each XCD's segment of the list keeps rank order.
-    for (int e = tid; e < E; e += kRouteThreads) {
-        const int c = s_cnt[e];
-        int r = 0;
-        for (int e2 = 0; e2 < E; ++e2) {
-            const int c2 = s_cnt[e2];
-            r += (c2 > c) || (c2 == c && e2 < e);
+    {
+        // lane l of every wave holds the counts of experts l, l + 64, ...;
+        // wave w ranks experts w, w + 16, ...: the number of experts ranked
+        // before e is a popcount of ballots over the lanes, with no LDS
+        // round trip per comparison
+        constexpr int kJ = kMaxExperts / 64;
+        int cj[kJ];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) cj[j] = lane + 64 * j < E ? s_cnt[lane + 64 * j] : -1;
+        for (int e = wave; e < E; e += kRouteWaves) {
+            const int je = e >> 6;  // wave-uniform
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j)
+                if (j == je) c = __builtin_amdgcn_readlane(cj[j], e & 63);
+            int r = 0;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                if (64 * j >= E) break;
+                const int e2 = lane + 64 * j;
+                const bool before = e2 < E && ((cj[j] > c) || (cj[j] == c && e2 < e));
+                r += __popcll(__ballot(before));
+            }
+            if (lane == 0) {
+                s_order[r] = e;
+                s_rtiles[r] = s_tiles[e];
+            }
         }
-        s_order[r] = e;
     }
     // GEMM-1 M-tiles: kMaxRowBlocks1 blocks (fewer weight re-reads) when that
     // still leaves min_tasks1 tasks, otherwise kMaxRowBlocks2 (more tasks to
-    // spread over the CUs); the last wave decides while the others rank
+    // spread over the CUs); the last wave decides after its share of the ranking
     if (wave == kRouteWaves - 1) {
         int big = 0;
         for (int e = lane; e < E; e += 64) big += (s_tiles[e] + kMaxRowBlocks1 - 1) / kMaxRowBlocks1;
@@ -246,10 +267,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     __syncthreads();
     const int mb1 = s_mb1;
-    // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2)
+    // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2); the
+    // M-tile sizes are powers of two
+    static_assert(kMaxRowBlocks1 == 8 && kMaxRowBlocks2 == 4, "M-tile sizes 8 and 4 group blocks");
+    const int lg_mb1 = mb1 == kMaxRowBlocks1 ? 3 : 2;
     auto mtiles = [&](int list, int r) {
-        const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
-        return (s_tiles[s_order[r]] + mb - 1) / mb;
+        const int lg = list == 0 ? lg_mb1 : 2;
+        return (s_rtiles[r] + (1 << lg) - 1) >> lg;
     };
     {
         // waves 0..7: GEMM-1 list, XCD = wave; waves 8..15: GEMM-2 list
@@ -272,12 +296,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         s_seg[tid][kXcds] = run;
     }
     __syncthreads();
-    for (int list = 0; list < 2; ++list) {
-        const int nb = list == 0 ? a.nb1 : a.nb2;
-        const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
-        int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
-        const int total = s_mtoff[list][E] * nb;
-        for (int i = tid; i < total; i += kRouteThreads) {
+    {
+        // both lists in one pass over their concatenated task indices
+        const int total0 = s_mtoff[0][E] * a.nb1;
+        const int total = total0 + s_mtoff[1][E] * a.nb2;
+        for (int g = tid; g < total; g += kRouteThreads) {
+            const int list = g < total0 ? 0 : 1;
+            const int i = list == 0 ? g : g - total0;
+            const int nb = list == 0 ? a.nb1 : a.nb2;
+            const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
+            int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
             // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb), column-major
             const int r = upper_index(s_mtoff[list], E, i / nb);
             const int mt = s_mt[list][r];
@@ -287,7 +315,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             const int e = s_order[r];
             const int x = (r * nb + cb) & (kXcds - 1);
             const int q = (cb - first_cb_on(r, nb, x)) / kXcds;
-            const int nsub = min(mb, s_tiles[e] - m * mb);
+            const int nsub = min(mb, s_rtiles[r] - m * mb);
             tasks[s_seg[list][x] + s_xpre[list][x][r] + q * mt + m] =
                 make_int4(e, s_poff[e] + m * mb * kBlockM, nsub, cb);
         }

@@ -226,7 +226,7 @@ def test_empty_batch_is_noop():
     assert out.shape == (0, 256)
 
 
-@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024"])
+@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024", "qwen_bf16", "ds_mxfp8_1024"])
 def test_forward_routing_and_task_list(oracle, name):
     """The workspace after a forward call holds the oracle's routing metadata and
     task lists that cover every (group block, column block) pair exactly once."""
