@@ -977,22 +977,40 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < a.k; ++j) {
-        const int64_t p = (int64_t)t * a.k + j;
-        const int id = a.ids[p];
-        if ((unsigned)id >= (unsigned)a.E) continue;
-        if (F32) {
-            const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.y) + p * a.d_h + c);
-            const float4 u = src[0], v = src[1];
-            acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
-            acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
-        } else {
-            const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(a.y) + p * a.d_h + c);
-            const unsigned wd[4] = {u.x, u.y, u.z, u.w};
+    // slots in groups of up to 4: the ids and the y rows of a group are loaded
+    // together (one memory round trip, not two); a dropped slot's row holds
+    // no result and its values are discarded unread by the sum
+    for (int j0 = 0; j0 < a.k; j0 += 4) {
+        int id[4];
+        uint4 raw[4][F32 ? 2 : 1];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[2 * i] += __uint_as_float(wd[i] << 16);
-                acc[2 * i + 1] += __uint_as_float(wd[i] & 0xFFFF0000u);
+        for (int jj = 0; jj < 4; ++jj) {
+            const int64_t p = (int64_t)t * a.k + j0 + jj;
+            if (j0 + jj >= a.k) break;
+            id[jj] = a.ids[p];
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned char*>(a.y) +
+                                                              (p * a.d_h + c) * (F32 ? 4 : 2));
+            raw[jj][0] = src[0];
+            if (F32) raw[jj][F32 ? 1 : 0] = src[1];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            if (j0 + jj >= a.k) break;
+            if ((unsigned)id[jj] >= (unsigned)a.E) continue;
+            if (F32) {
+                const uint4 u = raw[jj][0], v = raw[jj][F32 ? 1 : 0];
+                acc[0] += __uint_as_float(u.x); acc[1] += __uint_as_float(u.y);
+                acc[2] += __uint_as_float(u.z); acc[3] += __uint_as_float(u.w);
+                acc[4] += __uint_as_float(v.x); acc[5] += __uint_as_float(v.y);
+                acc[6] += __uint_as_float(v.z); acc[7] += __uint_as_float(v.w);
+            } else {
+                const uint4 u = raw[jj][0];
+                const unsigned wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += __uint_as_float(wd[i] << 16);
+                    acc[2 * i + 1] += __uint_as_float(wd[i] & 0xFFFF0000u);
+                }
             }
         }
     }
