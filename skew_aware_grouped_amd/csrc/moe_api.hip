@@ -171,6 +171,7 @@ int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, const int3
     a.E = num_experts;
     route_caps(N, num_experts, &a.n_pad_cap, &a.tile_cap);
     a.nb1 = a.nb2 = 0;
+    a.full = 1;
     a.counts = out->counts;
     a.offsets = out->offsets;
     a.padded_offsets = out->padded_offsets;

@@ -77,6 +77,7 @@ struct RouteArgs {
     int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
     int32_t min_tasks1;  // GEMM-1 takes kMaxRowBlocks1-block M-tiles only if that leaves this many tasks
     int32_t grid1, grid2;  // workgroups of the GEMM kernels (their first tasks are assigned statically)
+    int32_t full;          // also write pos, ppos and sorted_p (the layer itself consumes row_src only)
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;
     int32_t* ctl;  // control block [kCtlWords]
     int4* tasks1;

@@ -10,13 +10,20 @@
 // One workgroup of 16 wave64s does everything: N = T*k is at most a few ten
 // thousand assignments on the paths this serves.  Each wave owns a contiguous
 // chunk of the assignments.  Up to kLdsIds ids are read from HBM once, into
-// LDS, and the scatter reads them there; larger N reads them twice.
+// LDS, and the scatter reads them there and builds row_src in LDS, which then
+// goes out with coalesced stores; larger N reads the ids twice and scatters
+// row_src straight to memory.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kLdsIds = 16384;
+// padded rows of kLdsIds assignments over up to kMaxExperts experts
+constexpr int kLdsRows = kLdsIds + kMaxExperts * (kBlockM - 1);
+// M-tiles per list that the rank-lookup table (kept in the ids' LDS once the
+// scatter is done) can hold
+constexpr int kRankTable = kLdsIds / 2;
 
 // v + (the value of lane - k in the same row of 16 lanes, 0 where that lane
 // is outside the row), or with row_bcast the last lane of the previous row(s)
@@ -85,7 +92,8 @@ __device__ __forceinline__ int cbs_on(int r, int nb, int x) {
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
-    __shared__ int s_ids[kLdsIds];
+    __shared__ short s_ids[kLdsIds];   // valid ids, -1 for the others; later the rank tables
+    __shared__ int s_rows[kLdsRows];    // row_src while it is built
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_tiles[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
@@ -105,6 +113,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int E = a.E;
     const int N = a.N;
     const bool in_lds = N <= kLdsIds;
+    // row_src is built in LDS when the ids are there and the scatter is large
+    // enough for its scattered stores to cost more than the extra pass
+    const bool stage_rows = in_lds && N > kRouteThreads;
 
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wcnt[i / E][i % E] = 0;
     if (tid == 0) s_dropped = 0;
@@ -124,7 +135,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     int my_drop = 0;
     for (int p = c_lo + lane; p < c_hi; p += 64) {
         const int id = a.ids[p];
-        if (in_lds) s_ids[p] = id;
+        if (in_lds) s_ids[p] = (unsigned)id < (unsigned)E ? (short)id : (short)-1;
         if ((unsigned)id < (unsigned)E)
             atomicAdd(&s_wcnt[wave][id], 1);
         else
@@ -159,27 +170,37 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         a.offsets[e] = s_off[e];
         a.padded_offsets[e] = s_poff[e];
     }
-    // padding rows of each group and the unused tail of the padded space
-    for (int e = wave; e < E; e += kRouteWaves)
-        for (int r = s_poff[e] + s_cnt[e] + lane; r < s_poff[e + 1]; r += 64) a.row_src[r] = -1;
+    // padding rows of each group (in LDS: every row, the scatter then fills
+    // the valid ones) and the unused tail of the padded space
+    if (stage_rows) {
+        for (int i = tid; i < n_pad; i += kRouteThreads) s_rows[i] = -1;
+        __syncthreads();
+    } else {
+        for (int e = wave; e < E; e += kRouteWaves)
+            for (int r = s_poff[e] + s_cnt[e] + lane; r < s_poff[e + 1]; r += 64) a.row_src[r] = -1;
+    }
     for (int64_t i = n_pad + tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
-    for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
+    if (a.full)
+        for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
 
     // 3. stable scatter: each wave walks its chunk 64 assignments at a time.
-    // Lanes with the same expert find each other with 9 ballots over the id
-    // bits; the rank of an assignment is its wave's running base for that
-    // expert plus the number of lower lanes with the same expert.  The
+    // Lanes with the same expert find each other with one ballot per bit of
+    // the key (the expert id, or E for an invalid id: as many bits as E has,
+    // at most 9); the rank of an assignment is its wave's running base for
+    // that expert plus the number of lower lanes with the same expert.  The
     // lowest such lane then advances the base.  No workgroup barrier: the
     // bases of a wave are its own.
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int key_bits = 32 - __clz(E);
     for (int base = c_lo; base < c_lo + chunk; base += 64) {
         const int p = base + lane;
         const int id = p < c_hi ? (in_lds ? s_ids[p] : a.ids[p]) : -1;
         const bool valid = (unsigned)id < (unsigned)E;
-        const int key = valid ? id : 511;
+        const int key = valid ? id : E;
         uint64_t m = ~0ull;
 #pragma unroll
         for (int b = 0; b < 9; ++b) {
+            if (b >= key_bits) break;
             const bool bit = (key >> b) & 1;
             const uint64_t bal = __ballot(bit);
             m &= bit ? bal : ~bal;
@@ -187,11 +208,16 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         const int wrank = __popcll(m & lt_mask);
         if (valid) {
             const int r = s_wcnt[wave][id] + wrank;
-            a.pos[p] = s_off[id] + r;
-            a.ppos[p] = s_poff[id] + r;
-            a.sorted_p[s_off[id] + r] = p;
-            a.row_src[s_poff[id] + r] = p;
-        } else if (p < c_hi) {
+            if (a.full) {
+                a.pos[p] = s_off[id] + r;
+                a.ppos[p] = s_poff[id] + r;
+                a.sorted_p[s_off[id] + r] = p;
+            }
+            if (stage_rows)
+                s_rows[s_poff[id] + r] = p;
+            else
+                a.row_src[s_poff[id] + r] = p;
+        } else if (p < c_hi && a.full) {
             a.pos[p] = -1;
             a.ppos[p] = -1;
         }
@@ -200,6 +226,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         if (valid && wrank == 0) s_wcnt[wave][id] += __popcll(m);
     }
     __syncthreads();
+
+    if (stage_rows)  // row_src out of LDS, coalesced
+        for (int i = tid; i < n_pad; i += kRouteThreads) a.row_src[i] = s_rows[i];
 
     // 4. block map: expert and first padded row of each group block
     const int ntiles = n_pad / kBlockM;
@@ -295,6 +324,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
         s_seg[tid][kXcds] = run;
     }
+    // with more tasks than threads: the rank of every M-tile of each list, so
+    // that a task finds its expert rank with one LDS read instead of a binary
+    // search (the ids in LDS are no longer needed)
+    short* s_rank_of = s_ids;  // [2][kRankTable]
+    const bool rank_table = s_mtoff[0][E] * a.nb1 + s_mtoff[1][E] * a.nb2 > kRouteThreads &&
+                            s_mtoff[0][E] <= kRankTable && s_mtoff[1][E] <= kRankTable;
+    if (rank_table) {
+        const int mt0 = s_mtoff[0][E];
+        for (int g = tid; g < mt0 + s_mtoff[1][E]; g += kRouteThreads) {
+            const int list = g < mt0 ? 0 : 1;
+            const int m = list == 0 ? g : g - mt0;
+            s_rank_of[list * kRankTable + m] = (short)upper_index(s_mtoff[list], E, m);
+        }
+    }
     __syncthreads();
     {
         // both lists in one pass over their concatenated task indices
@@ -307,7 +350,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
             int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
             // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb), column-major
-            const int r = upper_index(s_mtoff[list], E, i / nb);
+            const int r = rank_table ? s_rank_of[list * kRankTable + i / nb] : upper_index(s_mtoff[list], E, i / nb);
             const int mt = s_mt[list][r];
             const int local = i - s_mtoff[list][r] * nb;
             const int cb = local / mt;

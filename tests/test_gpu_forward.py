@@ -228,8 +228,9 @@ def test_empty_batch_is_noop():
 
 @pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024", "qwen_bf16", "ds_mxfp8_1024"])
 def test_forward_routing_and_task_list(oracle, name):
-    """The workspace after a forward call holds the oracle's routing metadata and
-    task lists that cover every (group block, column block) pair exactly once."""
+    """The workspace after a forward call holds the oracle's counts, padded
+    permutation (row_src) and routing weight per padded row, and task lists that
+    cover every (group block, column block) pair exactly once."""
     import torch
     w = W.config(name)
     d = device.upload(w)
@@ -246,7 +247,10 @@ def test_forward_routing_and_task_list(oracle, name):
     r = oracle.route(w.topk_ids.ravel(), w.E, moe.moe_block_m())
     N = w.T * w.k
     assert np.array_equal(arr(L.counts, w.E), r["counts"])
-    assert np.array_equal(arr(L.pos, N), r["pos"])
+    assert np.array_equal(arr(L.offsets, w.E + 1), r["offsets"])
+    assert np.array_equal(arr(L.padded_offsets, w.E + 1), r["padded_offsets"])
+    # the layer writes the padded permutation its GEMMs consume; the compact
+    # pos / ppos / sorted_p arrays are moe_route's (tested in test_gpu_route)
     assert np.array_equal(arr(L.row_src, L.n_pad_cap), r["row_src"])
     # routing weight by padded row: a copy of topk_w, exact; 0 on padding rows
     n_pad = int(r["padded_offsets"][-1])
