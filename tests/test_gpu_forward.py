@@ -73,6 +73,15 @@ def test_small_shapes_full_parity(oracle, mode, packed):
 
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+def test_small_shapes_d_expert_384(oracle, mode, packed):
+    """d_e = 384: three FP8 / six bf16 GEMM-1 column blocks, ragged expert
+    groups up to several M-tiles."""
+    w = W.custom(300, 6, 2, 256, 384, mode, seed=23)
+    _check(w, oracle, label="d_e=384", packed=packed)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
 def test_clamped_activation_small_shapes(oracle, mode, packed):
     """The clamped activation on widened inputs (x scaled by 4: about a tenth
     of the gate and up values lie beyond the clamp), ragged expert groups."""
@@ -161,11 +170,12 @@ def _packed_reference(wt, gated, bn):
     return w5[:, row, b, s ^ (r & 7)].reshape(-1)
 
 
+@pytest.mark.parametrize("d_e", [256, 384])
 @pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
-def test_pack_weights_is_the_stated_permutation(mode):
+def test_pack_weights_is_the_stated_permutation(mode, d_e):
     """moe_pack_weights output, byte for byte, against the header's formula."""
     import torch
-    w = W.custom(8, 3, 2, 384, 256, mode, seed=3)
+    w = W.custom(8, 3, 2, 384, d_e, mode, seed=3)
     d = device.upload(w)
     p1, p2 = moe.pack_weights(d["w1"], d["w2"])
     torch.cuda.synchronize()
