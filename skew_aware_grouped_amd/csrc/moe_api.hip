@@ -34,12 +34,11 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     const int64_t N = (int64_t)d->num_tokens * d->top_k;
     const int64_t E = d->num_experts;
     route_caps(N, E, &L->n_pad_cap, &L->tile_cap);
-    // M-tiles: each expert's blocks grouped kMaxRowBlocks1 (GEMM-1) or
-    // kMaxRowBlocks2 (GEMM-2) at a time
-    // (GEMM-1 may fall back to kMaxRowBlocks2-block tiles, so both lists are
-    // sized for those)
-    const int64_t mtile_cap2 = L->tile_cap / kMaxRowBlocks2 + (E < N ? E : N);
-    const int64_t mtile_cap1 = mtile_cap2;
+    // M-tiles: each expert's blocks grouped 8 at a time (GEMM-1; GEMM-2 outside
+    // MXFP8 mode), or kSmallRowBlocks when 8-block tiles would leave too few
+    // tasks: both lists are sized for the smaller tiles
+    const int64_t mtile_cap1 = L->tile_cap / kSmallRowBlocks + (E < N ? E : N);
+    const int64_t mtile_cap2 = mtile_cap1;
     L->block_n1 = gemm1_block_n(d->mode);
     L->block_n2 = gemm2_block_n(d->mode);
     L->max_row_blocks = kMaxRowBlocks1;
@@ -231,6 +230,10 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.nb1 = d_e / L.block_n1;
     r.nb2 = d_h / L.block_n2;
     r.min_tasks1 = cus * occ1;
+    r.mb2 = gemm2_row_blocks(mode);
+    // GEMM-2's tasks are short: 128-row tiles only when every workgroup slot
+    // still gets two tasks (Qwen shapes at 1024 tokens stay at 64-row tiles)
+    r.min_tasks2 = 2 * cus * occ2;
     // persistent grids: at most one workgroup per task, at most what fits on the chip
     const int grid1 = (int)std::max<int64_t>(std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1), 1);
     const int grid2 = (int)std::max<int64_t>(std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2), 1);

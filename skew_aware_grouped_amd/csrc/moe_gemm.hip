@@ -954,11 +954,25 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
 #define MOE_G2(NS)                                                                                                 \
     gemm_task<MODE, false, NS, RING>(a.h, a.h_scale, a.row_src, 1, a.w2, a.w2_scale, a.zero, e, row0, cb, a.d_e, a.d_h, \
                                      a.packed != 0, smem, nullptr, &a, sch, q.rows[par], q.roww[par], par)
-        switch (nsub) {
-            case 1: MOE_G2(1); break;
-            case 2: MOE_G2(2); break;
-            case 3: MOE_G2(3); break;
-            default: MOE_G2(4); break;
+        // 128-row tasks outside MXFP8 mode (gemm2_row_blocks)
+        if constexpr (MODE != MOE_MODE_MXFP8) {
+            switch (nsub) {
+                case 1: MOE_G2(1); break;
+                case 2: MOE_G2(2); break;
+                case 3: MOE_G2(3); break;
+                case 4: MOE_G2(4); break;
+                case 5: MOE_G2(5); break;
+                case 6: MOE_G2(6); break;
+                case 7: MOE_G2(7); break;
+                default: MOE_G2(8); break;
+            }
+        } else {
+            switch (nsub) {
+                case 1: MOE_G2(1); break;
+                case 2: MOE_G2(2); break;
+                case 3: MOE_G2(3); break;
+                default: MOE_G2(4); break;
+            }
         }
 #undef MOE_G2
     }

@@ -15,11 +15,14 @@ namespace moe {
 constexpr int kBlockM = 16;
 // A GEMM-1 task covers up to kMaxRowBlocks1 consecutive group blocks of one
 // expert (128 rows), so a hot expert's W1 is streamed once per 128 of its
-// rows; a GEMM-2 task up to kMaxRowBlocks2 (64 rows: the larger FP8 body
-// would need more registers than two workgroups per CU leave).  The kernels
-// carry one fully unrolled body per block count.
+// rows, or kSmallRowBlocks when 128-row tiles would leave too few tasks.  A
+// GEMM-2 task covers up to gemm2_row_blocks(mode) blocks: 8 in the bf16 and
+// FP8 modes, 4 in MXFP8 mode (its 128-row body would need more registers than
+// two workgroups per CU leave).  The kernels carry one fully unrolled body per
+// block count.
 constexpr int kMaxRowBlocks1 = 8;
-constexpr int kMaxRowBlocks2 = 4;
+constexpr int kMaxRowBlocks2 = 8;
+constexpr int kSmallRowBlocks = 4;
 constexpr int kMaxRowBlocks = kMaxRowBlocks1;
 // Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.
 constexpr int kGemmWaves = 4;
@@ -69,6 +72,7 @@ __host__ __device__ inline int static_tasks(int grid, int x, int seg_len) {
 inline bool mode_fp8(int mode) { return mode == MOE_MODE_FP8 || mode == MOE_MODE_MXFP8; }  // e4m3 operands
 inline int gemm1_block_n(int mode) { return mode_fp8(mode) ? 128 : 64; }
 inline int gemm2_block_n(int) { return 128; }
+inline int gemm2_row_blocks(int mode) { return mode == MOE_MODE_MXFP8 ? kSmallRowBlocks : kMaxRowBlocks2; }
 
 struct RouteArgs {
     const int32_t* ids;
@@ -76,6 +80,8 @@ struct RouteArgs {
     int64_t n_pad_cap, tile_cap;
     int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
     int32_t min_tasks1;  // GEMM-1 takes kMaxRowBlocks1-block M-tiles only if that leaves this many tasks
+    int32_t mb2;         // largest GEMM-2 M-tile in group blocks (gemm2_row_blocks)
+    int32_t min_tasks2;  // GEMM-2 takes 8-block M-tiles only if that leaves this many tasks
     int32_t grid1, grid2;  // workgroups of the GEMM kernels (their first tasks are assigned statically)
     int32_t full;          // also write pos, ppos and sorted_p (the layer itself consumes row_src only)
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ int s_mtoff[2][kMaxExperts + 1];
     __shared__ int s_xpre[2][kXcds][kMaxExperts + 1];  // per list and XCD: tasks of lower ranks
     __shared__ int s_seg[2][kXcds + 1];
-    __shared__ int s_dropped, s_mb1;
+    __shared__ int s_dropped, s_mb1, s_mb2;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -285,23 +285,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             }
         }
     }
-    // GEMM-1 M-tiles: kMaxRowBlocks1 blocks (fewer weight re-reads) when that
-    // still leaves min_tasks1 tasks, otherwise kMaxRowBlocks2 (more tasks to
-    // spread over the CUs); the last wave decides after its share of the ranking
+    // M-tiles of 8 group blocks (fewer weight re-reads) when that still leaves
+    // min_tasks1 (min_tasks2) tasks, otherwise kSmallRowBlocks (more tasks to
+    // spread over the CUs); the last wave decides for both lists after its
+    // share of the ranking
     if (wave == kRouteWaves - 1) {
         int big = 0;
-        for (int e = lane; e < E; e += 64) big += (s_tiles[e] + kMaxRowBlocks1 - 1) / kMaxRowBlocks1;
+        for (int e = lane; e < E; e += 64) big += (s_tiles[e] + 7) >> 3;
         big = __builtin_amdgcn_readlane(wave_inclusive_scan(big, lane), 63);
-        if (lane == 0) s_mb1 = big * a.nb1 >= a.min_tasks1 ? kMaxRowBlocks1 : kMaxRowBlocks2;
+        if (lane == 0) {
+            s_mb1 = big * a.nb1 >= a.min_tasks1 ? kMaxRowBlocks1 : kSmallRowBlocks;
+            s_mb2 = a.mb2 == 8 && big * a.nb2 >= a.min_tasks2 ? 8 : kSmallRowBlocks;
+        }
     }
     __syncthreads();
-    const int mb1 = s_mb1;
+    const int mb1 = s_mb1, mb2 = s_mb2;
     // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2); the
     // M-tile sizes are powers of two
-    static_assert(kMaxRowBlocks1 == 8 && kMaxRowBlocks2 == 4, "M-tile sizes 8 and 4 group blocks");
-    const int lg_mb1 = mb1 == kMaxRowBlocks1 ? 3 : 2;
+    static_assert(kMaxRowBlocks1 == 8 && kMaxRowBlocks2 == 8 && kSmallRowBlocks == 4, "M-tile sizes 8 and 4 group blocks");
+    const int lg_mb1 = mb1 == 8 ? 3 : 2;
+    const int lg_mb2 = mb2 == 8 ? 3 : 2;
     auto mtiles = [&](int list, int r) {
-        const int lg = list == 0 ? lg_mb1 : 2;
+        const int lg = list == 0 ? lg_mb1 : lg_mb2;
         return (s_rtiles[r] + (1 << lg) - 1) >> lg;
     };
     {
@@ -347,7 +352,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             const int list = g < total0 ? 0 : 1;
             const int i = list == 0 ? g : g - total0;
             const int nb = list == 0 ? a.nb1 : a.nb2;
-            const int mb = list == 0 ? mb1 : kMaxRowBlocks2;
+            const int mb = list == 0 ? mb1 : mb2;
             int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
             // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb), column-major
             const int r = rank_table ? s_rank_of[list * kRankTable + i / nb] : upper_index(s_mtoff[list], E, i / nb);
