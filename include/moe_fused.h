@@ -221,9 +221,10 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
 
 /* Byte offsets of the workspace sections moe_fused_forward uses, for tests and
  * inspection after a call.  Of the routing arrays described for moe_route the
- * layer writes counts, offsets, padded_offsets, row_src and the block map (the
- * padded permutation its GEMMs consume); pos, ppos and sorted_p are sized here
- * but written by moe_route only.  row_w (fp32 [n_pad_cap]) holds the routing weight of each padded
+ * layer writes counts, offsets, padded_offsets and row_src (the padded
+ * permutation its GEMMs consume, with the task lists below); pos, ppos,
+ * sorted_p and the block map (tile_expert, tile_row0) are sized here but
+ * written by moe_route only.  row_w (fp32 [n_pad_cap]) holds the routing weight of each padded
  * row below padded_offsets[E] (0 on padding rows).  `stats` is a control block of int32 words: [0..4] = {dropped,
  * blocks, padded rows, GEMM-1 tasks, GEMM-2 tasks}; words [272..280] and
  * [288..296] hold the start of each of the 8 per-XCD segments (and the end of

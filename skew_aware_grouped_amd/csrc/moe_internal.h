@@ -83,7 +83,7 @@ struct RouteArgs {
     int32_t mb2;         // largest GEMM-2 M-tile in group blocks (gemm2_row_blocks)
     int32_t min_tasks2;  // GEMM-2 takes 8-block M-tiles only if that leaves this many tasks
     int32_t grid1, grid2;  // workgroups of the GEMM kernels (their first tasks are assigned statically)
-    int32_t full;          // also write pos, ppos and sorted_p (the layer itself consumes row_src only)
+    int32_t full;          // also write pos, ppos, sorted_p and the block map (the layer consumes row_src and task lists)
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;
     int32_t* ctl;  // control block [kCtlWords]
     int4* tasks1;

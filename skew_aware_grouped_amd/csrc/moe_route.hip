@@ -230,9 +230,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     if (stage_rows)  // row_src out of LDS, coalesced
         for (int i = tid; i < n_pad; i += kRouteThreads) a.row_src[i] = s_rows[i];
 
-    // 4. block map: expert and first padded row of each group block
+    // 4. block map: expert and first padded row of each group block (the
+    // layer's GEMMs take the task lists instead, so only for moe_route)
     const int ntiles = n_pad / kBlockM;
-    for (int64_t i = tid; i < a.tile_cap; i += kRouteThreads) {
+    for (int64_t i = tid; a.full && i < a.tile_cap; i += kRouteThreads) {
         if (i < ntiles) {
             const int r = (int)i * kBlockM;
             a.tile_expert[i] = upper_index(s_poff, E, r);
