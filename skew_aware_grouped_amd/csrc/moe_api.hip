@@ -231,6 +231,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.nb2 = d_h / L.block_n2;
     r.min_tasks1 = cus * occ1;
     r.mb2 = gemm2_row_blocks(mode);
+    r.mix1 = mode != MOE_MODE_FP8;
     // GEMM-2's tasks are short: 128-row tiles only when every workgroup slot
     // still gets two tasks (Qwen shapes at 1024 tokens stay at 64-row tiles)
     r.min_tasks2 = 2 * cus * occ2;

@@ -82,6 +82,7 @@ struct RouteArgs {
     int32_t min_tasks1;  // GEMM-1 takes kMaxRowBlocks1-block M-tiles only if that leaves this many tasks
     int32_t mb2;         // largest GEMM-2 M-tile in group blocks (gemm2_row_blocks)
     int32_t min_tasks2;  // GEMM-2 takes 8-block M-tiles only if that leaves this many tasks
+    int32_t mix1;        // GEMM-1 may mix 8- and 4-block M-tiles (not in FP8 mode, whose 128-row epilogue is long)
     int32_t grid1, grid2;  // workgroups of the GEMM kernels (their first tasks are assigned statically)
     int32_t full;          // also write pos, ppos, sorted_p and the block map (the layer consumes row_src and task lists)
     int32_t *counts, *offsets, *padded_offsets, *pos, *sorted_p, *ppos, *row_src, *tile_expert, *tile_row0;

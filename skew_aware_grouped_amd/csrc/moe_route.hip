@@ -304,10 +304,42 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2); the
     // M-tile sizes are powers of two
     static_assert(kMaxRowBlocks1 == 8 && kMaxRowBlocks2 == 8 && kSmallRowBlocks == 4, "M-tile sizes 8 and 4 group blocks");
-    const int lg_mb1 = mb1 == 8 ? 3 : 2;
+    // When 8-block GEMM-1 tiles leave workgroup slots idle but 4-block tiles
+    // make more tasks than slots (a second, partial round), the hottest ranks
+    // [0, r8) keep 8-block tiles: the fewest that bring the task count down to
+    // min_tasks1.  Every wave works r8 out itself (no barrier).  Not in FP8
+    // mode (mix1 = 0), where a 128-row task's epilogue costs more than the
+    // partial round it saves.
+    int r8 = mb1 == 8 ? E : 0;
+    if (mb1 != 8 && a.mix1) {
+        int t4 = 0, d8[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lane + i;
+            const int t = r < E ? s_rtiles[r] : 0;
+            t4 += (t + 3) >> 2;
+            d8[i] = ((t + 3) >> 2) - ((t + 7) >> 3);  // M-tiles saved by 8-block tiles
+        }
+        const int total4 = __builtin_amdgcn_readlane(wave_inclusive_scan(t4, lane), 63);
+        const int need = total4 * a.nb1 - a.min_tasks1;  // tasks to remove
+        if (need > 0) {
+            const int dl = d8[0] + d8[1] + d8[2] + d8[3];
+            int run = wave_inclusive_scan(dl, lane) - dl;  // saved by the ranks before this lane's
+            int first = kMaxExperts;                        // first rank whose prefix covers need
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                run += d8[i];
+                if (first == kMaxExperts && run * a.nb1 >= need && 4 * lane + i < E) first = 4 * lane + i;
+            }
+            const uint64_t hit = __ballot(first < kMaxExperts);
+            r8 = hit ? __builtin_amdgcn_readlane(first, __builtin_ctzll(hit)) + 1 : E;
+        }
+    }
+    // group blocks per GEMM-1 M-tile of rank r
+    auto mb1_of = [&](int r) { return r < r8 ? 8 : kSmallRowBlocks; };
     const int lg_mb2 = mb2 == 8 ? 3 : 2;
     auto mtiles = [&](int list, int r) {
-        const int lg = list == 0 ? lg_mb1 : lg_mb2;
+        const int lg = list == 0 ? (r < r8 ? 3 : 2) : lg_mb2;
         return (s_rtiles[r] + (1 << lg) - 1) >> lg;
     };
     {
@@ -353,10 +385,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             const int list = g < total0 ? 0 : 1;
             const int i = list == 0 ? g : g - total0;
             const int nb = list == 0 ? a.nb1 : a.nb2;
-            const int mb = list == 0 ? mb1 : mb2;
             int4* tasks = list == 0 ? a.tasks1 : a.tasks2;
             // rank r owns tasks [s_mtoff[r]*nb, s_mtoff[r+1]*nb), column-major
             const int r = rank_table ? s_rank_of[list * kRankTable + i / nb] : upper_index(s_mtoff[list], E, i / nb);
+            const int mb = list == 0 ? mb1_of(r) : mb2;
             const int mt = s_mt[list][r];
             const int local = i - s_mtoff[list][r] * nb;
             const int cb = local / mt;
