@@ -236,7 +236,7 @@ def test_empty_batch_is_noop():
     assert out.shape == (0, 256)
 
 
-@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024", "qwen_bf16", "ds_mxfp8_1024"])
+@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024", "qwen_bf16", "ds_mxfp8_1024", "qwen_mxfp8"])
 def test_forward_routing_and_task_list(oracle, name):
     """The workspace after a forward call holds the oracle's counts, padded
     permutation (row_src) and routing weight per padded row, and task lists that
