@@ -3,11 +3,16 @@
 
 A step is one moe_fused_forward call (routing -> GEMM-1 + SwiGLU -> GEMM-2 +
 routing weight -> combine) over the synthetic workload, inputs resident in
-HBM.  W untimed warmup steps, then K timed steps, each bracketed by HIP
-events on the stream the library launches on; the line reports the p50 step
-time, TFLOP/s at that p50 (algorithmic FLOPs = 6*d_h*d_e per valid
-assignment), the dominant kernel's roofline fraction from its own event-timed
-duration, and the CPU oracle timed on a bounded sample.
+HBM.  The default workload is the largest single-GPU one: 8192 tokens of the
+DeepSeek-shaped FP8 layer (7168/2048, 32 experts, top-2, two experts with 30%
+of the assignments each, 16 empty).  W untimed warmup steps, then K timed
+steps, each bracketed by HIP events on the stream the library launches on,
+with the L2s and the 256 MB Infinity Cache flushed before each step outside
+its events (cold); the same steps without the flush give the warm figures.
+The line reports the cold p50 step time (ms_per_step), TFLOP/s at that p50
+(algorithmic FLOPs = 6*d_h*d_e per valid assignment), the dominant kernel's
+roofline fraction from its mean dispatch duration, and the CPU oracle timed on
+a bounded sample.
 
 The weights are rewritten once, before any timing, into the packed tile order
 (moe_pack_weights), as a deployment does when it loads them; ``--weights
@@ -30,7 +35,7 @@ METRIC = "fused MoE layer p50 µs + TFLOP/s (% MFMA/HBM roofline), 1 MI355X"
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 5000.0, 3: 5000.0}  # dense MFMA: bf16 (F32ACT runs bf16 MFMA), fp8
 DTYPE = {0: "bf16", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp8_e4m3"}
-DEFAULT_CONFIG = "qwen_bf16"
+DEFAULT_CONFIG = "ds_fp8_8192"
 
 
 def gemm1_alg_bytes(w):
@@ -80,6 +85,18 @@ def measured_traffic(kernel, workload, weights):
     return None
 
 
+def cpu_model():
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, target_s=12.0):
     """The oracle as it stands, on a bounded sample of the workload: a token
     subset when the whole batch would take longer than ~target_s, otherwise the
@@ -103,6 +120,7 @@ def cpu_baseline(w, target_s=12.0):
     nv = int(((sub_ids >= 0) & (sub_ids < w.E)).sum())
     flops = 6.0 * w.d_h * w.d_e * nv * reps
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{n} of {w.T} tokens ({nv} assignments) of {w.name}, {reps} pass(es), {dt:.2f} s, "
                       f"fp32 C oracle with OpenMP over tokens",
             "seconds": round(dt, 3)}
@@ -169,17 +187,18 @@ def main():
     for _ in range(args.warmup):
         device.run(d, out=out, workspace=ws)
     stream = torch.cuda.current_stream()
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
 
-    def timed_steps(n, flush=None):
+    def timed_steps(n, cold):
         """n layer calls, each between two events on the library's stream (no
-        event between its kernels); with ``flush``, a read of a 1 GiB buffer
-        before each call, outside its events, leaves the L2s and the 256 MB
-        Infinity Cache holding other (clean) lines."""
+        event between its kernels); cold: a read of a 1 GiB buffer before each
+        call, outside its events, leaves the L2s and the 256 MB Infinity Cache
+        holding other (clean) lines."""
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for a, b in evs:
-            if flush is not None:
+            if cold:
                 flush.sum()
             a.record(stream)
             device.run(d, out=out, workspace=ws, stream=stream)
@@ -187,18 +206,26 @@ def main():
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs]), time.perf_counter() - t0
 
-    step_ms, wall = timed_steps(args.steps)
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-    cold_ms, _ = timed_steps(min(args.steps, 20), flush)
+    def dispatch_steps(n, cold):
+        """n calls of the kernel-timing variant: each of the four dispatches
+        records its own start and end (the durations a kernel trace reports)."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(n)]
+        for i in range(n):
+            if cold:
+                flush.sum()
+            device.run(d, out=out, workspace=ws, stream=stream, events=ev[i])
+        torch.cuda.synchronize()
+        return np.array([[e[2 * j].elapsed_time(e[2 * j + 1]) for j in range(4)] for e in ev])
+
+    cold_ms, wall = timed_steps(args.steps, cold=True)
+    warm_ms, _ = timed_steps(args.steps, cold=False)
+    # per-kernel durations over as many cold as warm dispatches: every launch
+    # of the run is one or the other, so the mean is the one a kernel trace of
+    # the whole command averages to
+    stage_ms = np.concatenate([dispatch_steps(args.steps, cold=True), dispatch_steps(args.steps, cold=False)])
     del flush
-    # per-kernel durations: the kernel-timing variant has each dispatch record
-    # its own start and end (what a kernel trace reports), in separate steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        device.run(d, out=out, workspace=ws, stream=stream, events=ev[i])
-    torch.cuda.synchronize()
-    stage_ms = np.array([[e[2 * j].elapsed_time(e[2 * j + 1]) for j in range(4)] for e in ev])
-    p50 = float(np.median(step_ms))
+    p50 = float(np.median(cold_ms))
+    warm_p50 = float(np.median(warm_ms))
     flops = W.flops(w)
     alg_bytes = W.algorithmic_bytes(w)
     tflops = flops / (p50 * 1e-3) / 1e12
@@ -219,7 +246,11 @@ def main():
         roof = {"kernel": "gemm1_kernel", "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4)}
     roof.update({"traffic": measured_traffic("gemm1_kernel", w.name, args.weights), "alg_bytes_per_launch": g1_bytes,
-                 "alg_flops_per_launch": g1_flops, "avg_launch_us": round(k_us, 2)})
+                 "alg_flops_per_launch": g1_flops, "avg_launch_us": round(k_us, 2),
+                 "avg_launch_source": f"mean of {len(stage_ms)} dispatch-event durations on the library's "
+                                      f"stream ({args.steps} after a cache flush, {args.steps} warm)",
+                 "avg_launch_us_cold": round(float(np.mean(stage_ms[:args.steps, 1])) * 1e3, 2),
+                 "avg_launch_us_warm": round(float(np.mean(stage_ms[args.steps:, 1])) * 1e3, 2)})
     res = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -228,6 +259,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(p50, 5),
+        "ms_per_step_is": "cold p50 (caches flushed before each step)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -238,12 +270,13 @@ def main():
                    "valid_assignments": w.valid_assignments(), "routing": str(w.meta.get("routing")),
                    "weight_layout": args.weights},
         "p50_us": round(p50 * 1e3, 2),
-        "p10_us": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
-        "p90_us": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
-        "cold_p50_us": round(float(np.median(cold_ms)) * 1e3, 2),
-        "cold_p10_us": round(float(np.percentile(cold_ms, 10)) * 1e3, 2),
-        "cold_p90_us": round(float(np.percentile(cold_ms, 90)) * 1e3, 2),
-        "wall_us_per_step": round(wall / args.steps * 1e6, 2),
+        "p10_us": round(float(np.percentile(cold_ms, 10)) * 1e3, 2),
+        "p90_us": round(float(np.percentile(cold_ms, 90)) * 1e3, 2),
+        "warm_p50_us": round(warm_p50 * 1e3, 2),
+        "warm_p10_us": round(float(np.percentile(warm_ms, 10)) * 1e3, 2),
+        "warm_p90_us": round(float(np.percentile(warm_ms, 90)) * 1e3, 2),
+        "warm_tflops": round(flops / (warm_p50 * 1e-3) / 1e12, 3),
+        "wall_us_per_step_cold_incl_flush": round(wall / args.steps * 1e6, 2),
         "gflop": round(flops / 1e9, 4),
         "alg_mb": round(alg_bytes / 1e6, 3),
         "layer_gbs": round(layer_gbs, 1),

@@ -28,6 +28,16 @@
  *  - Return value: MOE_OK (0) or an error code.  Argument checks run on the host
  *    before anything is enqueued; on error nothing is enqueued.  MOE_ERR_HIP
  *    reports a failed launch (the HIP error is then cleared).
+ *  - The caller lends all device memory, the workspace included (PipeLink,
+ *    section 5.3: each owner of the MoE megakernel builds its descriptors from
+ *    caller-lent buffers).  So the library holds no device allocation: there
+ *    is no call to install or release a library-owned workspace, no
+ *    out-of-memory error, and nothing to shut down.  Faults of enqueued device
+ *    work surface through the stream (hipStreamSynchronize and the like), as
+ *    for any kernel; no kernel here waits on the device, so there is no
+ *    watchdog word to poll.
+ *  - Shapes travel in moe_dims (plain integers); each pointer is a dense
+ *    row-major array whose dtype the mode fixes.
  */
 #ifndef MOE_FUSED_H
 #define MOE_FUSED_H
@@ -115,12 +125,19 @@ typedef struct {
 } moe_scales;
 
 /* Bytes of device workspace moe_fused_forward needs for these dims (routing
- * metadata, task lists, the intermediate and the per-assignment rows).
+ * metadata, task lists, the intermediate and the per-assignment rows): the
+ * caller-lent buffer of PipeLink section 5.3 (the MoE megakernel's owners
+ * take their buffers from the caller), sized on the host with no device call.
  * Returns 0 if the dims are invalid. */
 MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
 
 /*
- * Fused MoE forward:
+ * Fused MoE forward (tilelang.dataflow README, section 3.5 "Fused MoE: map ->
+ * reshared -> map", steps 1 to 5: grouping metadata, GEMM-1 with the gated
+ * activation, GEMM-2, routing weights, output rows).  The whole call is
+ * enqueued without host computation and can be captured in a HIP graph, the
+ * property PipeLink section 4 ("Contract-Guided Linking") states for an open
+ * session behind its C interface.
  *   out[t] = sum_{j<k} topk_w[t,j] * W2[e] . ( silu(W1[e][0:d_e] . x[t]) * (W1[e][d_e:2d_e] . x[t]) ),
  *   e = topk_ids[t,j]  (or the clamped activation in place of silu(g) * u).
  *
@@ -139,12 +156,21 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
  * block map and per-XCD task lists), grouped GEMM-1 with the SwiGLU epilogue,
  * grouped GEMM-2 with the routing-weight epilogue, and the top-k combine in
  * ascending slot order.  The result is bitwise identical across calls.
+ * Ownership: every buffer is the caller's; the call keeps no pointer past
+ * the stream work it enqueues.  num_tokens == 0 returns MOE_OK and enqueues
+ * nothing.  Errors: MOE_ERR_INVALID_ARG (null dims, a field of dims out of
+ * range, a null or misaligned tensor pointer, missing scales in a quantised
+ * mode); MOE_ERR_UNSUPPORTED (dims within range but outside the envelope
+ * above, e.g. d_hidden not a multiple of 128); MOE_ERR_WORKSPACE (workspace
+ * null, too small or not 256-byte aligned); MOE_ERR_HIP (a launch failed).
  */
 MOE_API int moe_fused_forward(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
                       const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
-/* moe_fused_forward with kernel timing: events[0..7] (hipEvent_t, created by
+/* moe_fused_forward with kernel timing (kernel durations are what the
+ * tilelang.dataflow README's "Fused MoE vs MegaMoE" comparison times for the
+ * competitor, from its profiler): events[0..7] (hipEvent_t, created by
  * the caller with timing enabled) receive the start and end of the routing,
  * GEMM-1, GEMM-2 and combine kernels as their dispatches record them
  * (events[2i] start, events[2i+1] end of kernel i), so hipEventElapsedTime on
@@ -158,7 +184,9 @@ MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, cons
 
 /*
  * Rewrite row-major W1 and W2 (bf16 or e4m3 as dims->mode says) into the
- * packed tile order, once, when the weights are loaded; the forward call then
+ * packed tile order, once, when the weights are loaded (a storage choice for
+ * the weight shard each GEMM task loads, tilelang.dataflow README section 3.5
+ * step 2; no page defines this order); the forward call then
  * streams each task's weight tile as one contiguous block instead of one
  * 128-byte piece per weight row (dims->weight_layout is ignored here).  The
  * permutation moves 16-byte chunks; block scales keep their layout.
@@ -184,8 +212,9 @@ MOE_API int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w
  * multiple of this (tilelang.dataflow README section 3.5, "padded offsets"). */
 MOE_API int32_t moe_block_m(void);
 
-/* Capacities of the padded row space and of the block map for N = T*k
- * assignments over E experts: n_pad_cap = N + min(E,N)*(block_m-1),
+/* Capacities of the padded row space and of the block map (tilelang.dataflow
+ * README section 3.5 step 1: padded offsets, expert of each group block) for
+ * N = T*k assignments over E experts: n_pad_cap = N + min(E,N)*(block_m-1),
  * tile_cap = n_pad_cap / block_m. */
 MOE_API int moe_route_caps(int32_t num_tokens, int32_t top_k, int32_t num_experts, int64_t* n_pad_cap,
                    int64_t* tile_cap);
@@ -215,12 +244,19 @@ typedef struct {
 } moe_route_out;
 
 /* Routing metadata alone (the first step of moe_fused_forward, same kernel),
- * for N = T*k flat assignment ids. */
+ * for N = T*k flat assignment ids: the group sizes, offsets, padded offsets
+ * and expert of each group block that tilelang.dataflow README section 3.5
+ * step 1 takes as the fused MoE's input, plus the stable permutation.
+ * MOE_ERR_INVALID_ARG for a null output pointer (or null ids with N > 0) or
+ * top_k / num_experts outside [1,8] / [1,256]; MOE_ERR_UNSUPPORTED for
+ * N >= 2^31. */
 MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, const int32_t* topk_ids,
               const moe_route_out* out, void* stream);
 
 /* Byte offsets of the workspace sections moe_fused_forward uses, for tests and
- * inspection after a call.  Of the routing arrays described for moe_route the
+ * inspection after a call.  The task lists are the device-built form of the
+ * per-queue plans of tilelang.dataflow README section 3.5 (a hot expert
+ * yields more group-block tasks; queues may take unequal amounts of work).  Of the routing arrays described for moe_route the
  * layer writes counts, offsets, padded_offsets and row_src (the padded
  * permutation its GEMMs consume, with the task lists below); pos, ppos,
  * sorted_p and the block map (tile_expert, tile_row0) are sized here but

@@ -3,8 +3,8 @@
 The functions with the C names marshal arguments and call the library; every
 step of the layer runs in the HIP kernels.  ``fused_forward`` is a torch
 convenience on top: it derives the dims from tensor shapes, checks dtypes, keeps
-a workspace tensor per device and passes ``data_ptr()`` values and the current
-stream.  There is no fallback: if the library is missing, loading fails.
+a workspace tensor per (device, stream) and passes ``data_ptr()`` values and the
+current stream.  There is no fallback: if the library is missing, loading fails.
 """
 from __future__ import annotations
 
@@ -180,14 +180,24 @@ def _mode_of(x, w1, x_scale=None):
 _workspaces = {}
 
 
-def workspace_for(dims: moe_dims, device):
-    """A cached uint8 workspace tensor large enough for ``dims`` on ``device``."""
+def workspace_for(dims: moe_dims, device, stream=None):
+    """A cached uint8 workspace tensor large enough for ``dims``, one per
+    (device, stream): calls that share a workspace must be ordered on one
+    stream (the routing counters, task queues and intermediates in it are
+    rewritten by every call), so two streams never get the same buffer.  The
+    tensor is allocated on that stream, so torch's allocator does not reuse
+    its memory while work queued there may still read it."""
     import torch
     need = moe_workspace_bytes(dims)
-    key = (str(device),)
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    key = (str(dev), int(s.cuda_stream))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
@@ -248,7 +258,7 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
             if t is None or not (t.is_cuda and t.is_contiguous()) or t.dtype != sdt:
                 raise ValueError(f"{name} must be a contiguous {sdt} device tensor")
         scales = moe_scales(x_scale.data_ptr(), w1_scale.data_ptr(), w2_scale.data_ptr())
-    ws = workspace if workspace is not None else workspace_for(dims, x.device)
+    ws = workspace if workspace is not None else workspace_for(dims, x.device, stream)
     args = (dims, x.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w1.data_ptr(), w2.data_ptr(), scales,
             out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(stream))
     if events is None:
