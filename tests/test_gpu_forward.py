@@ -224,7 +224,10 @@ def test_edge_cases(oracle, case, mode, packed):
         ids[::3, 0] = -1
         ids[1::5, 1] = E + 3
         ids[7, :] = -2  # a token with no valid assignment -> zero row
-    w = W.custom(T, E, k, 256, 256 if mode in FP8_MODES else 128, mode, seed=13, topk_ids=ids)
+    # FP8 modes at d_e = 512: with every slot of a token on one expert, a
+    # flipped code of the intermediate repeats in both slots, and at d_e = 256
+    # the per-row bound sits at the edge of that flip noise (3.1e-2 measured)
+    w = W.custom(T, E, k, 256, 512 if mode in FP8_MODES else 128, mode, seed=13, topk_ids=ids)
     _check(w, oracle, label=case, packed=packed)
 
 
