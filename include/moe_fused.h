@@ -58,6 +58,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED 2 /* shape outside the supported envelope (see moe_dims) */
 #define MOE_ERR_WORKSPACE 3   /* workspace missing or smaller than moe_workspace_bytes() */
 #define MOE_ERR_HIP 4         /* a HIP launch or device query failed */
+#define MOE_ERR_SCRATCH 5     /* moe_fused_forward_noalloc: the dims need more than MOE_NOALLOC_SCRATCH_BYTES */
 
 /* Data modes (dtypes of x / weights / out):
  *  MOE_MODE_F32ACT  x fp32 [T,d_h]; W1, W2 bf16; out fp32.  The GEMMs run on
@@ -167,6 +168,31 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
 MOE_API int moe_fused_forward(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
                       const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * moe_fused_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory inside the library: each
+ * GPU the library runs on holds its own copy until the process ends.  Its
+ * device address is looked up once per device, on the first call with that
+ * device current (make one call before capturing the call in a graph).  The
+ * call allocates nothing and frees nothing; same kernels and result, bit for
+ * bit, as moe_fused_forward with a workspace of its own.
+ * The scratch keeps the last call's contents; every call writes what it reads
+ * before reading it.  Calls on one GPU share that GPU's scratch: calls that
+ * overlap in time on one GPU (two streams, or two host threads) race and give
+ * wrong results; order them on one stream.
+ * Errors: those of moe_fused_forward, with MOE_ERR_SCRATCH (checked on the
+ * host before anything else, nothing enqueued) when moe_workspace_bytes(dims)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES (e.g. 8192 tokens of the 7168/2048 top-2
+ * layer, whose per-assignment rows alone take 235 MB), and MOE_ERR_HIP if the
+ * scratch's address cannot be obtained.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+MOE_API int moe_fused_forward_noalloc(const moe_dims* dims, const void* x, const int32_t* topk_ids,
+                                      const float* topk_w, const void* w1, const void* w2,
+                                      const moe_scales* scales, void* out, void* stream);
 
 /* moe_fused_forward with kernel timing (kernel durations are what the
  * tilelang.dataflow README's "Fused MoE vs MegaMoE" comparison times for the

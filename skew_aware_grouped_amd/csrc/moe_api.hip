@@ -113,6 +113,33 @@ hipError_t device_info(int mode, int* cus, int* occ1, int* occ2) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Workspace of moe_fused_forward_noalloc, for callers that cannot allocate
+// device memory.  A file-scope device array: every GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  In host
+// code `scratch` names a host-side stand-in, not device memory, so it is never
+// passed to a kernel or copy: the device address comes from
+// hipGetSymbolAddress, taken once per device (with that device current) and
+// kept in g_scratch.
+__device__ __attribute__((aligned(256))) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+void* g_scratch[64] = {};
+
+hipError_t scratch_of_current_device(void** p) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (!g_scratch[dev]) {
+        void* q = nullptr;
+        err = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!q || ((uintptr_t)q & (kAlign - 1))) return hipErrorInvalidSymbol;
+        g_scratch[dev] = q;
+    }
+    *p = g_scratch[dev];
+    return hipSuccess;
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -129,6 +156,7 @@ const char* moe_error_string(int code) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape";
         case MOE_ERR_WORKSPACE: return "workspace missing or too small";
         case MOE_ERR_HIP: return "HIP launch or query failed";
+        case MOE_ERR_SCRATCH: return "workspace these dims need exceeds the fixed scratch of the no-allocation entry point";
         default: return "unknown error";
     }
 }
@@ -339,6 +367,28 @@ int moe_fused_forward(const moe_dims* dims, const void* x, const int32_t* topk_i
                       const void* w1, const void* w2, const moe_scales* scales, void* out, void* workspace,
                       size_t workspace_bytes, void* stream) {
     return forward_impl(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,
+                        nullptr);
+}
+
+int moe_fused_forward_noalloc(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                              const void* w1, const void* w2, const moe_scales* scales, void* out, void* stream) {
+    // the size check comes first: a rejected call touches no device
+    if (dims && dims_ok(dims) && dims->num_tokens > 0) {
+        moe_ws_layout L;
+        layout_of(dims, &L);
+        if (L.total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    }
+    if (dims && dims->num_tokens == 0 && dims_ok(dims)) return MOE_OK;
+    void* ws = nullptr;
+    if (dims && dims_ok(dims)) {
+        if (scratch_of_current_device(&ws) != hipSuccess) {
+            (void)hipGetLastError();
+            return MOE_ERR_HIP;
+        }
+    }
+    // invalid dims fall through to forward_impl's own checks (ws may be null
+    // then; it is rejected before any use)
+    return forward_impl(dims, x, topk_ids, topk_w, w1, w2, scales, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
                         nullptr);
 }
 

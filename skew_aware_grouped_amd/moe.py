@@ -22,6 +22,8 @@ MOE_ERR_INVALID_ARG = 1
 MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
+MOE_ERR_SCRATCH = 5
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 MOE_MODE_F32ACT = 0
 MOE_MODE_BF16 = 1
@@ -85,6 +87,8 @@ def lib():
     L.moe_fused_forward_profiled.restype = ctypes.c_int
     L.moe_fused_forward_profiled.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, P(moe_scales), vp, vp,
                                              ctypes.c_size_t, vp, P(vp)]
+    L.moe_fused_forward_noalloc.restype = ctypes.c_int
+    L.moe_fused_forward_noalloc.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, P(moe_scales), vp, vp]
     L.moe_pack_weights.restype = ctypes.c_int
     L.moe_pack_weights.argtypes = [P(moe_dims), vp, vp, vp, vp, vp]
     L.moe_block_m.restype = ctypes.c_int32
@@ -117,6 +121,12 @@ def moe_fused_forward(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace,
     return int(lib().moe_fused_forward(ctypes.byref(dims) if dims is not None else None, x, topk_ids, topk_w, w1,
                                        w2, ctypes.byref(scales) if scales is not None else None, out, workspace,
                                        workspace_bytes, stream))
+
+
+def moe_fused_forward_noalloc(dims, x, topk_ids, topk_w, w1, w2, scales, out, stream) -> int:
+    return int(lib().moe_fused_forward_noalloc(ctypes.byref(dims) if dims is not None else None, x, topk_ids, topk_w,
+                                               w1, w2, ctypes.byref(scales) if scales is not None else None, out,
+                                               stream))
 
 
 def moe_fused_forward_profiled(dims, x, topk_ids, topk_w, w1, w2, scales, out, workspace, workspace_bytes, stream,

@@ -111,3 +111,15 @@ def test_pack_weights_argument_errors_without_gpu():
     assert call(c=w1 + 256) == moe.MOE_ERR_INVALID_ARG  # w1_packed overlaps w1
     assert call(e=w1) == moe.MOE_ERR_INVALID_ARG  # w2_packed overlaps w1
     assert call(e=p1 + n1 - 16) == moe.MOE_ERR_INVALID_ARG  # the packed buffers overlap
+
+
+def test_noalloc_rejects_oversize_before_any_device_call():
+    """The no-allocation entry point refuses dims whose workspace exceeds its
+    fixed scratch, on the host, before looking up the scratch's address."""
+    d = _dims(T=8192)  # 8192 tokens of the 7168/2048 top-2 FP8 layer
+    assert moe.moe_workspace_bytes(d) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    p = 1 << 20
+    rc = moe.moe_fused_forward_noalloc(d, p, p, p, p, p, moe.moe_scales(p, p, p), p, None)
+    assert rc == moe.MOE_ERR_SCRATCH
+    assert "scratch" in moe.moe_error_string(rc)
+    assert moe.moe_fused_forward_noalloc(None, p, p, p, p, p, None, p, None) == moe.MOE_ERR_INVALID_ARG
