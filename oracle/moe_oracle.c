@@ -40,6 +40,14 @@
  * shared exponent floor(log2(amax)) - 8 (8 = the largest E4M3 exponent) and
  * saturating round-to-nearest-even elements.
  *
+ * INT8 mode (tokens quantised to int8 before the expert GEMMs, which
+ * dequantise them: the CUCo page, section 4 "Evaluation", DeepSeek-V3 MoE
+ * Dispatch and Combine, steps (1) and (3); the page fixes neither the
+ * granularity nor the weights' type): one fp32 scale per token, dequantised
+ * value = int8 code * scale; the weights are bf16 (the page computes in a
+ * higher precision than the tokens travel in) and the intermediate is
+ * rounded to bf16 as in BF16 mode.
+ *
  * Clamped activation (flag ORACLE_ACT_CLAMPED; the pages name the GPT-OSS
  * variant of SwiGLU as an independent activation owner, PipeLink section 5.3,
  * without defining it; the definition taken is the published GPT-OSS one):
@@ -60,6 +68,7 @@
 #define ORACLE_MODE_BF16 1   /* x bf16, W bf16, out bf16 */
 #define ORACLE_MODE_FP8 2    /* x e4m3 + scales, W e4m3 + 128x128 block scales, out bf16 */
 #define ORACLE_MODE_MXFP8 3  /* x, W e4m3 with E8M0 scales per 32 along the reduction dimension, out bf16 */
+#define ORACLE_MODE_INT8 4   /* x int8 codes + one fp32 scale per token, W bf16, out bf16 */
 
 /* flags */
 #define ORACLE_MIRROR_H 1 /* round the intermediate where the method stores it */
@@ -198,6 +207,8 @@ void oracle_mx_requant_block(double* a, int64_t n, uint8_t* scale) {
 static inline double ld_x(int mode, int f64, const void* x, const void* xs, int64_t d_h, int64_t t, int64_t c) {
     if (mode == ORACLE_MODE_F32ACT) return ((const float*)x)[t * d_h + c];
     if (mode == ORACLE_MODE_BF16) return oracle_bf16_decode(((const uint16_t*)x)[t * d_h + c]);
+    if (mode == ORACLE_MODE_INT8) /* x_scale [T]: one per token */
+        return R((double)((const int8_t*)x)[t * d_h + c] * ((const float*)xs)[t], f64);
     if (mode == ORACLE_MODE_MXFP8)  /* x_scale [T, d_h/32] */
         return e4m3_table[((const uint8_t*)x)[t * d_h + c]] *
                oracle_e8m0_decode(((const uint8_t*)xs)[t * (d_h / MXBLK) + c / MXBLK]);
@@ -220,7 +231,7 @@ static inline double ld_w(int mode, int f64, const void* w, const void* ws, int6
 
 static int check_dims(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_e) {
     if (T < 0 || E < 1 || k < 1 || d_h < 1 || d_e < 1) return 0;
-    if (mode < 0 || mode > 3) return 0;
+    if (mode < 0 || mode > 4) return 0;
     if (mode == ORACLE_MODE_FP8 && (d_h % QBLK || d_e % QBLK)) return 0;
     if (mode == ORACLE_MODE_MXFP8 && (d_h % MXBLK || d_e % MXBLK)) return 0;
     return 1;
@@ -291,6 +302,7 @@ int moe_oracle_forward(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d
     if (!x || !topk_ids || !topk_w || !w1 || !w2 || !out_acc) return ORACLE_EINVAL;
     if ((mode == ORACLE_MODE_FP8 || mode == ORACLE_MODE_MXFP8) && (!x_scale || !w1_scale || !w2_scale))
         return ORACLE_EINVAL;
+    if (mode == ORACLE_MODE_INT8 && !x_scale) return ORACLE_EINVAL;
     if (!rows) nrows = T;
     oracle_init();
 #pragma omp parallel for schedule(dynamic, 1)

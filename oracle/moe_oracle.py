@@ -23,6 +23,7 @@ MODE_F32ACT = 0
 MODE_BF16 = 1
 MODE_FP8 = 2
 MODE_MXFP8 = 3
+MODE_INT8 = 4
 MIRROR_H = 1
 ACC64 = 2
 ACT_CLAMPED = 4  # clamped activation (GPT-OSS variant of SwiGLU)
@@ -186,9 +187,10 @@ def forward(inp, rows=None, mirror: bool = True, acc64: bool = False):
     def c(a, dt):
         return None if a is None else np.ascontiguousarray(a, dtype=dt)
 
-    xdt = {MODE_F32ACT: np.float32, MODE_BF16: np.uint16, MODE_FP8: np.uint8, MODE_MXFP8: np.uint8}[mode]
+    xdt = {MODE_F32ACT: np.float32, MODE_BF16: np.uint16, MODE_FP8: np.uint8, MODE_MXFP8: np.uint8,
+           MODE_INT8: np.int8}[mode]
     wdt = np.uint8 if mode in (MODE_FP8, MODE_MXFP8) else np.uint16
-    sdt = np.uint8 if mode == MODE_MXFP8 else np.float32  # E8M0 bytes or fp32 scales
+    sdt = np.uint8 if mode == MODE_MXFP8 else np.float32  # E8M0 bytes or fp32 scales (per token in INT8 mode)
     x = c(inp.x, xdt)
     xs = c(inp.x_scale, sdt)
     ids = c(inp.topk_ids, np.int32)

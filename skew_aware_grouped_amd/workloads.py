@@ -20,6 +20,11 @@ and skewed routing with hot and empty experts:
                  28 share the rest by Zipf(1.0) (largest remainder, at least 1).
 * ``ds_fp8_8192`` 8192 tokens, 7168/2048, FP8; two experts get 30% each, 16
                  experts none, 14 share the rest by Zipf(1.0).
+* ``qwen_int8``, ``ds_int8_1024``: the Qwen-FP8 and 1024-token DeepSeek recipes
+                 with tokens quantised to int8 (one fp32 scale per token,
+                 s = amax/127, codes rounded to nearest even) and bf16 weights:
+                 the token quantisation of the CUCo page's DeepSeek-V3 MoE
+                 workload (its section 4, steps (1) and (3)).
 * ``qwen_mxfp8``, ``ds_mxfp8_<T>`` (T in {1024, 8192}): the same recipes in MXFP8
                  (the MX variant the pages name for the MoE kernels of PipeLink
                  section 5.3): e4m3 codes with one E8M0 scale per 32 values along
@@ -47,6 +52,7 @@ MODE_F32ACT = 0
 MODE_BF16 = 1
 MODE_FP8 = 2
 MODE_MXFP8 = 3
+MODE_INT8 = 4
 ACT_SWIGLU = 0          # silu(gate) * up
 ACT_SWIGLU_CLAMPED = 1  # clamped gate/up, gate * sigmoid(1.702 gate) * (up + 1)
 QBLK = 128
@@ -137,6 +143,16 @@ def quantize_mx(a: np.ndarray):
     return _to_e4m3_codes(q.reshape(R, C).astype(np.float32)), b.astype(np.uint8)
 
 
+def quantize_int8_rows(a: np.ndarray):
+    """[R, C] float -> int8 codes [R, C], fp32 scales [R] (one per row): s = amax/127
+    (1 for an all-zero row), codes = x/s rounded to nearest even, clamped to +-127."""
+    a = np.asarray(a, np.float32)
+    amax = np.abs(a).max(axis=1).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(127.0), np.float32(1.0)).astype(np.float32)
+    q = np.clip(np.rint(a / s[:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
 # ---------------------------------------------------------------- routing
 def route_uniform(rng, T, E, k):
     return np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
@@ -202,6 +218,8 @@ CONFIGS["ds_fp8_8192"] = dict(index=4, T=8192, E=32, k=2, d_h=7168, d_e=2048, mo
 CONFIGS["qwen_mxfp8"] = dict(CONFIGS["qwen_fp8"], index=5, mode=MODE_MXFP8)
 CONFIGS["ds_mxfp8_1024"] = dict(CONFIGS["ds_fp8_1024"], index=6, mode=MODE_MXFP8)
 CONFIGS["ds_mxfp8_8192"] = dict(CONFIGS["ds_fp8_8192"], index=7, mode=MODE_MXFP8)
+CONFIGS["qwen_int8"] = dict(CONFIGS["qwen_fp8"], index=8, mode=MODE_INT8)
+CONFIGS["ds_int8_1024"] = dict(CONFIGS["ds_fp8_1024"], index=9, mode=MODE_INT8)
 
 
 def make_routing(index, T, E, k, routing):
@@ -261,6 +279,8 @@ def make_workload(name, index, T, E, k, d_h, d_e, mode, routing, topk_ids=None, 
     x_scale = None
     if mode == MODE_FP8:
         x, x_scale = quantize_rows(xf)
+    elif mode == MODE_INT8:
+        x, x_scale = quantize_int8_rows(xf)
     elif mode == MODE_MXFP8:
         x, x_scale = quantize_mx(xf)
     else:
@@ -299,8 +319,10 @@ def algorithmic_bytes(w: MoEWorkload) -> float:
         per_expert += 4 * (2 * w.d_e // QBLK) * (w.d_h // QBLK) + 4 * (w.d_h // QBLK) * (w.d_e // QBLK)
     if w.mode == MODE_MXFP8:
         per_expert += 3 * w.d_h * w.d_e // MXBLK
-    xb = {MODE_F32ACT: 4, MODE_BF16: 2, MODE_FP8: 1, MODE_MXFP8: 1}[w.mode]
+    xb = {MODE_F32ACT: 4, MODE_BF16: 2, MODE_FP8: 1, MODE_MXFP8: 1, MODE_INT8: 1}[w.mode]
     x_bytes = w.T * w.d_h * xb + (w.T * (w.d_h // QBLK) * 4 if w.mode == MODE_FP8 else 0)
+    if w.mode == MODE_INT8:  # one fp32 scale per token
+        x_bytes += w.T * 4
     if w.mode == MODE_MXFP8:
         x_bytes += w.T * (w.d_h // MXBLK)
     out_bytes = w.T * w.d_h * (4 if w.mode == MODE_F32ACT else 2)

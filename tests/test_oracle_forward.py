@@ -31,6 +31,8 @@ def normwise(got, ref):
 def _deq_x(w):
     if w.mode == W.MODE_F32ACT:
         return torch.from_numpy(w.x).double()
+    if w.mode == W.MODE_INT8:  # int8 code * the token's fp32 scale
+        return torch.from_numpy(w.x.astype(np.int64)).double() * torch.from_numpy(w.x_scale).double()[:, None]
     if w.mode == W.MODE_BF16:
         return torch.from_numpy(w.x.view(np.int16)).view(torch.bfloat16).double()
     q = torch.from_numpy(w.x).view(torch.float8_e4m3fn).double()
@@ -53,7 +55,7 @@ def _deq_w(w, a, s):
 
 
 def _torch_h_round(a, mode):
-    if mode in (W.MODE_F32ACT, W.MODE_BF16):
+    if mode in (W.MODE_F32ACT, W.MODE_BF16, W.MODE_INT8):
         return a.float().to(torch.bfloat16).double()
     if mode == W.MODE_MXFP8:
         # per row per 32: X = floor(log2(amax)) - 8 (from frexp's exponent), values / 2^X
@@ -98,7 +100,7 @@ def _small(mode, T=24, E=5, k=3, d_h=256, d_e=256, seed=3, ids=None):
     return W.custom(T, E, k, d_h, d_e, mode, seed=seed, routing=routing, topk_ids=ids)
 
 
-MODES = [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8]
+MODES = [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8]
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -268,3 +270,33 @@ def test_mxfp8_with_power_of_two_blocks_equals_fp8(oracle):
     m.w2_scale = (ex2 + 127).astype(np.uint8).repeat(128, axis=1).repeat(4, axis=2)  # [E, d_h, d_e/32]
     acc_mx, _ = oracle.forward(m, mirror=False)
     assert np.array_equal(acc_fp8, acc_mx)
+
+
+def test_int8_with_unit_scales_equals_bf16(oracle):
+    """INT8 tokens whose scales are all 1 are the integers themselves, which
+    bf16 holds exactly: the INT8 mode must give, bit for bit, the BF16 mode's
+    output on x = bf16(code) with the same bf16 weights (pins the int8 decode,
+    signs included, to the pinned BF16 path)."""
+    w = _small(W.MODE_INT8, T=14, E=4, k=2, seed=8)
+    w.x_scale = np.ones_like(w.x_scale)
+    acc_i8, out_i8 = oracle.forward(w)
+    b = W.MoEWorkload(**{**w.__dict__})
+    b.mode = W.MODE_BF16
+    b.x = W.to_bf16_bits(w.x.astype(np.float32))
+    b.x_scale = None
+    acc_bf, out_bf = oracle.forward(b)
+    assert np.array_equal(acc_i8, acc_bf) and np.array_equal(out_i8, out_bf)
+    assert (w.x < 0).any() and ((w.x == 127).any() or (w.x == -127).any())
+
+
+def test_int8_scale_is_per_token(oracle):
+    """Scaling one token's int8 scale by 2 (an exact change of its dequantised
+    row) changes that token's output row and no other."""
+    w = _small(W.MODE_INT8, T=10, E=4, k=2, seed=9)
+    _, base = oracle.forward(w)
+    w2 = W.MoEWorkload(**{**w.__dict__})
+    w2.x_scale = w.x_scale.copy()
+    w2.x_scale[4] *= np.float32(2)
+    _, o = oracle.forward(w2)
+    changed = np.nonzero((o != base).any(axis=1))[0].tolist()
+    assert changed == [4]

@@ -3,7 +3,8 @@
 Each case edits one plausible mistake into a copy of the oracle's C source
 (dropped term, wrong sign, wrong index, transposed operand, broken rounding,
 broken stability, a wrong MX scale index, exponent or bias, a dropped clamp,
-term or slope of the clamped activation), builds it, and runs the CPU pin tests against it in a
+term or slope of the clamped activation, an ignored, unsigned or wrongly indexed int8
+token scale), builds it, and runs the CPU pin tests against it in a
 subprocess; the run must fail.  The product path is not involved.
 """
 import os
@@ -36,6 +37,10 @@ MUTATIONS = {
     "act_up_lower_clamp_dropped": ("if (u < -ACT_LIMIT) u = -ACT_LIMIT;", ""),
     "act_plus_one_dropped": ("R(u + 1.0, f64)", "u"),
     "act_alpha_one": ("R((double)ACT_ALPHA * g, f64)", "g"),
+    "int8_scale_ignored": ("((const int8_t*)x)[t * d_h + c] * ((const float*)xs)[t], f64)",
+                           "((const int8_t*)x)[t * d_h + c], f64)"),
+    "int8_read_unsigned": ("((const int8_t*)x)[t * d_h + c]", "((const uint8_t*)x)[t * d_h + c]"),
+    "int8_scale_by_column": ("((const float*)xs)[t], f64)", "((const float*)xs)[c % 8], f64)"),
 }
 
 PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_routing.py", "tests/test_oracle_forward.py",
