@@ -33,8 +33,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused MoE layer p50 µs + TFLOP/s (% MFMA/HBM roofline), 1 MI355X"
 PEAK_HBM_GBS = 8000.0
-PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 5000.0, 3: 5000.0}  # dense MFMA: bf16 (F32ACT runs bf16 MFMA), fp8
-DTYPE = {0: "bf16", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp8_e4m3"}
+# dense MFMA: bf16 (F32ACT and INT8 tokens run bf16 MFMA), fp8
+PEAK_TFLOPS = {0: 2500.0, 1: 2500.0, 2: 5000.0, 3: 5000.0, 4: 2500.0}
+DTYPE = {0: "bf16", 1: "bf16", 2: "fp8_e4m3", 3: "mxfp8_e4m3", 4: "bf16 (int8 tokens)"}
 DEFAULT_CONFIG = "ds_fp8_8192"
 
 
@@ -44,13 +45,15 @@ def gemm1_alg_bytes(w):
     a = w.active_experts()
     fp8 = w.mode in (W.MODE_FP8, W.MODE_MXFP8)
     wb = 1 if fp8 else 2
-    xb = 1 if fp8 else {W.MODE_F32ACT: 4, W.MODE_BF16: 2}[w.mode]
+    xb = 1 if fp8 else {W.MODE_F32ACT: 4, W.MODE_BF16: 2, W.MODE_INT8: 1}[w.mode]
     nv = w.valid_assignments()
     b = a * 2 * w.d_e * w.d_h * wb + w.T * w.d_h * xb + nv * w.d_e * wb
     if w.mode == W.MODE_FP8:  # fp32 scales per 128x128 block (W1), per row per 128 (x, h)
         b += a * (2 * w.d_e // 128) * (w.d_h // 128) * 4 + w.T * (w.d_h // 128) * 4 + nv * (w.d_e // 128) * 4
     if w.mode == W.MODE_MXFP8:  # one E8M0 byte per row per 32 values
         b += a * 2 * w.d_e * (w.d_h // 32) + w.T * (w.d_h // 32) + nv * (w.d_e // 32)
+    if w.mode == W.MODE_INT8:  # one fp32 scale per token
+        b += w.T * 4
     return float(b)
 
 

@@ -70,11 +70,19 @@ extern "C" {
  *  MOE_MODE_MXFP8   x, W1, W2 e4m3 codes with E8M0 scales per 32 values along
  *                   K; out bf16.  The intermediate is requantised per row per
  *                   32 columns (shared exponent floor(log2 amax) - 8, elements
- *                   saturated to +-448). */
+ *                   saturated to +-448).
+ *  MOE_MODE_INT8    x int8 codes with one fp32 scale per token (tokens
+ *                   quantised to int8 and dequantised by GEMM-1: the CUCo
+ *                   page, section 4, DeepSeek-V3 MoE Dispatch and Combine,
+ *                   steps (1) and (3)); W1, W2 bf16; out bf16.  The codes are
+ *                   widened to bf16 exactly, the bf16 GEMMs run on them and
+ *                   each row's fp32 accumulators take its token's scale before
+ *                   the activation; the intermediate is bf16 as in BF16 mode. */
 #define MOE_MODE_F32ACT 0
 #define MOE_MODE_BF16 1
 #define MOE_MODE_FP8 2
 #define MOE_MODE_MXFP8 3
+#define MOE_MODE_INT8 4
 
 /* Storage order of W1 and W2 (moe_dims.weight_layout):
  *  MOE_WEIGHTS_ROW_MAJOR  w1 [E, 2*d_e, d_h], w2 [E, d_h, d_e] as described for
@@ -109,7 +117,8 @@ typedef struct {
 } moe_dims;
 
 /* Scales of the quantised modes (dequantised value = code * scale).  Required
- * in MOE_MODE_FP8 and MOE_MODE_MXFP8, ignored otherwise.
+ * in MOE_MODE_FP8 and MOE_MODE_MXFP8 (all three) and MOE_MODE_INT8 (x_scale
+ * only), ignored otherwise.
  * MOE_MODE_FP8, fp32:
  *  x_scale   [T, d_h/128]                 one scale per token per 128 columns
  *  w1_scale  [E, 2*d_e/128, d_h/128]      one scale per 128x128 block of W1
@@ -118,7 +127,9 @@ typedef struct {
  * makes the rows it scales NaN):
  *  x_scale   [T, d_h/32]                  one byte per token per 32 columns
  *  w1_scale  [E, 2*d_e, d_h/32]           one byte per W1 row per 32 columns
- *  w2_scale  [E, d_h, d_e/32]             one byte per W2 row per 32 columns */
+ *  w2_scale  [E, d_h, d_e/32]             one byte per W2 row per 32 columns
+ * MOE_MODE_INT8, fp32:
+ *  x_scale   [T]                          one scale per token (w1_scale, w2_scale unused) */
 typedef struct {
     const void* x_scale;
     const void* w1_scale;
@@ -142,14 +153,14 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
  *   out[t] = sum_{j<k} topk_w[t,j] * W2[e] . ( silu(W1[e][0:d_e] . x[t]) * (W1[e][d_e:2d_e] . x[t]) ),
  *   e = topk_ids[t,j]  (or the clamped activation in place of silu(g) * u).
  *
- *  x         [T, d_h]            fp32 / bf16 / e4m3 per mode
+ *  x         [T, d_h]            fp32 / bf16 / e4m3 / int8 per mode
  *  topk_ids  [T, k] int32        expert of each assignment p = t*k + j; ids
  *                                outside [0,E) are dropped (contribute 0)
  *  topk_w    [T, k] fp32         routing weights, used as given
  *  w1        [E, 2*d_e, d_h]     rows [0,d_e) gate, [d_e,2*d_e) up; K (d_h) contiguous
  *  w2        [E, d_h, d_e]       K (d_e) contiguous
  *                                (with MOE_WEIGHTS_PACKED: the outputs of moe_pack_weights)
- *  scales    FP8 and MXFP8 modes only (may be NULL otherwise)
+ *  scales    FP8, MXFP8 and INT8 modes only (may be NULL otherwise)
  *  out       [T, d_h]            fp32 (F32ACT) or bf16; every row is written
  *  workspace device buffer of at least moe_workspace_bytes(dims) bytes, 256-byte aligned
  *

@@ -15,7 +15,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool dims_ok(const moe_dims* d) {
     if (!d) return false;
-    if (d->mode < MOE_MODE_F32ACT || d->mode > MOE_MODE_MXFP8) return false;
+    if (d->mode < MOE_MODE_F32ACT || d->mode > MOE_MODE_INT8) return false;
     if (d->num_tokens < 0 || d->num_experts < 1 || d->num_experts > kMaxExperts) return false;
     if (d->top_k < 1 || d->top_k > 8) return false;
     if ((int64_t)d->num_tokens * d->top_k >= ((int64_t)1 << 31)) return false;
@@ -41,7 +41,7 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     const int64_t mtile_cap2 = mtile_cap1;
     L->block_n1 = gemm1_block_n(d->mode);
     L->block_n2 = gemm2_block_n(d->mode);
-    L->max_row_blocks = kMaxRowBlocks1;
+    L->max_row_blocks = gemm1_max_row_blocks(d->mode, N);
     L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
     L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
     const size_t hb = mode_fp8(d->mode) ? 1 : 2;
@@ -72,22 +72,25 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
                                                   : 0);
     L->y = take(yb * N * d->d_hidden);
     L->zero = take(kZeroBytes);
-    // F32ACT: x rounded to bf16 once, then the bf16 GEMMs run on it
-    L->x_bf16 = take(d->mode == MOE_MODE_F32ACT ? 2 * (size_t)d->num_tokens * d->d_hidden : 0);
+    // F32ACT: x rounded to bf16 once; INT8: the codes widened to bf16 (exact);
+    // the bf16 GEMMs then run on it
+    L->x_bf16 = take(d->mode == MOE_MODE_F32ACT || d->mode == MOE_MODE_INT8 ? 2 * (size_t)d->num_tokens * d->d_hidden
+                                                                            : 0);
     L->total = o;
 }
 
 // Per-device cache of the chip size and of the GEMM kernels' occupancy.
+// Slot 4 holds the 8-wave FP8 GEMM-1 (fp8_wide).
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int occ1[4] = {0, 0, 0, 0};
-    int occ2[4] = {0, 0, 0, 0};
+    int occ1[5] = {0, 0, 0, 0, 0};
+    int occ2[5] = {0, 0, 0, 0, 0};
 };
 std::mutex g_mu;
 DeviceInfo g_dev[64];
 
-hipError_t device_info(int mode, int* cus, int* occ1, int* occ2) {
+hipError_t device_info(int mode, bool wide, int* cus, int* occ1, int* occ2) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
@@ -97,8 +100,8 @@ hipError_t device_info(int mode, int* cus, int* occ1, int* occ2) {
     if (!di.ready) {
         err = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        for (int m = 0; m < 4; ++m) {
-            err = gemm_occupancy(m, &di.occ1[m], &di.occ2[m]);
+        for (int m = 0; m < 5; ++m) {
+            err = gemm_occupancy(m < 4 ? m : MOE_MODE_FP8, m == 4, &di.occ1[m], &di.occ2[m]);
             if (err != hipSuccess) return err;
             if (di.occ1[m] < 1) di.occ1[m] = 1;
             if (di.occ2[m] < 1) di.occ2[m] = 1;
@@ -106,8 +109,9 @@ hipError_t device_info(int mode, int* cus, int* occ1, int* occ2) {
         di.ready = true;
     }
     *cus = di.cus;
-    *occ1 = di.occ1[mode];
-    *occ2 = di.occ2[mode];
+    const int slot = wide ? 4 : gemm_mode(mode);
+    *occ1 = di.occ1[slot];
+    *occ2 = di.occ2[slot];
     return hipSuccess;
 }
 
@@ -198,6 +202,7 @@ int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, const int3
     a.E = num_experts;
     route_caps(N, num_experts, &a.n_pad_cap, &a.tile_cap);
     a.nb1 = a.nb2 = 0;
+    a.mb1_max = kMaxRowBlocks1;
     a.full = 1;
     a.counts = out->counts;
     a.offsets = out->offsets;
@@ -219,7 +224,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!dims) return MOE_ERR_INVALID_ARG;
     if (!dims_ok(dims)) {
         // shape fields present but outside the envelope
-        if (dims->mode < 0 || dims->mode > MOE_MODE_MXFP8 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
+        if (dims->mode < 0 || dims->mode > MOE_MODE_INT8 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
             dims->d_hidden <= 0 || dims->d_expert <= 0 ||
             (dims->weight_layout != MOE_WEIGHTS_ROW_MAJOR && dims->weight_layout != MOE_WEIGHTS_PACKED) ||
             (dims->activation != MOE_ACT_SWIGLU && dims->activation != MOE_ACT_SWIGLU_CLAMPED))
@@ -235,6 +240,9 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
         return MOE_ERR_INVALID_ARG;
     if (mode_fp8(mode) && (!scales || !scales->x_scale || !scales->w1_scale || !scales->w2_scale))
         return MOE_ERR_INVALID_ARG;
+    // INT8: one fp32 scale per token (4-byte aligned)
+    if (mode == MOE_MODE_INT8 && (!scales || !scales->x_scale || ((uintptr_t)scales->x_scale & 3)))
+        return MOE_ERR_INVALID_ARG;
     // MXFP8 scale rows are loaded 4 bytes at a time
     if (mode == MOE_MODE_MXFP8 && (((uintptr_t)scales->x_scale | (uintptr_t)scales->w1_scale | (uintptr_t)scales->w2_scale) & 3))
         return MOE_ERR_INVALID_ARG;
@@ -243,7 +251,8 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
 
     int cus = 0, occ1 = 1, occ2 = 1;
-    if (device_info(mode, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
+    const bool wide = fp8_wide(mode, T * dims->top_k);
+    if (device_info(mode, wide, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // timing events of launch i (route, GEMM-1, GEMM-2, combine), or none
     auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
@@ -258,6 +267,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.nb1 = d_e / L.block_n1;
     r.nb2 = d_h / L.block_n2;
     r.min_tasks1 = cus * occ1;
+    r.mb1_max = gemm1_max_row_blocks(mode, T * k);
     r.mb2 = gemm2_row_blocks(mode);
     r.mix1 = mode != MOE_MODE_FP8;
     // GEMM-2's tasks are short: 128-row tiles only when every workgroup slot
@@ -287,6 +297,10 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
         uint16_t* xb = at<uint16_t>(workspace, L.x_bf16);
         if (launch_x_to_bf16(static_cast<const float*>(x), xb, T * d_h, s) != hipSuccess) return MOE_ERR_HIP;
         xg = xb;
+    } else if (mode == MOE_MODE_INT8) {
+        uint16_t* xb = at<uint16_t>(workspace, L.x_bf16);
+        if (launch_i8_to_bf16(static_cast<const int8_t*>(x), xb, T * d_h, s) != hipSuccess) return MOE_ERR_HIP;
+        xg = xb;
     }
 
     Gemm1Args g1{};
@@ -302,12 +316,13 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g1.h_scale = mode_fp8(mode) ? at<unsigned char>(workspace, L.h_scale) : nullptr;
     g1.topk_w = topk_w;
     g1.row_w = at<float>(workspace, L.row_w);
+    g1.x_row_scale = mode == MOE_MODE_INT8 ? static_cast<const float*>(scales->x_scale) : nullptr;
     g1.k = k;
     g1.d_h = d_h;
     g1.d_e = d_e;
     g1.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
     g1.act = dims->activation;
-    if (launch_gemm1(mode, g1, grid1, s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm1(gemm_mode(mode), wide, g1, grid1, s, ev(2), ev(3)) != hipSuccess) return MOE_ERR_HIP;
 
     Gemm2Args g2{};
     g2.h = g1.h;
@@ -323,7 +338,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.d_h = d_h;
     g2.d_e = d_e;
     g2.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
-    if (launch_gemm2(mode, g2, grid2, s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm2(gemm_mode(mode), g2, grid2, s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
 
     CombineArgs c{};
     c.y = g2.y;
@@ -333,7 +348,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     c.k = k;
     c.E = E;
     c.d_h = d_h;
-    if (launch_combine(mode, c, s, ev(6), ev(7)) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_combine(gemm_mode(mode), c, s, ev(6), ev(7)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -47,6 +47,7 @@
 // E8M0 byte of row (or column) r for K values [32g, 32g+32), whichever lanes
 // hold them.  Each stage carries the 4 scale bytes of every A and B row.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -211,26 +212,32 @@ constexpr int kClaimLead = 6;
 // rows of a task rounded up to whole 64-lane loads (the row-index loads fill
 // 64 entries per instruction)
 constexpr int kRowsLds = (kAMaxRows + 63) / 64 * 64;
+// the FP8 GEMM-1 kernel's tasks have up to 256 rows
+constexpr int kRowsLdsFp8G1 = 16 * kMaxRowBlocksFp8G1;
+static_assert(kRowsLdsFp8G1 % 64 == 0, "row-index staging in whole 64-lane loads");
 
-struct QueueLds {
+template <int ROWS>
+struct QueueLdsT {
     int seg[kXcds + 1];  // segment starts (and the end of the last)
     unsigned mask;       // segments found exhausted (scheduler lane 0)
     int slot;            // the task of the next round, -1 when none is left
     int4 task;           // its record {expert, first padded row, row blocks, column block}
     int rec[64];         // landing area of the record load (16 copies)
-    int rows[2][kRowsLds];    // row_src of the task's rows, by round parity
-    float roww[2][kRowsLds];  // GEMM-2: routing weight of the task's rows
+    int rows[2][ROWS];    // row_src of the task's rows, by round parity
+    float roww[2][ROWS];  // GEMM-2: routing weight of the task's rows
 };
+using QueueLds = QueueLdsT<kRowsLds>;
 
 // Scheduler wave state of one round.  claim() runs on lane 0; the other
 // steps on the whole scheduler wave, in order.
-struct Sched {
+template <int ROWS>
+struct SchedT {
     int32_t* ctl;
     int base;
     const int4* tasks;
     const int32_t* row_src;
     const float* row_w;  // GEMM-2 only
-    QueueLds* q;
+    QueueLdsT<ROWS>* q;
     int xcd;
     int x = -1, raw = 0;  // lane 0: segment and result of the atomic sent ahead
     int slot = -1;
@@ -327,7 +334,7 @@ struct Sched {
         const int row0 = __builtin_amdgcn_readfirstlane(q->rec[1]);
         const int n = 16 * __builtin_amdgcn_readfirstlane(q->rec[2]);
 #pragma unroll
-        for (int j = 0; j < kRowsLds / 64; ++j) {
+        for (int j = 0; j < ROWS / 64; ++j) {
             if (64 * j >= n) break;
             const int r = 64 * j + lane < n ? 64 * j + lane : 0;
             g2l4(row_src + row0 + r, lds_offset(&q->rows[par][64 * j]));
@@ -344,6 +351,7 @@ struct Sched {
         }
     }
 };
+using Sched = SchedT<kRowsLds>;
 
 // ------------------------------------------------------------------ configs
 // Stage of the ring for a task of NSUB group blocks: the K block of the
@@ -365,7 +373,7 @@ struct Cfg {
     // MXFP8: the 4 scale bytes of this K block for every A row, then every B row
     static constexpr int kStageS = kBS ? 1024 : kMX ? 4 * (kAMaxRows + kBRows) : 0;
     static constexpr int stage_bytes(int nsub) { return kStageB + 16 * nsub * kRowBytes + kStageS; }
-    // ring: FP8 GEMM-1 (256 weight rows per stage) takes a whole CU's LDS
+    // ring: FP8 / MXFP8 GEMM-1 (256 weight rows per stage) takes a whole CU's LDS
     // (three stages of a 128-row task, four of a 16-row one); the others take
     // four stages of a one-block task, so two workgroups share a CU
     static constexpr int kRing = (GATED && kFP8) ? 160 * 1024 - 2560 : 4 * stage_bytes(1);
@@ -557,6 +565,18 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
             ep_w = p >= 0 ? g1->topk_w[p] : 0.f;
         }
     }
+    // INT8 tokens (bf16 GEMM on the widened codes): each row's token scale,
+    // loaded ahead like the routing weight (waves 0 and 1, one row per lane)
+    // and applied to the gate and up accumulators before the activation
+    float ep_xs = 0.f;
+    bool xs_owner = false;
+    if constexpr (GATED && !kFP8) {
+        xs_owner = g1->x_row_scale && w < 2 && w_row < kRows;
+        if (xs_owner) {
+            const int p = rows[w_row];
+            ep_xs = p >= 0 ? g1->x_row_scale[p / a_div] : 0.f;
+        }
+    }
 
     auto issue = [&](int kc) {
         const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
@@ -734,6 +754,26 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
     lds_barrier();  // every wave is done with the ring
     unsigned char* stage = smem;                                              // [16*NSUB][kEpiRow]
     float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * kAMaxRows);  // [waves][kAMaxRows]
+    if constexpr (GATED && !kFP8) {
+        if (g1->x_row_scale) {  // uniform: INT8 mode
+            // dequantisation: the GEMM ran on the integer codes, so each row's
+            // accumulators take its token's scale (one fp32 multiply each)
+            float* s_xs = s_amax;  // [kAMaxRows], past the staging rows
+            if (xs_owner) s_xs[w_row] = ep_xs;
+            lds_barrier();
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sc = s_xs[16 * s + 4 * lg + i];
+#pragma unroll
+                    for (int f = 0; f < C::kNFW; ++f) {
+                        acc[s][f][0][i] *= sc;
+                        acc[s][f][1][i] *= sc;
+                    }
+                }
+        }
+    }
     if constexpr (GATED) {
         if (w_owner) g1->row_w[row0 + w_row] = ep_w;
         float hv[NSUB][C::kNFW][4];
@@ -978,6 +1018,373 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
     }
 }
 
+// ------------------------------------------------------- FP8 GEMM-1 (8 waves)
+// Block-scaled FP8 GEMM-1 with SwiGLU and the per-row-per-128 requantisation
+// of h, for tasks of up to 16 group blocks (256 rows) by 128 output columns
+// (256 weight rows: 128 gate, 128 up).  Eight waves, two per SIMD: wave
+// (wm, wn) = (w / 4, w % 4) owns output columns [32 wn, 32 wn + 32) (two
+// 16-column fragments, gate and up) of the task's row blocks wm, wm + 2,
+// wm + 4, ...  Each K block of every row block is one 16x16x128 MFMA per
+// fragment from zero, promoted into the fp32 accumulator with (row scale of
+// x) * (block scale of W1) -- one FMA per accumulator element.  With two
+// waves per SIMD the promotion of one wave runs while the other's MFMAs do,
+// so the body needs no software pipelining of its own.
+//
+// A stage (one K block) holds the 256 weight rows (32 KB), the task's token
+// rows (2 KB per group block) and their row scales; 256-row tasks bring in 64
+// KB per 16.8 MFLOP, where 128-row ones bring 48 KB per 8.4: the per-CU rate
+// of direct-to-LDS loads (about 66-74 GB/s with eight issuing waves, measured)
+// bounds this kernel before HBM or the MFMAs do.  Seven waves issue the
+// stage loads; the last one is the scheduler (as in gemm_task) and computes.
+struct G1F8 {
+    static constexpr int kWaves = kGemm1Fp8Waves;
+    static constexpr int kSched = kWaves - 1;
+    static constexpr int kLoaders = kWaves - 1;
+    static constexpr int kStoreThreads = 64 * kSched;
+    static constexpr int kMaxRows = 16 * kMaxRowBlocksFp8G1;
+    static constexpr int kBN = 128;
+    static constexpr int kBRows = 2 * kBN;
+    static constexpr int kBAll = kBRows / 8;                         // B loads per stage
+    static constexpr int kBMax = (kBAll + kLoaders - 1) / kLoaders;  // per loading wave, at most
+    static constexpr int kAMax = (2 * kMaxRowBlocksFp8G1 + kLoaders - 1) / kLoaders;
+    static constexpr int kStageB = kBRows * kRowBytes;
+    // row scales of up to 256 rows (4 B each), then the gate and up block scales
+    static constexpr int kScaleBlk = 4 * kMaxRows;
+    static constexpr int kStageS = kScaleBlk + 16;
+    static constexpr int stage_bytes(int nsub) { return kStageB + 16 * nsub * kRowBytes + kStageS; }
+    static constexpr int kRing = 160 * 1024 - 5 * 1024;
+    static constexpr int stages(int nsub) { return kRing / stage_bytes(nsub) < 8 ? kRing / stage_bytes(nsub) : 8; }
+    static constexpr int kEpiRow = kBN;  // one e4m3 byte per column
+};
+static_assert(G1F8::kEpiRow * G1F8::kMaxRows + 4 * G1F8::kMaxRows * 4 <= G1F8::kRing,
+              "epilogue staging must fit in the ring");
+static_assert(G1F8::stages(kMaxRowBlocksFp8G1) >= 2, "ring too small");
+static_assert(G1F8::stage_bytes(1) % 16 == 0, "stages 16-byte aligned");
+
+// Row blocks of the task that wave row wm computes: wm, wm + 2, ...
+template <int NSUB, int WM>
+struct G1F8Rows {
+    static constexpr int n = WM == 0 ? (NSUB + 1) / 2 : NSUB / 2;
+};
+
+// One K block of the FP8 GEMM-1 for a wave owning NW row blocks
+// (2 i + wm, i < NW): MFMAs of each row block against the wave's four B
+// fragments (two columns x gate/up), each promoted into acc[i].
+template <int NW, int NA>
+__device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_rows_bytes, int wm, int wn, int lr,
+                                            int lg, int swz, v4f (&acc)[NA][2][2]) {
+    if constexpr (NW > 0) {
+        const unsigned char* sb = st;
+        const unsigned char* sa = st + G1F8::kStageB;
+        const float* sc = reinterpret_cast<const float*>(st + G1F8::kStageB + nsub_rows_bytes);
+        const float swg = sc[G1F8::kScaleBlk / 4], swu = sc[G1F8::kScaleBlk / 4 + 1];
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+        v8i Bf[2][2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int brow = 16 * (2 * wn + f) + lr;
+            Bf[f][0] = lds_frag32(sb + brow * kRowBytes, lg, swz);
+            Bf[f][1] = lds_frag32(sb + (G1F8::kBN + brow) * kRowBytes, lg, swz);
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int s = 2 * i + wm;
+            const v8i A = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
+            v4f t[2][2];
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) t[f][g] = mfma_fp8(A, Bf[f][g], zero4);
+            const float4 sx = *reinterpret_cast<const float4*>(sc + 16 * s + 4 * lg);
+            const float sxa[4] = {sx.x, sx.y, sx.z, sx.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pg = sxa[j] * swg, pu = sxa[j] * swu;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    acc[i][f][0][j] += t[f][0][j] * pg;
+                    acc[i][f][1][j] += t[f][1][j] * pu;
+                }
+            }
+            // one row block at a time: the compiler must not hoist the next
+            // blocks' fragments and MFMA results (they would not fit in the
+            // registers two waves per SIMD leave); the other wave on the SIMD
+            // covers the MFMA latency instead
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <int NSUB>
+__device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, int cb, unsigned char* smem,
+                                          SchedT<kRowsLdsFp8G1>& sch, const int* rows, int par) {
+    using C = G1F8;
+    constexpr int S = C::stages(NSUB);
+    constexpr int kStage = C::stage_bytes(NSUB);
+    constexpr int kStageA = 16 * NSUB * kRowBytes;
+    constexpr int kAInstr = 2 * NSUB;  // A loads per stage: 8 rows each
+    constexpr int kRows = 16 * NSUB;
+    constexpr int kScaleChunks = (kRows + 63) / 64;  // row-scale loads: 64 rows each
+    const int K = g.d_h, N_out = g.d_e;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 2, wn = w & 3;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nk = K / 128;
+    const unsigned smem_lds = lds_offset(smem);
+    const int64_t ld_bytes = K;  // bytes per operand row
+    const unsigned char* zero = g.zero;
+    const float* a_scale = static_cast<const float*>(g.x_scale);
+    const float* w_scale = static_cast<const float*>(g.w1_scale);
+    const bool loader = w < C::kLoaders;
+    // vector-memory loads per stage of this wave: B instructions w, w+7, ...,
+    // A instructions the same way, row-scale chunk c by wave (c == 0 ? 0 : c + 1),
+    // the block scales by wave 1
+    const int n_b = loader ? (C::kBAll - 1 - w) / C::kLoaders + 1 : 0;
+    const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / C::kLoaders + 1 : 0;
+    const int my_chunk = w == 0 ? 0 : (w >= 2 ? w - 1 : -1);  // row-scale chunk of this wave, or -1
+    const bool s_rows = my_chunk >= 0 && my_chunk < kScaleChunks;
+    const int n_s = (s_rows ? 1 : 0) + (w == 1 ? 1 : 0);
+    const int loads_per_stage = n_b + n_a + n_s;
+
+    const unsigned char* bsrc[C::kBMax];
+    const int64_t b_step = g.packed ? C::kStageB : kRowBytes;
+#pragma unroll
+    for (int j = 0; j < C::kBMax; ++j) {
+        const int b = w + C::kLoaders * j;  // B instruction: tile rows 8*b .. 8*b+7
+        if (g.packed) {
+            const int64_t tile = (int64_t)e * (N_out / C::kBN) + cb;
+            bsrc[j] = static_cast<const unsigned char*>(g.w1) + tile * nk * C::kStageB + (b * 64 + lane) * 16;
+            continue;
+        }
+        const int r = 8 * b + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        const int64_t wrow = r < C::kBN ? (int64_t)cb * C::kBN + r : (int64_t)N_out + (int64_t)cb * C::kBN + (r - C::kBN);
+        bsrc[j] = static_cast<const unsigned char*>(g.w1) + ((int64_t)e * 2 * N_out + wrow) * ld_bytes + c * 16;
+    }
+    const unsigned char* asrc[C::kAMax];
+    bool apad[C::kAMax];
+#pragma unroll
+    for (int j = 0; j < C::kAMax; ++j) {
+        const int ai = w + C::kLoaders * j;
+        const int r = 8 * ai + (lane >> 3);
+        const int c = (lane & 7) ^ (r & 7);
+        apad[j] = false;
+        asrc[j] = zero;
+        if (loader && ai < kAInstr) {
+            const int p = rows[r];
+            apad[j] = p < 0;
+            asrc[j] = apad[j] ? zero + c * 16 : static_cast<const unsigned char*>(g.x) + (int64_t)(p / g.k) * ld_bytes + c * 16;
+        }
+    }
+    // row scale of tile row 64 * my_chunk + lane (zero row for padding and
+    // past the task's rows: those lanes read zeros and never advance), or in
+    // wave 1 lanes 0 and 1 the gate and up block scales of W1
+    const int kq = K / kQ;
+    const float* ssrc = reinterpret_cast<const float*>(zero);
+    bool sfix = true;
+    if (s_rows) {
+        const int srow = 64 * my_chunk + lane;
+        const int p = srow < kRows ? rows[srow] : -1;
+        if (p >= 0) {
+            ssrc = a_scale + (int64_t)(p / g.k) * kq;
+            sfix = false;
+        }
+    }
+    const float* bsc = reinterpret_cast<const float*>(zero);
+    bool bfix = true;
+    if (w == 1 && lane < 2) {
+        // W1 scales [E][2 d_e/128][d_h/128]: gate block row cb, up block row d_e/128 + cb
+        const int64_t nrb = 2 * (int64_t)N_out / kQ;
+        const int64_t brow = lane == 0 ? cb : N_out / kQ + cb;
+        bsc = w_scale + ((int64_t)e * nrb + brow) * kq;
+        bfix = false;
+    }
+
+    // routing weight of each tile row (column block 0 only; waves 0..3 hold
+    // rows 64 w + lane), stored by padded row for GEMM-2
+    const int w_row = 64 * w + lane;
+    const bool w_owner = cb == 0 && w < 4 && w_row < kRows;
+    float ep_w = 0.f;
+    if (w_owner) {
+        const int p = rows[w_row];
+        ep_w = p >= 0 ? g.topk_w[p] : 0.f;
+    }
+
+    auto issue = [&](int kc) {
+        const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
+        const int64_t koff = (int64_t)kc * kRowBytes;
+        const int64_t boff = (int64_t)kc * b_step;
+        if (!loader) return;
+#pragma unroll
+        for (int j = 0; j < C::kBMax; ++j) {
+            const int b = w + C::kLoaders * j;
+            if (b < C::kBAll) g2l16(bsrc[j] + boff, st + (unsigned)(b * 1024));
+        }
+#pragma unroll
+        for (int j = 0; j < C::kAMax; ++j) {
+            const int ai = w + C::kLoaders * j;
+            if (ai < kAInstr) g2l16(apad[j] ? asrc[j] : asrc[j] + koff, st + (unsigned)(C::kStageB + ai * 1024));
+        }
+        const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
+        if (s_rows) g2l4(sfix ? ssrc : ssrc + kc, ss + (unsigned)(256 * my_chunk));
+        // lanes 0 and 1 only: the other lanes would land past the stage
+        if (w == 1 && lane < 2) g2l4(bfix ? bsc : bsc + kc, ss + (unsigned)C::kScaleBlk);
+    };
+
+    const int swz = lr & 7;
+    const int npro = nk < S - 1 ? nk : S - 1;
+    for (int kc = 0; kc < npro; ++kc) issue(kc);
+    const int claim_at = nk > kClaimLead ? nk - kClaimLead : 0;
+    const int settle_at = nk > kClaimLead - 2 ? nk - (kClaimLead - 2) : 0;
+    const int rows_at = nk > kClaimLead - 4 ? nk - (kClaimLead - 4) : 0;
+    unsigned char* stage = smem;                                               // [kRows][kEpiRow]
+    float* s_amax = reinterpret_cast<float*>(smem + C::kEpiRow * C::kMaxRows);  // [4 wn][kMaxRows]
+
+    // The K loop and the epilogue of a wave row with NW row blocks.  The two
+    // wave rows run their own copy (the branch is uniform per wave), so each
+    // copy keeps its accumulators in fixed registers; both execute the same
+    // sequence of workgroup barriers.
+    auto body = [&](auto nw_c) {
+        constexpr int NW = decltype(nw_c)::value;
+        constexpr int NA = NW > 0 ? NW : 1;
+        v4f acc[NA][2][2];
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int f = 0; f < 2; ++f) acc[i][f][0] = acc[i][f][1] = zero4;
+        for (int kc = 0; kc < nk; ++kc) {
+            if (loader) {
+                const int younger = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
+                wait_vm_le(younger * loads_per_stage);
+            }
+            lds_barrier();
+            if (kc + S - 1 < nk) issue(kc + S - 1);
+            if (w == C::kSched) {
+                if (kc == claim_at && lane == 0) sch.claim();
+                if (kc == settle_at) sch.settle(true);
+                if (kc == rows_at) sch.load_rows(par ^ 1);
+            }
+            g1f8_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
+        }
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+
+        // ---- epilogue: SwiGLU, amax per row over the task's 128 columns
+        // (four waves hold 32 columns each), requantisation, staging, stores
+        lds_barrier();
+        if (w_owner) g.row_w[row0 + w_row] = ep_w;
+        float hv[NA][2][4];
+        const bool clamped = g.act == MOE_ACT_SWIGLU_CLAMPED;
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    hv[i][f][j] = clamped ? clamped_act(acc[i][f][0][j], acc[i][f][1][j])
+                                          : silu_mul(acc[i][f][0][j], acc[i][f][1][j]);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int s = 2 * i + wm;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float m = fmaxf(fabsf(hv[i][0][j]), fabsf(hv[i][1][j]));
+                m = row16_max(m);  // the 16 lanes of a row group hold one tile row
+                if (lr == 0) s_amax[wn * C::kMaxRows + 16 * s + 4 * lg + j] = m;
+            }
+        }
+        lds_barrier();
+        float* hs = static_cast<float*>(g.h_scale);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int s = 2 * i + wm;
+            float4 m = *reinterpret_cast<const float4*>(&s_amax[16 * s + 4 * lg]);
+#pragma unroll
+            for (int ww = 1; ww < 4; ++ww) {
+                const float4 o = *reinterpret_cast<const float4*>(&s_amax[ww * C::kMaxRows + 16 * s + 4 * lg]);
+                m = make_float4(fmaxf(m.x, o.x), fmaxf(m.y, o.y), fmaxf(m.z, o.z), fmaxf(m.w, o.w));
+            }
+            const float am4[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 16 * s + 4 * lg + j;
+                const float am = am4[j];
+                // scale amax/448; values are multiplied by its reciprocal
+                const float sc = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
+                const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
+                const unsigned q2 =
+                    (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][0][j] * inv, hv[i][1][j] * inv, 0, false);
+                stage[rr * C::kEpiRow + 32 * wn + lr] = (unsigned char)(q2 & 0xffu);
+                stage[rr * C::kEpiRow + 32 * wn + 16 + lr] = (unsigned char)((q2 >> 8) & 0xffu);
+                if (wn == 0 && lr == 0) hs[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
+            }
+        }
+        lds_barrier();
+        // h[row0 + r][cb*128 ...]: 128 bytes per row
+        constexpr int kChunks = C::kEpiRow / 16;
+        unsigned char* h = static_cast<unsigned char*>(g.h);
+        if (w != C::kSched)
+            for (int i = threadIdx.x; i < kRows * kChunks; i += C::kStoreThreads) {
+                const int r = i / kChunks, c = i - r * kChunks;
+                *reinterpret_cast<v4i*>(h + (int64_t)(row0 + r) * N_out + (int64_t)cb * C::kEpiRow + c * 16) =
+                    *reinterpret_cast<const v4i*>(stage + r * C::kEpiRow + c * 16);
+            }
+        if (w == C::kSched) sch.publish();
+        lds_barrier();  // the ring and the staging area are refilled by the next task
+    };
+    if (wm == 0)
+        body(std::integral_constant<int, G1F8Rows<NSUB, 0>::n>{});
+    else
+        body(std::integral_constant<int, G1F8Rows<NSUB, 1>::n>{});
+}
+
+__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
+    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+    const int xcd = my_xcd();
+    if (threadIdx.x <= kXcds) q.seg[threadIdx.x] = a.ctl[kCtlSeg1 + threadIdx.x];
+    if (threadIdx.x == 0) q.mask = 0;
+    lds_barrier();
+    if (threadIdx.x >= 64 * G1F8::kSched) {
+        SchedT<kRowsLdsFp8G1> sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
+        sch.first();
+        sch.load_rows(0);
+        sch.publish();
+    }
+    lds_barrier();
+    for (int par = 0;; par ^= 1) {
+        // readfirstlane: the task is uniform, and the compiler must know it
+        // (a task loop it takes as divergent may split a one-thread region
+        // next to the back-edge off the loop)
+        const int t = __builtin_amdgcn_readfirstlane(q.slot);
+        if (t < 0) break;
+        const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
+        const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
+        SchedT<kRowsLdsFp8G1> sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
+#define MOE_G1F8(NS) g1f8_task<NS>(a, e, row0, cb, smem, sch, q.rows[par], par)
+        switch (nsub) {
+            case 1: MOE_G1F8(1); break;
+            case 2: MOE_G1F8(2); break;
+            case 3: MOE_G1F8(3); break;
+            case 4: MOE_G1F8(4); break;
+            case 5: MOE_G1F8(5); break;
+            case 6: MOE_G1F8(6); break;
+            case 7: MOE_G1F8(7); break;
+            case 8: MOE_G1F8(8); break;
+            case 9: MOE_G1F8(9); break;
+            case 10: MOE_G1F8(10); break;
+            case 11: MOE_G1F8(11); break;
+            case 12: MOE_G1F8(12); break;
+            case 13: MOE_G1F8(13); break;
+            case 14: MOE_G1F8(14); break;
+            case 15: MOE_G1F8(15); break;
+            default: MOE_G1F8(16); break;
+        }
+#undef MOE_G1F8
+    }
+}
+
 // ---------------------------------------------------------------- combine
 // out[t, c..c+8) = sum_j y[t*k + j, c..c+8) in ascending j from +0.0, fp32,
 // one final rounding.  Dropped assignments have no y row and are skipped.
@@ -1042,6 +1449,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
 }
 
+// int8 codes -> bf16, exactly (|q| <= 128 has at most 8 significant bits):
+// 16 codes per thread
+__global__ __launch_bounds__(256) void i8_to_bf16_kernel(const int8_t* x, uint16_t* xb, int64_t n16) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n16) return;
+    const int4 v = reinterpret_cast<const int4*>(x)[i];
+    const int wd[4] = {v.x, v.y, v.z, v.w};
+    unsigned o[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const float lo = (float)(int8_t)((wd[j] >> (16 * b)) & 0xff);
+            const float hi = (float)(int8_t)((wd[j] >> (16 * b + 8)) & 0xff);
+            o[2 * j + b] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+        }
+    uint4* dst = reinterpret_cast<uint4*>(xb) + 2 * i;
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
 __global__ __launch_bounds__(256) void x_to_bf16_kernel(const float* x, uint16_t* xb, int64_t n8) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n8) return;
@@ -1093,6 +1521,13 @@ hipError_t launch_pack(const void* w, void* wp, int64_t E, int64_t n_out, int64_
     return hipGetLastError();
 }
 
+hipError_t launch_i8_to_bf16(const int8_t* x, uint16_t* xb, int64_t n, hipStream_t s) {
+    const int64_t n16 = n / 16;
+    if (n16 == 0) return hipSuccess;
+    hipLaunchKernelGGL(i8_to_bf16_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s, x, xb, n16);
+    return hipGetLastError();
+}
+
 hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s) {
     const int64_t n8 = n / 8;
     if (n8 == 0) return hipSuccess;
@@ -1100,9 +1535,12 @@ hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+hipError_t launch_gemm1(int mode, bool wide, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0,
+                        hipEvent_t t1) {
     if (mode == MOE_MODE_MXFP8)
         hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_MXFP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
+    else if (mode == MOE_MODE_FP8 && wide)
+        hipExtLaunchKernelGGL(gemm1_fp8_kernel, dim3(grid), dim3(kGemm1Fp8Threads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_FP8)
         hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else
@@ -1133,13 +1571,14 @@ hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEven
     return hipGetLastError();
 }
 
-hipError_t gemm_occupancy(int mode, int* g1, int* g2) {
+hipError_t gemm_occupancy(int mode, bool wide, int* g1, int* g2) {
     hipError_t e1, e2;
     if (mode == MOE_MODE_MXFP8) {
         e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
     } else if (mode == MOE_MODE_FP8) {
-        e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
+        e1 = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_fp8_kernel, kGemm1Fp8Threads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
     } else if (mode == MOE_MODE_BF16) {
         e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_BF16>, kGemmThreads, 0);

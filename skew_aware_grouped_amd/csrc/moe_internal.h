@@ -24,6 +24,23 @@ constexpr int kMaxRowBlocks1 = 8;
 constexpr int kMaxRowBlocks2 = 8;
 constexpr int kSmallRowBlocks = 4;
 constexpr int kMaxRowBlocks = kMaxRowBlocks1;
+// FP8 GEMM-1 runs its own kernel: 8 waves (two per SIMD, so one wave's
+// block-scale promotion overlaps the other's MFMAs) and tasks of up to 16
+// group blocks (256 rows), so that each weight byte brought into LDS feeds
+// twice the rows: the per-CU rate of direct-to-LDS loads, not HBM, bounds
+// this kernel at large batches.
+constexpr int kMaxRowBlocksFp8G1 = 16;
+constexpr int kGemm1Fp8Waves = 8;
+constexpr int kGemm1Fp8Threads = 64 * kGemm1Fp8Waves;
+// It serves batches of at least kFp8WideMinAssignments routed rows (an
+// average of 256 rows per expert at 32 experts); smaller FP8 batches stream
+// weights and take the 4-wave kernel, whose stage loads and epilogue are
+// shorter per task.
+constexpr int64_t kFp8WideMinAssignments = 8192;
+inline bool fp8_wide(int mode, int64_t n_assign) { return mode == MOE_MODE_FP8 && n_assign >= kFp8WideMinAssignments; }
+inline int gemm1_max_row_blocks(int mode, int64_t n_assign) {
+    return fp8_wide(mode, n_assign) ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
+}
 // Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = 64 * kGemmWaves;
@@ -70,6 +87,8 @@ __host__ __device__ inline int static_tasks(int grid, int x, int seg_len) {
 // block row of W1's scales; bf16 GEMM-1 uses 64; GEMM-2 uses 128 (one W2
 // scale block row).
 inline bool mode_fp8(int mode) { return mode == MOE_MODE_FP8 || mode == MOE_MODE_MXFP8; }  // e4m3 operands
+// The GEMM kernels of a mode: INT8 tokens run the bf16 GEMMs on their widened codes
+inline int gemm_mode(int mode) { return mode == MOE_MODE_INT8 ? MOE_MODE_BF16 : mode; }
 inline int gemm1_block_n(int mode) { return mode_fp8(mode) ? 128 : 64; }
 inline int gemm2_block_n(int) { return 128; }
 inline int gemm2_row_blocks(int mode) { return mode == MOE_MODE_MXFP8 ? kSmallRowBlocks : kMaxRowBlocks2; }
@@ -79,7 +98,8 @@ struct RouteArgs {
     int32_t N, E;
     int64_t n_pad_cap, tile_cap;
     int32_t nb1, nb2;  // column blocks of GEMM-1 / GEMM-2; 0 = do not build task lists
-    int32_t min_tasks1;  // GEMM-1 takes kMaxRowBlocks1-block M-tiles only if that leaves this many tasks
+    int32_t min_tasks1;  // GEMM-1 takes its largest M-tiles only if that leaves this many tasks
+    int32_t mb1_max;     // largest GEMM-1 M-tile in group blocks (gemm1_max_row_blocks)
     int32_t mb2;         // largest GEMM-2 M-tile in group blocks (gemm2_row_blocks)
     int32_t min_tasks2;  // GEMM-2 takes 8-block M-tiles only if that leaves this many tasks
     int32_t mix1;        // GEMM-1 may mix 8- and 4-block M-tiles (not in FP8 mode, whose 128-row epilogue is long)
@@ -105,6 +125,7 @@ struct Gemm1Args {
     void* h_scale;  // FP8: fp32 [n_pad, d_e/128]; MXFP8: E8M0 bytes [n_pad, d_e/32]
     const float* topk_w;  // [T*k] routing weights
     float* row_w;         // [n_pad] routing weight of each padded row (0 on padding), written by column block 0
+    const float* x_row_scale;  // INT8 mode: fp32 [T], one per token, applied to GEMM-1's accumulators; else null
     int32_t k, d_h, d_e;
     int32_t packed;  // W1 in the packed tile order
     int32_t act;     // MOE_ACT_*
@@ -137,17 +158,21 @@ struct CombineArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 // x fp32 -> bf16 (round to nearest even), n elements, multiple of 8
 hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t s);
+// int8 codes -> bf16 (exact), n elements, multiple of 16
+hipError_t launch_i8_to_bf16(const int8_t* x, uint16_t* xb, int64_t n, hipStream_t s);
 // W (row-major [E][rows][K bytes]) -> packed tile order for tasks of `bn`
 // output columns (gated: gate and up rows of a column block together)
 hipError_t launch_pack(const void* w, void* wp, int64_t E, int64_t n_out, int64_t k_bytes, int bn, bool gated,
                        hipStream_t s);
-hipError_t launch_gemm1(int mode, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
+// wide: FP8 only, the 8-wave kernel (fp8_wide)
+hipError_t launch_gemm1(int mode, bool wide, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
 hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
 hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);
-// Resident workgroups per CU of the persistent GEMM kernels (occupancy query).
-hipError_t gemm_occupancy(int mode, int* g1_blocks_per_cu, int* g2_blocks_per_cu);
+// Resident workgroups per CU of the persistent GEMM kernels (occupancy query;
+// wide: the 8-wave FP8 GEMM-1).
+hipError_t gemm_occupancy(int mode, bool wide, int* g1_blocks_per_cu, int* g2_blocks_per_cu);
 
 }  // namespace moe

@@ -288,14 +288,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     // M-tiles of 8 group blocks (fewer weight re-reads) when that still leaves
     // min_tasks1 (min_tasks2) tasks, otherwise kSmallRowBlocks (more tasks to
-    // spread over the CUs); the last wave decides for both lists after its
-    // share of the ranking
+    // spread over the CUs); FP8 GEMM-1 (mb1_max 16) takes 16-block M-tiles
+    // when those still leave min_tasks1 tasks.  The last wave decides for both
+    // lists after its share of the ranking
     if (wave == kRouteWaves - 1) {
-        int big = 0;
-        for (int e = lane; e < E; e += 64) big += (s_tiles[e] + 7) >> 3;
+        int big = 0, big16 = 0;
+        for (int e = lane; e < E; e += 64) {
+            big += (s_tiles[e] + 7) >> 3;
+            big16 += (s_tiles[e] + 15) >> 4;
+        }
         big = __builtin_amdgcn_readlane(wave_inclusive_scan(big, lane), 63);
+        big16 = __builtin_amdgcn_readlane(wave_inclusive_scan(big16, lane), 63);
         if (lane == 0) {
-            s_mb1 = big * a.nb1 >= a.min_tasks1 ? kMaxRowBlocks1 : kSmallRowBlocks;
+            s_mb1 = a.mb1_max == 16 && big16 * a.nb1 >= a.min_tasks1 ? 16
+                    : big * a.nb1 >= a.min_tasks1                   ? kMaxRowBlocks1
+                                                                    : kSmallRowBlocks;
             s_mb2 = a.mb2 == 8 && big * a.nb2 >= a.min_tasks2 ? 8 : kSmallRowBlocks;
         }
     }
@@ -303,7 +310,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int mb1 = s_mb1, mb2 = s_mb2;
     // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2); the
     // M-tile sizes are powers of two
-    static_assert(kMaxRowBlocks1 == 8 && kMaxRowBlocks2 == 8 && kSmallRowBlocks == 4, "M-tile sizes 8 and 4 group blocks");
+    static_assert(kMaxRowBlocks1 == 8 && kMaxRowBlocks2 == 8 && kSmallRowBlocks == 4 && kMaxRowBlocksFp8G1 == 16,
+                  "M-tile sizes 16, 8 and 4 group blocks");
     // When 8-block GEMM-1 tiles leave workgroup slots idle but 4-block tiles
     // make more tasks than slots (a second, partial round), the hottest ranks
     // [0, r8) keep 8-block tiles: the fewest that bring the task count down to
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // mode (mix1 = 0), where a 128-row task's epilogue costs more than the
     // partial round it saves.
     int r8 = mb1 == 8 ? E : 0;
-    if (mb1 != 8 && a.mix1) {
+    if (mb1 == kSmallRowBlocks && a.mix1) {
         int t4 = 0, d8[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -336,10 +344,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
     }
     // group blocks per GEMM-1 M-tile of rank r
-    auto mb1_of = [&](int r) { return r < r8 ? 8 : kSmallRowBlocks; };
+    auto lg1 = [&](int r) { return mb1 == 16 ? 4 : r < r8 ? 3 : 2; };
+    auto mb1_of = [&](int r) { return 1 << lg1(r); };
     const int lg_mb2 = mb2 == 8 ? 3 : 2;
     auto mtiles = [&](int list, int r) {
-        const int lg = list == 0 ? (r < r8 ? 3 : 2) : lg_mb2;
+        const int lg = list == 0 ? lg1(r) : lg_mb2;
         return (s_rtiles[r] + (1 << lg) - 1) >> lg;
     };
     {

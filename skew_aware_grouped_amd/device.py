@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import moe
-from .workloads import MODE_BF16, MODE_F32ACT, MODE_FP8, MODE_MXFP8, MoEWorkload
+from .workloads import MODE_BF16, MODE_F32ACT, MODE_FP8, MODE_INT8, MODE_MXFP8, MoEWorkload
 
 
 def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
@@ -22,6 +22,8 @@ def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
         d["x"] = t(w.x)
     elif w.mode == MODE_BF16:
         d["x"] = t(w.x.view(np.int16), torch.bfloat16)
+    elif w.mode == MODE_INT8:
+        d["x"] = t(w.x.astype(np.int8))
     else:
         d["x"] = t(w.x, torch.float8_e4m3fn)
     if w.mode in (MODE_FP8, MODE_MXFP8):  # fp32 block scales or uint8 E8M0 scales
@@ -34,6 +36,8 @@ def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
         d["w1"] = t(w.w1.view(np.int16), torch.bfloat16)
         d["w2"] = t(w.w2.view(np.int16), torch.bfloat16)
         d["x_scale"] = d["w1_scale"] = d["w2_scale"] = None
+        if w.mode == MODE_INT8:  # one fp32 scale per token
+            d["x_scale"] = t(w.x_scale.astype(np.float32))
     d["topk_ids"] = t(w.topk_ids.astype(np.int32))
     d["topk_w"] = t(w.topk_w.astype(np.float32))
     d["weight_layout"] = moe.MOE_WEIGHTS_ROW_MAJOR

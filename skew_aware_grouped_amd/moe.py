@@ -29,6 +29,7 @@ MOE_MODE_F32ACT = 0
 MOE_MODE_BF16 = 1
 MOE_MODE_FP8 = 2
 MOE_MODE_MXFP8 = 3
+MOE_MODE_INT8 = 4
 
 MOE_WEIGHTS_ROW_MAJOR = 0
 MOE_WEIGHTS_PACKED = 1
@@ -178,8 +179,11 @@ def _stream_ptr(stream=None):
 
 
 def _mode_of(x, w1, x_scale=None):
-    """e4m3 weights: MXFP8 when the scales are E8M0 bytes (uint8), else FP8."""
+    """e4m3 weights: MXFP8 when the scales are E8M0 bytes (uint8), else FP8;
+    int8 tokens: INT8."""
     import torch
+    if x.dtype == torch.int8:
+        return MOE_MODE_INT8
     if w1.dtype in (torch.float8_e4m3fn, torch.uint8):
         return MOE_MODE_MXFP8 if x_scale is not None and x_scale.dtype == torch.uint8 else MOE_MODE_FP8
     if x.dtype == torch.float32:
@@ -250,7 +254,8 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     GEMM-2 and combine kernels) the kernel-timing variant is used.  With
     ``weight_layout=MOE_WEIGHTS_PACKED``, w1 and w2 are ``pack_weights`` outputs.
     e4m3 weights take fp32 block scales (FP8 mode) or uint8 E8M0 scales per 32
-    values (MXFP8 mode); the dtype of ``x_scale`` selects the mode."""
+    values (MXFP8 mode); the dtype of ``x_scale`` selects the mode.  int8 ``x``
+    (INT8 mode) takes bf16 weights and one fp32 ``x_scale`` per token."""
     import torch
     dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout, x_scale=x_scale, activation=activation)
     if out is None:
@@ -262,7 +267,12 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     if topk_ids.dtype != torch.int32 or topk_w.dtype != torch.float32:
         raise ValueError("topk_ids must be int32 and topk_w float32")
     scales = None
-    if dims.mode in (MOE_MODE_FP8, MOE_MODE_MXFP8):
+    if dims.mode == MOE_MODE_INT8:
+        if x_scale is None or not (x_scale.is_cuda and x_scale.is_contiguous()) or x_scale.dtype != torch.float32 \
+                or x_scale.numel() != x.shape[0]:
+            raise ValueError("x_scale must be a contiguous float32 device tensor with one scale per token")
+        scales = moe_scales(x_scale.data_ptr(), None, None)
+    elif dims.mode in (MOE_MODE_FP8, MOE_MODE_MXFP8):
         sdt = torch.uint8 if dims.mode == MOE_MODE_MXFP8 else torch.float32
         for name, t in (("x_scale", x_scale), ("w1_scale", w1_scale), ("w2_scale", w2_scale)):
             if t is None or not (t.is_cuda and t.is_contiguous()) or t.dtype != sdt:

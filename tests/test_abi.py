@@ -30,7 +30,7 @@ def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048, layout=m
 
 
 def test_workspace_layout_is_disjoint_and_aligned():
-    for mode in (0, 1, 2, 3):
+    for mode in (0, 1, 2, 3, 4):
         d = _dims(mode=mode)
         L = moe.moe_workspace_layout(d)
         offs = [L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.row_w, L.tile_expert,
@@ -46,7 +46,7 @@ def test_invalid_dims_rejected():
     assert moe.moe_workspace_bytes(_dims(d_h=100)) == 0
     assert moe.moe_workspace_bytes(_dims(E=0)) == 0
     assert moe.moe_workspace_bytes(_dims(k=9)) == 0
-    assert moe.moe_workspace_bytes(_dims(mode=4)) == 0
+    assert moe.moe_workspace_bytes(_dims(mode=5)) == 0
     assert moe.moe_workspace_bytes(_dims(mode=-1)) == 0
     assert moe.moe_workspace_bytes(_dims(layout=2)) == 0
     assert moe.moe_workspace_bytes(_dims(layout=moe.MOE_WEIGHTS_PACKED)) == moe.moe_workspace_bytes(_dims())

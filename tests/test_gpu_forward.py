@@ -18,7 +18,7 @@ from skew_aware_grouped_amd import device, moe, workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {W.MODE_F32ACT: 1e-2, W.MODE_BF16: 1e-2, W.MODE_FP8: 3e-2, W.MODE_MXFP8: 3e-2}
+TOL = {W.MODE_F32ACT: 1e-2, W.MODE_BF16: 1e-2, W.MODE_FP8: 3e-2, W.MODE_MXFP8: 3e-2, W.MODE_INT8: 1e-2}
 FP8_MODES = (W.MODE_FP8, W.MODE_MXFP8)
 
 
@@ -96,7 +96,7 @@ def _check(w, oracle, rows=None, label="", packed=False):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_small_shapes_full_parity(oracle, mode, packed):
     """Several tiles in every direction with ragged expert groups."""
     w = W.custom(200, 8, 3, 384, 256, mode, seed=21)
@@ -104,7 +104,7 @@ def test_small_shapes_full_parity(oracle, mode, packed):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_small_shapes_d_expert_384(oracle, mode, packed):
     """d_e = 384: three FP8 / six bf16 GEMM-1 column blocks, ragged expert
     groups up to several M-tiles."""
@@ -113,7 +113,7 @@ def test_small_shapes_d_expert_384(oracle, mode, packed):
 
 
 @pytest.mark.parametrize("packed", [False, True])
-@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_clamped_activation_small_shapes(oracle, mode, packed):
     """The clamped activation on widened inputs (x scaled by 4: about a tenth
     of the gate and up values lie beyond the clamp), ragged expert groups."""
@@ -135,7 +135,7 @@ def test_workload_full_parity(oracle, name):
 
 
 @pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_128", "ds_fp8_256", "ds_fp8_512", "ds_fp8_1024", "ds_fp8_8192",
-                                  "qwen_mxfp8", "ds_mxfp8_1024", "ds_mxfp8_8192"])
+                                  "qwen_mxfp8", "ds_mxfp8_1024", "ds_mxfp8_8192", "qwen_int8", "ds_int8_1024"])
 def test_workload_sampled_parity(oracle, name):
     """Full-size workloads on packed weights (the layout bench.py times; the
     row-major layout is bitwise equal, tested below)."""
@@ -144,7 +144,7 @@ def test_workload_sampled_parity(oracle, name):
     _check(w, oracle, rows=_sample_rows(w), label=name, packed=True)
 
 
-@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_large_batch_routing_path(oracle, mode):
     """T*k = 18000 assignments, above the 16384 the routing kernel keeps in
     LDS: the ids are read twice and row_src is scattered straight to memory,
@@ -171,7 +171,7 @@ def test_more_m_tiles_than_rank_table(oracle):
     _check(w, oracle, rows=_sample_rows(w, n=64), label="m_tiles_8k")
 
 
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_determinism_two_launches_and_streams(mode):
     import torch
     w = W.custom(300, 16, 2, 512, 256, mode, seed=5, routing=("zipf", 1.2, 3))
@@ -212,7 +212,7 @@ EDGE_CASES = {
 
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("case", sorted(EDGE_CASES))
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_edge_cases(oracle, case, mode, packed):
     c = EDGE_CASES[case]
     rng = np.random.default_rng(9)
@@ -268,7 +268,7 @@ def test_pack_weights_is_the_stated_permutation(mode, d_e):
 
 
 @pytest.mark.parametrize("name", ["tiny", "qwen_bf16", "qwen_fp8", "ds_fp8_128", "ds_fp8_1024", "ds_fp8_8192",
-                                  "qwen_mxfp8", "ds_mxfp8_1024"])
+                                  "qwen_mxfp8", "ds_mxfp8_1024", "qwen_int8"])
 def test_packed_weights_bitwise_equal_row_major(name):
     """The packed layout changes where the GEMMs read each weight tile from,
     not what they compute: the output is bitwise the row-major one."""
@@ -313,7 +313,8 @@ def test_empty_batch_is_noop():
     assert out.shape == (0, 256)
 
 
-@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024", "qwen_bf16", "ds_mxfp8_1024", "qwen_mxfp8"])
+@pytest.mark.parametrize("name", ["qwen_fp8", "ds_fp8_1024", "qwen_bf16", "ds_mxfp8_1024", "qwen_mxfp8", "qwen_int8",
+                                  "ds_fp8_8192"])
 def test_forward_routing_and_task_list(oracle, name):
     """The workspace after a forward call holds the oracle's counts, padded
     permutation (row_src) and routing weight per padded row, and task lists that

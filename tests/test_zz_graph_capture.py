@@ -20,7 +20,7 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_graph_replays_match_eager(mode):
     shape = (200, 8, 2, 256, 256)
     d = device.upload(W.custom(*shape, mode, seed=31))

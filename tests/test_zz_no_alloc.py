@@ -19,6 +19,8 @@ def _args(d, out, mode):
     scales = None
     if mode in (W.MODE_FP8, W.MODE_MXFP8):
         scales = moe.moe_scales(d["x_scale"].data_ptr(), d["w1_scale"].data_ptr(), d["w2_scale"].data_ptr())
+    elif mode == W.MODE_INT8:
+        scales = moe.moe_scales(d["x_scale"].data_ptr(), None, None)
     return dims, (d["x"].data_ptr(), d["topk_ids"].data_ptr(), d["topk_w"].data_ptr(), d["w1"].data_ptr(),
                   d["w2"].data_ptr(), scales, out.data_ptr())
 
@@ -27,7 +29,7 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8])
+@pytest.mark.parametrize("mode", [W.MODE_F32ACT, W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
 def test_noalloc_matches_workspace_entry_point(mode):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
