@@ -41,7 +41,7 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     const int64_t mtile_cap2 = mtile_cap1;
     L->block_n1 = gemm1_block_n(d->mode);
     L->block_n2 = gemm2_block_n(d->mode);
-    L->max_row_blocks = gemm1_max_row_blocks(d->mode, N);
+    L->max_row_blocks = gemm1_max_row_blocks(d->mode, d->num_tokens, d->top_k, d->d_hidden, d->d_expert);
     L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
     L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
     const size_t hb = mode_fp8(d->mode) ? 1 : 2;
@@ -251,7 +251,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
 
     int cus = 0, occ1 = 1, occ2 = 1;
-    const bool wide = fp8_wide(mode, T * dims->top_k);
+    const bool wide = fp8_wide(mode, T, dims->top_k, dims->d_hidden, dims->d_expert);
     if (device_info(mode, wide, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
     hipStream_t s = static_cast<hipStream_t>(stream);
     // timing events of launch i (route, GEMM-1, GEMM-2, combine), or none
@@ -267,7 +267,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.nb1 = d_e / L.block_n1;
     r.nb2 = d_h / L.block_n2;
     r.min_tasks1 = cus * occ1;
-    r.mb1_max = gemm1_max_row_blocks(mode, T * k);
+    r.mb1_max = wide ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
     r.mb2 = gemm2_row_blocks(mode);
     r.mix1 = mode != MOE_MODE_FP8;
     // GEMM-2's tasks are short: 128-row tiles only when every workgroup slot

@@ -159,6 +159,16 @@ __device__ __forceinline__ void g2l4(const void* g, unsigned lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
 }
 __device__ __forceinline__ unsigned lds_offset(const void* p) { return (unsigned)(uintptr_t)p; }
+// The same loads from a uniform (SGPR) base plus a 32-bit per-lane offset:
+// one VGPR per address instead of two.
+__device__ __forceinline__ void g2l16s(const void* base, unsigned off, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void g2l4s(const void* base, unsigned off, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(off), "s"(base)
+                 : "memory", "m0");
+}
 
 // Workgroup barrier for LDS hand-offs (stages of the ring, the epilogue's
 // staging, the task queue state): this wave's LDS accesses are complete
@@ -1069,7 +1079,11 @@ struct G1F8Rows {
 
 // One K block of the FP8 GEMM-1 for a wave owning NW row blocks
 // (2 i + wm, i < NW): MFMAs of each row block against the wave's four B
-// fragments (two columns x gate/up), each promoted into acc[i].
+// fragments (two columns x gate/up), each promoted into acc[i].  The A
+// fragment and row scales of block i + 1 are read from LDS while block i's
+// MFMAs run; the promotion then waits for block i's results, during which
+// the other wave on the SIMD issues its MFMAs (registers do not allow a
+// second set of MFMA results in flight).
 template <int NW, int NA>
 __device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_rows_bytes, int wm, int wn, int lr,
                                             int lg, int swz, v4f (&acc)[NA][2][2]) {
@@ -1086,16 +1100,23 @@ __device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_ro
             Bf[f][0] = lds_frag32(sb + brow * kRowBytes, lg, swz);
             Bf[f][1] = lds_frag32(sb + (G1F8::kBN + brow) * kRowBytes, lg, swz);
         }
+        v8i A = lds_frag32(sa + (16 * wm + lr) * kRowBytes, lg, swz);
+        float4 sx = *reinterpret_cast<const float4*>(sc + 16 * wm + 4 * lg);
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int s = 2 * i + wm;
-            const v8i A = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
             v4f t[2][2];
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
                 for (int g = 0; g < 2; ++g) t[f][g] = mfma_fp8(A, Bf[f][g], zero4);
-            const float4 sx = *reinterpret_cast<const float4*>(sc + 16 * s + 4 * lg);
+            v8i An = A;
+            float4 sxn = sx;
+            if (i + 1 < NW) {
+                const int s = 2 * (i + 1) + wm;
+                An = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
+                sxn = *reinterpret_cast<const float4*>(sc + 16 * s + 4 * lg);
+            }
+            __builtin_amdgcn_sched_barrier(0);
             const float sxa[4] = {sx.x, sx.y, sx.z, sx.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -1106,11 +1127,9 @@ __device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_ro
                     acc[i][f][1][j] += t[f][1][j] * pu;
                 }
             }
-            // one row block at a time: the compiler must not hoist the next
-            // blocks' fragments and MFMA results (they would not fit in the
-            // registers two waves per SIMD leave); the other wave on the SIMD
-            // covers the MFMA latency instead
             __builtin_amdgcn_sched_barrier(0);
+            A = An;
+            sx = sxn;
         }
     }
 }
@@ -1133,7 +1152,6 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
     const int nk = K / 128;
     const unsigned smem_lds = lds_offset(smem);
     const int64_t ld_bytes = K;  // bytes per operand row
-    const unsigned char* zero = g.zero;
     const float* a_scale = static_cast<const float*>(g.x_scale);
     const float* w_scale = static_cast<const float*>(g.w1_scale);
     const bool loader = w < C::kLoaders;
@@ -1147,58 +1165,63 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
     const int n_s = (s_rows ? 1 : 0) + (w == 1 ? 1 : 0);
     const int loads_per_stage = n_b + n_a + n_s;
 
-    const unsigned char* bsrc[C::kBMax];
-    const int64_t b_step = g.packed ? C::kStageB : kRowBytes;
+    // Addresses: uniform bases (the task's weight tile or expert, x, the
+    // scale arrays) plus 32-bit per-lane offsets, so each load costs one VGPR
+    // (the host sends tensors whose offsets could pass 2^31 to the 4-wave
+    // kernel).  Padding rows read token row 0 (their results are never used:
+    // rows are independent in every step, and GEMM-2 stores no padding row).
+    const unsigned char* wbase;
+    unsigned b_step;
+    if (g.packed) {
+        const int64_t tile = (int64_t)e * (N_out / C::kBN) + cb;
+        wbase = static_cast<const unsigned char*>(g.w1) + tile * nk * C::kStageB;
+        b_step = C::kStageB;
+    } else {
+        wbase = static_cast<const unsigned char*>(g.w1) + (int64_t)e * 2 * N_out * ld_bytes;
+        b_step = kRowBytes;
+    }
+    unsigned boff[C::kBMax];
 #pragma unroll
     for (int j = 0; j < C::kBMax; ++j) {
         const int b = w + C::kLoaders * j;  // B instruction: tile rows 8*b .. 8*b+7
         if (g.packed) {
-            const int64_t tile = (int64_t)e * (N_out / C::kBN) + cb;
-            bsrc[j] = static_cast<const unsigned char*>(g.w1) + tile * nk * C::kStageB + (b * 64 + lane) * 16;
-            continue;
+            boff[j] = (unsigned)((b * 64 + lane) * 16);
+        } else {
+            const int r = 8 * b + (lane >> 3);
+            const int c = (lane & 7) ^ (r & 7);
+            const int wrow = r < C::kBN ? cb * C::kBN + r : N_out + cb * C::kBN + (r - C::kBN);
+            boff[j] = (unsigned)wrow * (unsigned)ld_bytes + (unsigned)(c * 16);
         }
-        const int r = 8 * b + (lane >> 3);
-        const int c = (lane & 7) ^ (r & 7);
-        const int64_t wrow = r < C::kBN ? (int64_t)cb * C::kBN + r : (int64_t)N_out + (int64_t)cb * C::kBN + (r - C::kBN);
-        bsrc[j] = static_cast<const unsigned char*>(g.w1) + ((int64_t)e * 2 * N_out + wrow) * ld_bytes + c * 16;
     }
-    const unsigned char* asrc[C::kAMax];
-    bool apad[C::kAMax];
+    const unsigned char* xbase = static_cast<const unsigned char*>(g.x);
+    unsigned aoff[C::kAMax];
 #pragma unroll
     for (int j = 0; j < C::kAMax; ++j) {
         const int ai = w + C::kLoaders * j;
         const int r = 8 * ai + (lane >> 3);
         const int c = (lane & 7) ^ (r & 7);
-        apad[j] = false;
-        asrc[j] = zero;
+        aoff[j] = 0;
         if (loader && ai < kAInstr) {
             const int p = rows[r];
-            apad[j] = p < 0;
-            asrc[j] = apad[j] ? zero + c * 16 : static_cast<const unsigned char*>(g.x) + (int64_t)(p / g.k) * ld_bytes + c * 16;
+            aoff[j] = (unsigned)(p >= 0 ? p / g.k : 0) * (unsigned)ld_bytes + (unsigned)(c * 16);
         }
     }
-    // row scale of tile row 64 * my_chunk + lane (zero row for padding and
-    // past the task's rows: those lanes read zeros and never advance), or in
-    // wave 1 lanes 0 and 1 the gate and up block scales of W1
+    // row scale of tile row 64 * my_chunk + lane (row 0's past the task's rows
+    // and on padding rows), or in wave 1 lanes 0 and 1 the gate and up block
+    // scales of W1; byte offsets
     const int kq = K / kQ;
-    const float* ssrc = reinterpret_cast<const float*>(zero);
-    bool sfix = true;
+    unsigned soff = 0;
     if (s_rows) {
         const int srow = 64 * my_chunk + lane;
         const int p = srow < kRows ? rows[srow] : -1;
-        if (p >= 0) {
-            ssrc = a_scale + (int64_t)(p / g.k) * kq;
-            sfix = false;
-        }
+        soff = (unsigned)(p >= 0 ? p / g.k : 0) * (unsigned)(4 * kq);
     }
-    const float* bsc = reinterpret_cast<const float*>(zero);
-    bool bfix = true;
+    unsigned bsoff = 0;
     if (w == 1 && lane < 2) {
         // W1 scales [E][2 d_e/128][d_h/128]: gate block row cb, up block row d_e/128 + cb
-        const int64_t nrb = 2 * (int64_t)N_out / kQ;
-        const int64_t brow = lane == 0 ? cb : N_out / kQ + cb;
-        bsc = w_scale + ((int64_t)e * nrb + brow) * kq;
-        bfix = false;
+        const int nrb = 2 * N_out / kQ;
+        const int brow = lane == 0 ? cb : N_out / kQ + cb;
+        bsoff = (unsigned)((e * nrb + brow) * kq) * 4u;
     }
 
     // routing weight of each tile row (column block 0 only; waves 0..3 hold
@@ -1213,23 +1236,23 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
 
     auto issue = [&](int kc) {
         const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
-        const int64_t koff = (int64_t)kc * kRowBytes;
-        const int64_t boff = (int64_t)kc * b_step;
+        const unsigned koff = (unsigned)kc * kRowBytes;
+        const unsigned kboff = (unsigned)kc * b_step;
         if (!loader) return;
 #pragma unroll
         for (int j = 0; j < C::kBMax; ++j) {
             const int b = w + C::kLoaders * j;
-            if (b < C::kBAll) g2l16(bsrc[j] + boff, st + (unsigned)(b * 1024));
+            if (b < C::kBAll) g2l16s(wbase, boff[j] + kboff, st + (unsigned)(b * 1024));
         }
 #pragma unroll
         for (int j = 0; j < C::kAMax; ++j) {
             const int ai = w + C::kLoaders * j;
-            if (ai < kAInstr) g2l16(apad[j] ? asrc[j] : asrc[j] + koff, st + (unsigned)(C::kStageB + ai * 1024));
+            if (ai < kAInstr) g2l16s(xbase, aoff[j] + koff, st + (unsigned)(C::kStageB + ai * 1024));
         }
         const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
-        if (s_rows) g2l4(sfix ? ssrc : ssrc + kc, ss + (unsigned)(256 * my_chunk));
+        if (s_rows) g2l4s(a_scale, soff + 4u * (unsigned)kc, ss + (unsigned)(256 * my_chunk));
         // lanes 0 and 1 only: the other lanes would land past the stage
-        if (w == 1 && lane < 2) g2l4(bfix ? bsc : bsc + kc, ss + (unsigned)C::kScaleBlk);
+        if (w == 1 && lane < 2) g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)C::kScaleBlk);
     };
 
     const int swz = lr & 7;

@@ -36,10 +36,15 @@ constexpr int kGemm1Fp8Threads = 64 * kGemm1Fp8Waves;
 // average of 256 rows per expert at 32 experts); smaller FP8 batches stream
 // weights and take the 4-wave kernel, whose stage loads and epilogue are
 // shorter per task.
+// The 8-wave kernel addresses x, one expert's W1 and the scales with 32-bit
+// offsets from uniform bases, so it also needs T*d_h and 2*d_e*d_h below 2^31.
 constexpr int64_t kFp8WideMinAssignments = 8192;
-inline bool fp8_wide(int mode, int64_t n_assign) { return mode == MOE_MODE_FP8 && n_assign >= kFp8WideMinAssignments; }
-inline int gemm1_max_row_blocks(int mode, int64_t n_assign) {
-    return fp8_wide(mode, n_assign) ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
+inline bool fp8_wide(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
+    return mode == MOE_MODE_FP8 && T * k >= kFp8WideMinAssignments && T * d_h < ((int64_t)1 << 31) &&
+           2 * d_e * d_h < ((int64_t)1 << 31);
+}
+inline int gemm1_max_row_blocks(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
+    return fp8_wide(mode, T, k, d_h, d_e) ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
 }
 // Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.
 constexpr int kGemmWaves = 4;
