@@ -423,3 +423,144 @@ int moe_oracle_route(const int32_t* ids, int64_t N, int E, int bm, int32_t* coun
     free(seen);
     return ORACLE_OK;
 }
+
+/*
+ * Backward pass of the layer with recompute (the pages' MoE megakernel serves
+ * forward, backward and recompute passes from the same components: PipeLink
+ * section 5.3; the derivative itself is the chain rule of the forward above).
+ * BF16 mode only (x, W1, W2 and dout bf16).  Nothing of the forward is kept:
+ * g, u and the intermediate are recomputed from x and W1.
+ *
+ * For each valid assignment p = t*k + j (e = ids[p], w = topk_w[p]), in fp32:
+ *   g_r, u_r, a_r = silu(g_r) u_r as in the forward, h_r = a_r rounded to bf16
+ *     (with ORACLE_MIRROR_H, as the forward stores it; else h_r = a_r)
+ *   q_r   = sum_n dout[t][n] W2[e][n][r]                (n ascending)
+ *   dtopk_w[p] = sum_r q_r h_r                           (r ascending)
+ *   dh_r  = w q_r
+ *   dg_r  = dh_r u_r silu'(g_r),  du_r = dh_r silu(g_r),
+ *     silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g))
+ *   dx[t][c]       += sum_r dg_r W1[e][r][c] + du_r W1[e][d_e + r][c]
+ *   dW1[e][r][c]   += dg_r x[t][c],  dW1[e][d_e + r][c] += du_r x[t][c]
+ *   dW2[e][n][r]   += (w dout[t][n]) h_r
+ * With ORACLE_MIRROR_H the rounding points of the method are mirrored: dg and
+ * du are rounded to bf16 before they enter dx and dW1, and w dout[t][n] is
+ * rounded to bf16 before it enters dW2 (the backward GEMMs take bf16
+ * operands).  Accumulation orders: dx per token over its slots in ascending
+ * j (and within one slot r ascending, gate before up); dW1 and dW2 over the
+ * assignments of an expert in ascending p.  Dropped ids contribute nothing and
+ * get dtopk_w = 0.  Outputs: dx [T, d_h], dw1 [E, 2 d_e, d_h], dw2
+ * [E, d_h, d_e], dtopk_w [T, k], all fp32 (fp64 values with ORACLE_ACC64, then
+ * stored as float).  Returns ORACLE_EINVAL for a mode other than BF16 or bad
+ * shapes, ORACLE_ENOMEM if scratch cannot be allocated.
+ */
+int moe_oracle_backward(int mode, int64_t T, int E, int k, int64_t d_h, int64_t d_e, const void* x,
+                        const int32_t* topk_ids, const float* topk_w, const void* w1, const void* w2,
+                        const uint16_t* dout, int flags, float* dx, float* dw1, float* dw2, float* dtopk_w) {
+    int f64 = (flags & ORACLE_ACC64) != 0;
+    int mirror = (flags & ORACLE_MIRROR_H) != 0;
+    int64_t t, p, r, c, n, i;
+    int j;
+    double *g, *u, *h, *dg, *du, *q, *dxr, *gw1, *gw2;
+    if (mode != ORACLE_MODE_BF16 || !check_dims(mode, T, E, k, d_h, d_e)) return ORACLE_EINVAL;
+    if (!x || !topk_ids || !topk_w || !w1 || !w2 || !dout || !dx || !dw1 || !dw2 || !dtopk_w) return ORACLE_EINVAL;
+    oracle_init();
+    g = (double*)malloc(sizeof(double) * (size_t)(6 * d_e + 2 * d_h));
+    gw1 = (double*)calloc((size_t)(E * 2 * d_e * d_h), sizeof(double));
+    gw2 = (double*)calloc((size_t)(E * d_h * d_e), sizeof(double));
+    if (!g || !gw1 || !gw2) {
+        free(g);
+        free(gw1);
+        free(gw2);
+        return ORACLE_ENOMEM;
+    }
+    u = g + d_e;
+    h = u + d_e;
+    dg = h + d_e;
+    du = dg + d_e;
+    q = du + d_e;
+    dxr = q + d_e; /* d_h: dx of the current token */
+    for (t = 0; t < T; ++t) {
+        for (c = 0; c < d_h; ++c) dxr[c] = 0.0;
+        for (j = 0; j < k; ++j) {
+            int32_t e;
+            double wt, dsum = 0.0;
+            p = t * k + j;
+            e = topk_ids[p];
+            wt = topk_w[p];
+            if (e < 0 || e >= E) {
+                dtopk_w[p] = 0.0f;
+                continue;
+            }
+            /* recompute: gate and up accumulators, the activation and h */
+            for (r = 0; r < d_e; ++r) {
+                double gg = 0.0, uu = 0.0, sg;
+                for (c = 0; c < d_h; ++c) {
+                    double xv = ld_x(mode, f64, x, NULL, d_h, t, c);
+                    gg = R(gg + R(ld_w(mode, f64, w1, NULL, 2 * d_e, d_h, e, r, c) * xv, f64), f64);
+                    uu = R(uu + R(ld_w(mode, f64, w1, NULL, 2 * d_e, d_h, e, d_e + r, c) * xv, f64), f64);
+                }
+                g[r] = gg;
+                u[r] = uu;
+                sg = f64 ? gg / (1.0 + exp(-gg)) : R(gg / R(1.0 + (double)expf((float)-gg), 0), 0);
+                h[r] = R(sg * uu, f64);
+                if (mirror) h[r] = oracle_bf16_decode(oracle_bf16_encode((float)h[r]));
+            }
+            /* q = dout[t] . W2[e] (the unweighted gradient of h) */
+            for (r = 0; r < d_e; ++r) {
+                double s = 0.0;
+                for (n = 0; n < d_h; ++n)
+                    s = R(s + R(oracle_bf16_decode(dout[t * d_h + n]) * ld_w(mode, f64, w2, NULL, d_h, d_e, e, n, r), f64),
+                          f64);
+                q[r] = s;
+            }
+            for (r = 0; r < d_e; ++r) dsum = R(dsum + R(q[r] * h[r], f64), f64);
+            dtopk_w[p] = (float)dsum;
+            /* activation backward */
+            for (r = 0; r < d_e; ++r) {
+                double dh = R(wt * q[r], f64), sig, silu, dsilu;
+                sig = f64 ? 1.0 / (1.0 + exp(-g[r])) : R(1.0 / R(1.0 + (double)expf((float)-g[r]), 0), 0);
+                silu = R(g[r] * sig, f64);
+                dsilu = R(sig * R(1.0 + R(g[r] * R(1.0 - sig, f64), f64), f64), f64);
+                dg[r] = R(R(dh * u[r], f64) * dsilu, f64);
+                du[r] = R(dh * silu, f64);
+                if (mirror) {
+                    dg[r] = oracle_bf16_decode(oracle_bf16_encode((float)dg[r]));
+                    du[r] = oracle_bf16_decode(oracle_bf16_encode((float)du[r]));
+                }
+            }
+            /* dx of this slot, added to the token's sum */
+            for (c = 0; c < d_h; ++c) {
+                double s = 0.0;
+                for (r = 0; r < d_e; ++r) {
+                    s = R(s + R(dg[r] * ld_w(mode, f64, w1, NULL, 2 * d_e, d_h, e, r, c), f64), f64);
+                    s = R(s + R(du[r] * ld_w(mode, f64, w1, NULL, 2 * d_e, d_h, e, d_e + r, c), f64), f64);
+                }
+                dxr[c] = R(dxr[c] + s, f64);
+            }
+            /* weight gradients, accumulated in ascending p per expert */
+            for (r = 0; r < d_e; ++r)
+                for (c = 0; c < d_h; ++c) {
+                    double xv = ld_x(mode, f64, x, NULL, d_h, t, c);
+                    i = (e * 2 * d_e + r) * d_h + c;
+                    gw1[i] = R(gw1[i] + R(dg[r] * xv, f64), f64);
+                    i = (e * 2 * d_e + d_e + r) * d_h + c;
+                    gw1[i] = R(gw1[i] + R(du[r] * xv, f64), f64);
+                }
+            for (n = 0; n < d_h; ++n) {
+                double dy = R(wt * oracle_bf16_decode(dout[t * d_h + n]), f64);
+                if (mirror) dy = oracle_bf16_decode(oracle_bf16_encode((float)dy));
+                for (r = 0; r < d_e; ++r) {
+                    i = (e * d_h + n) * d_e + r;
+                    gw2[i] = R(gw2[i] + R(dy * h[r], f64), f64);
+                }
+            }
+        }
+        for (c = 0; c < d_h; ++c) dx[t * d_h + c] = (float)dxr[c];
+    }
+    for (i = 0; i < E * 2 * d_e * d_h; ++i) dw1[i] = (float)gw1[i];
+    for (i = 0; i < E * d_h * d_e; ++i) dw2[i] = (float)gw2[i];
+    free(g);
+    free(gw1);
+    free(gw2);
+    return ORACLE_OK;
+}

@@ -73,6 +73,8 @@ def _load():
     lib.moe_oracle_forward.restype = i32
     lib.moe_oracle_forward.argtypes = [i32, i64, i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                        vp, i64, vp, vp]
+    lib.moe_oracle_backward.restype = i32
+    lib.moe_oracle_backward.argtypes = [i32, i64, i32, i32, i64, i64, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp]
     lib.moe_oracle_route.restype = i32
     lib.moe_oracle_route.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, i64, vp]
     _lib = lib
@@ -208,3 +210,30 @@ def forward(inp, rows=None, mirror: bool = True, acc64: bool = False):
     if rc != 0:
         raise ValueError(f"moe_oracle_forward failed with code {rc}")
     return acc, out
+
+
+# ---------------------------------------------------------------- backward
+def backward(inp, dout_bits, mirror: bool = True, acc64: bool = False):
+    """Gradients of the layer (BF16 mode) for the output gradient ``dout_bits``
+    (bf16 bits [T, d_h]): returns dx [T, d_h], dw1 [E, 2 d_e, d_h],
+    dw2 [E, d_h, d_e], dtopk_w [T, k], all float32 (see moe_oracle_backward)."""
+    lib = _load()
+    if int(inp.mode) != MODE_BF16:
+        raise ValueError("the backward oracle takes BF16 mode")
+    T, E, k, d_h, d_e = int(inp.T), int(inp.E), int(inp.k), int(inp.d_h), int(inp.d_e)
+    x = np.ascontiguousarray(inp.x, dtype=np.uint16)
+    ids = np.ascontiguousarray(inp.topk_ids, dtype=np.int32)
+    tw = np.ascontiguousarray(inp.topk_w, dtype=np.float32)
+    w1 = np.ascontiguousarray(inp.w1, dtype=np.uint16)
+    w2 = np.ascontiguousarray(inp.w2, dtype=np.uint16)
+    dout = np.ascontiguousarray(dout_bits, dtype=np.uint16)
+    dx = np.zeros((T, d_h), np.float32)
+    dw1 = np.zeros((E, 2 * d_e, d_h), np.float32)
+    dw2 = np.zeros((E, d_h, d_e), np.float32)
+    dtw = np.zeros((T, k), np.float32)
+    flags = (MIRROR_H if mirror else 0) | (ACC64 if acc64 else 0)
+    rc = lib.moe_oracle_backward(MODE_BF16, T, E, k, d_h, d_e, _ptr(x), _ptr(ids), _ptr(tw), _ptr(w1), _ptr(w2),
+                                 _ptr(dout), flags, _ptr(dx), _ptr(dw1), _ptr(dw2), _ptr(dtw))
+    if rc != 0:
+        raise ValueError(f"moe_oracle_backward failed with code {rc}")
+    return dx, dw1, dw2, dtw

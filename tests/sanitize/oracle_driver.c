@@ -22,6 +22,28 @@ int moe_oracle_forward(int, int64_t, int, int, int64_t, int64_t, const void*, co
                        int64_t, double*, void*);
 int moe_oracle_route(const int32_t*, int64_t, int, int, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*, int32_t*,
                      int32_t*, int64_t, int32_t*, int32_t*, int64_t, int64_t*);
+int moe_oracle_backward(int, int64_t, int, int, int64_t, int64_t, const void*, const int32_t*, const float*,
+                        const void*, const void*, const uint16_t*, int, float*, float*, float*, float*);
+
+static int backward_case(int64_t T, int E, int k, int64_t d_h, int64_t d_e, int flags) {
+    uint16_t* x = malloc(2 * T * d_h + 2);
+    uint16_t* w1 = malloc(2 * E * 2 * d_e * d_h);
+    uint16_t* w2 = malloc(2 * E * d_h * d_e);
+    uint16_t* dout = malloc(2 * T * d_h + 2);
+    int32_t* ids = malloc(4 * T * k + 4);
+    float* tw = malloc(4 * T * k + 4);
+    float *dx = malloc(4 * T * d_h + 4), *dw1 = malloc(4 * E * 2 * d_e * d_h), *dw2 = malloc(4 * E * d_h * d_e);
+    float* dtw = malloc(4 * T * k + 4);
+    int64_t i;
+    int rc;
+    for (i = 0; i < T * d_h; ++i) { x[i] = oracle_bf16_encode(frnd()); dout[i] = oracle_bf16_encode(frnd()); }
+    for (i = 0; i < E * 2 * d_e * d_h; ++i) w1[i] = oracle_bf16_encode(frnd() * 0.1f);
+    for (i = 0; i < E * d_h * d_e; ++i) w2[i] = oracle_bf16_encode(frnd() * 0.1f);
+    for (i = 0; i < T * k; ++i) { ids[i] = (rnd() % 5 == 0) ? -1 : (int32_t)(rnd() % E); tw[i] = frnd(); }
+    rc = moe_oracle_backward(1, T, E, k, d_h, d_e, x, ids, tw, w1, w2, dout, flags, dx, dw1, dw2, dtw);
+    free(x); free(w1); free(w2); free(dout); free(ids); free(tw); free(dx); free(dw1); free(dw2); free(dtw);
+    return rc;
+}
 
 static uint64_t rs = 88172645463325252ull;
 static uint32_t rnd(void) {
@@ -127,6 +149,9 @@ int main(void) {
             bad |= forward_case(mode, 5, 4, 8, 128, 256, 0, f | 2) != 0;
         }
     bad |= forward_case(1, 0, 3, 2, 128, 128, 0, 1) != 0;
+    bad |= backward_case(7, 3, 2, 128, 128, 1) != 0;
+    bad |= backward_case(4, 1, 3, 128, 256, 2) != 0;
+    bad |= backward_case(0, 2, 2, 128, 128, 1) != 0;
     /* invalid shapes must be refused */
     bad |= forward_case(2, 4, 2, 1, 100, 128, 0, 1) == 0;
     bad |= forward_case(5, 4, 2, 1, 128, 128, 0, 1) == 0;

@@ -4,7 +4,8 @@ Each case edits one plausible mistake into a copy of the oracle's C source
 (dropped term, wrong sign, wrong index, transposed operand, broken rounding,
 broken stability, a wrong MX scale index, exponent or bias, a dropped clamp,
 term or slope of the clamped activation, an ignored, unsigned or wrongly indexed int8
-token scale), builds it, and runs the CPU pin tests against it in a
+token scale, and in the backward a wrong derivative sign, a dropped routing
+weight, a transposed index or swapped gate/up rows), builds it, and runs the CPU pin tests against it in a
 subprocess; the run must fail.  The product path is not involved.
 """
 import os
@@ -41,10 +42,18 @@ MUTATIONS = {
                            "((const int8_t*)x)[t * d_h + c], f64)"),
     "int8_read_unsigned": ("((const int8_t*)x)[t * d_h + c]", "((const uint8_t*)x)[t * d_h + c]"),
     "int8_scale_by_column": ("((const float*)xs)[t], f64)", "((const float*)xs)[c % 8], f64)"),
+    "bwd_dsilu_sign": ("R(1.0 - sig, f64)", "R(1.0 + sig, f64)"),
+    "bwd_routing_weight_dropped": ("double dh = R(wt * q[r], f64)", "double dh = q[r]"),
+    "bwd_dw2_unweighted": ("double dy = R(wt * oracle_bf16_decode(dout[t * d_h + n]), f64);",
+                           "double dy = oracle_bf16_decode(dout[t * d_h + n]);"),
+    "bwd_dx_up_uses_gate_rows": ("R(du[r] * ld_w(mode, f64, w1, NULL, 2 * d_e, d_h, e, d_e + r, c), f64)",
+                                 "R(du[r] * ld_w(mode, f64, w1, NULL, 2 * d_e, d_h, e, r, c), f64)"),
+    "bwd_dw2_transposed_index": ("i = (e * d_h + n) * d_e + r;", "i = (e * d_h + r) * d_e + n;"),
+    "bwd_dtopk_uses_dh": ("dsum = R(dsum + R(q[r] * h[r], f64), f64);", "dsum = R(dsum + R(wt * q[r] * h[r], f64), f64);"),
 }
 
 PIN_TESTS = ["tests/test_oracle_codecs.py", "tests/test_oracle_routing.py", "tests/test_oracle_forward.py",
-             "tests/test_oracle_activation.py"]
+             "tests/test_oracle_activation.py", "tests/test_oracle_backward.py"]
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
