@@ -25,6 +25,15 @@ int moe_oracle_route(const int32_t*, int64_t, int, int, int32_t*, int32_t*, int3
 int moe_oracle_backward(int, int64_t, int, int, int64_t, int64_t, const void*, const int32_t*, const float*,
                         const void*, const void*, const uint16_t*, int, float*, float*, float*, float*);
 
+static uint64_t rs = 88172645463325252ull;
+static uint32_t rnd(void) {
+    rs ^= rs << 13;
+    rs ^= rs >> 7;
+    rs ^= rs << 17;
+    return (uint32_t)rs;
+}
+static float frnd(void) { return (float)((rnd() & 0xffffff) / 16777216.0 * 2.0 - 1.0); }
+
 static int backward_case(int64_t T, int E, int k, int64_t d_h, int64_t d_e, int flags) {
     uint16_t* x = malloc(2 * T * d_h + 2);
     uint16_t* w1 = malloc(2 * E * 2 * d_e * d_h);
@@ -44,15 +53,6 @@ static int backward_case(int64_t T, int E, int k, int64_t d_h, int64_t d_e, int 
     free(x); free(w1); free(w2); free(dout); free(ids); free(tw); free(dx); free(dw1); free(dw2); free(dtw);
     return rc;
 }
-
-static uint64_t rs = 88172645463325252ull;
-static uint32_t rnd(void) {
-    rs ^= rs << 13;
-    rs ^= rs >> 7;
-    rs ^= rs << 17;
-    return (uint32_t)rs;
-}
-static float frnd(void) { return (float)((rnd() & 0xffffff) / 16777216.0 * 2.0 - 1.0); }
 
 static int route_case(int64_t N, int E, int bm) {
     int32_t* ids = malloc(sizeof(int32_t) * (N ? N : 1));
