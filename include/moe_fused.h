@@ -245,6 +245,35 @@ MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, cons
 MOE_API int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void* w1_packed,
                              void* w2_packed, void* stream);
 
+/*
+ * Backward pass with recompute (the MoE megakernel of PipeLink section 5.3
+ * serves forward, backward and recompute passes; the gradients are the chain
+ * rule of the forward above).  BF16 mode, row-major weights and SwiGLU only
+ * (MOE_ERR_UNSUPPORTED otherwise).  Nothing of the forward is kept: the gate
+ * and up accumulators and h are recomputed from x and W1.
+ *
+ *  x, topk_ids, topk_w, w1, w2  as for moe_fused_forward (bf16 x, W1, W2)
+ *  dout      [T, d_h] bf16       gradient of the layer output
+ *  dx        [T, d_h] fp32       out: gradient of x
+ *  dw1       [E, 2*d_e, d_h] fp32  out: gradient of W1 (every expert written; 0 for experts without rows)
+ *  dw2       [E, d_h, d_e] fp32  out: gradient of W2
+ *  dtopk_w   [T, k] fp32         out: gradient of the routing weights (0 for dropped ids)
+ *  workspace at least moe_backward_workspace_bytes(dims) bytes, 256-byte aligned
+ *
+ * Per routed row p (token t, expert e, weight w), with h = bf16(silu(g) u):
+ *   q = dout[t] . W2[e],  dtopk_w[p] = <q, h>,  dh = w q,
+ *   dg = bf16(dh u silu'(g)),  du = bf16(dh silu(g)),
+ *   dx[t] = sum over the token's slots (ascending) of [dg du] . W1[e],
+ *   dW1[e] = sum_p [dg du]^T x[t],  dW2[e] = sum_p bf16(w dout[t])^T h.
+ * The bf16 roundings of dg, du and w dout are where the backward's bf16 GEMMs
+ * take their operands.  Errors as for moe_fused_forward; every pointer 16-byte
+ * aligned.  The caller owns all buffers; nothing is allocated.
+ */
+MOE_API size_t moe_backward_workspace_bytes(const moe_dims* dims);
+MOE_API int moe_fused_backward(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                               const void* w1, const void* w2, const void* dout, float* dx, float* dw1, float* dw2,
+                               float* dtopk_w, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Rows per group block: each expert's group of routed rows is padded to a
  * multiple of this (tilelang.dataflow README section 3.5, "padded offsets"). */
 MOE_API int32_t moe_block_m(void);

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_fused.so")
-SOURCES = ["moe_route.hip", "moe_gemm.hip", "moe_api.hip"]
+SOURCES = ["moe_route.hip", "moe_gemm.hip", "moe_backward.hip", "moe_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 ALU ops are switched off for every HIP translation unit.

@@ -352,6 +352,54 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     return MOE_OK;
 }
 
+// ------------------------------------------------------------- backward
+// Workspace of moe_fused_backward: routing arrays, transposed weights, the
+// recomputed gate/up accumulators and every intermediate of the backward.
+struct BwdLayout {
+    size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, tile_expert, tile_row0, stats;
+    size_t w1t, w2t, gu, q, h, dgu, dxp, dgut, xpt, dyt, ht, total;
+    int64_t n_pad_cap, tile_cap, ldt;
+};
+
+static void bwd_layout_of(const moe_dims* d, BwdLayout* L) {
+    const int64_t N = (int64_t)d->num_tokens * d->top_k, E = d->num_experts, d_h = d->d_hidden, d_e = d->d_expert;
+    route_caps(N, E, &L->n_pad_cap, &L->tile_cap);
+    L->ldt = (L->n_pad_cap + 63) / 64 * 64;  // row length of the transposed (K = padded rows) operands
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align_up(o + (bytes ? bytes : 1));
+        return at;
+    };
+    L->counts = take(4 * E);
+    L->offsets = take(4 * (E + 1));
+    L->padded_offsets = take(4 * (E + 1));
+    L->pos = take(4 * N);
+    L->sorted_p = take(4 * N);
+    L->ppos = take(4 * N);
+    L->row_src = take(4 * L->n_pad_cap);
+    L->tile_expert = take(4 * L->tile_cap);
+    L->tile_row0 = take(4 * L->tile_cap);
+    L->stats = take(4 * kCtlWords);
+    L->w1t = take(2 * (size_t)E * 2 * d_e * d_h);
+    L->w2t = take(2 * (size_t)E * d_h * d_e);
+    L->gu = take(4 * (size_t)L->n_pad_cap * 2 * d_e);
+    L->q = take(4 * (size_t)L->n_pad_cap * d_e);
+    L->h = take(2 * (size_t)L->n_pad_cap * d_e);
+    L->dgu = take(2 * (size_t)L->n_pad_cap * 2 * d_e);
+    L->dxp = take(4 * (size_t)L->n_pad_cap * d_h);
+    L->dgut = take(2 * (size_t)2 * d_e * L->ldt);
+    L->xpt = take(2 * (size_t)d_h * L->ldt);
+    L->dyt = take(2 * (size_t)d_h * L->ldt);
+    L->ht = take(2 * (size_t)d_e * L->ldt);
+    L->total = o;
+}
+
+static bool bwd_dims_ok(const moe_dims* d) {
+    return dims_ok(d) && d->mode == MOE_MODE_BF16 && d->weight_layout == MOE_WEIGHTS_ROW_MAJOR &&
+           d->activation == MOE_ACT_SWIGLU;
+}
+
 int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void* w1_packed, void* w2_packed,
                      void* stream) {
     if (!dims) return MOE_ERR_INVALID_ARG;
@@ -405,6 +453,103 @@ int moe_fused_forward_noalloc(const moe_dims* dims, const void* x, const int32_t
     // then; it is rejected before any use)
     return forward_impl(dims, x, topk_ids, topk_w, w1, w2, scales, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream,
                         nullptr);
+}
+
+size_t moe_backward_workspace_bytes(const moe_dims* dims) {
+    if (!bwd_dims_ok(dims)) return 0;
+    BwdLayout L;
+    bwd_layout_of(dims, &L);
+    return L.total;
+}
+
+int moe_fused_backward(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,
+                       const void* w1, const void* w2, const void* dout, float* dx, float* dw1, float* dw2,
+                       float* dtopk_w, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!dims) return MOE_ERR_INVALID_ARG;
+    if (!dims_ok(dims)) return MOE_ERR_INVALID_ARG;
+    if (!bwd_dims_ok(dims)) return MOE_ERR_UNSUPPORTED;
+    const int64_t T = dims->num_tokens;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_ids || !topk_w || !w1 || !w2 || !dout || !dx || !dw1 || !dw2 || !dtopk_w)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(dout) || !aligned16(dx) ||
+        !aligned16(dw1) || !aligned16(dw2) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(dtopk_w))
+        return MOE_ERR_INVALID_ARG;
+    BwdLayout L;
+    bwd_layout_of(dims, &L);
+    if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int32_t E = dims->num_experts, k = dims->top_k, d_h = dims->d_hidden, d_e = dims->d_expert;
+    const int64_t N = T * k;
+
+    RouteArgs r{};
+    r.ids = topk_ids;
+    r.N = (int32_t)N;
+    r.E = E;
+    r.n_pad_cap = L.n_pad_cap;
+    r.tile_cap = L.tile_cap;
+    r.nb1 = r.nb2 = 0;
+    r.mb1_max = kMaxRowBlocks1;
+    r.full = 1;
+    r.counts = at<int32_t>(workspace, L.counts);
+    r.offsets = at<int32_t>(workspace, L.offsets);
+    r.padded_offsets = at<int32_t>(workspace, L.padded_offsets);
+    r.pos = at<int32_t>(workspace, L.pos);
+    r.sorted_p = at<int32_t>(workspace, L.sorted_p);
+    r.ppos = at<int32_t>(workspace, L.ppos);
+    r.row_src = at<int32_t>(workspace, L.row_src);
+    r.tile_expert = at<int32_t>(workspace, L.tile_expert);
+    r.tile_row0 = at<int32_t>(workspace, L.tile_row0);
+    r.ctl = at<int32_t>(workspace, L.stats);
+    if (launch_route(r, s) != hipSuccess) return MOE_ERR_HIP;
+    const int32_t* poff = r.padded_offsets;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* w1b = static_cast<const uint16_t*>(w1);
+    const uint16_t* w2b = static_cast<const uint16_t*>(w2);
+    const uint16_t* db = static_cast<const uint16_t*>(dout);
+    uint16_t* w1t = at<uint16_t>(workspace, L.w1t);
+    uint16_t* w2t = at<uint16_t>(workspace, L.w2t);
+    float* gu = at<float>(workspace, L.gu);
+    float* q = at<float>(workspace, L.q);
+    uint16_t* h = at<uint16_t>(workspace, L.h);
+    uint16_t* dgu = at<uint16_t>(workspace, L.dgu);
+    float* dxp = at<float>(workspace, L.dxp);
+    uint16_t* dgut = at<uint16_t>(workspace, L.dgut);
+    uint16_t* xpt = at<uint16_t>(workspace, L.xpt);
+    uint16_t* dyt = at<uint16_t>(workspace, L.dyt);
+    uint16_t* ht = at<uint16_t>(workspace, L.ht);
+    const int R = (int)L.n_pad_cap;
+    bool ok = true;
+    // transposed weights: W1^T [E][d_h][2 d_e], W2^T [E][d_e][d_h]
+    ok = ok && launch_transpose(w1b, d_h, (int64_t)2 * d_e * d_h, w1t, 2 * d_e, (int64_t)2 * d_e * d_h, 2 * d_e, d_h,
+                                E, nullptr, 1, nullptr, nullptr, s) == hipSuccess;
+    ok = ok && launch_transpose(w2b, d_e, (int64_t)d_h * d_e, w2t, d_h, (int64_t)d_h * d_e, d_h, d_e, E, nullptr, 1,
+                                nullptr, nullptr, s) == hipSuccess;
+    // recompute [g u] per padded row; q = dout . W2[e]
+    ok = ok && launch_bwd_gemm_rows(xb, d_h, r.row_src, k, w1b, d_h, (int64_t)2 * d_e * d_h, gu, 2 * d_e, 2 * d_e, d_h,
+                                    r.tile_expert, r.tile_row0, r.ctl, L.tile_cap, s) == hipSuccess;
+    ok = ok && launch_bwd_gemm_rows(db, d_h, r.row_src, k, w2t, d_h, (int64_t)d_e * d_h, q, d_e, d_e, d_h,
+                                    r.tile_expert, r.tile_row0, r.ctl, L.tile_cap, s) == hipSuccess;
+    // h, dg, du, dtopk_w
+    ok = ok && launch_bwd_act(gu, q, r.row_src, poff + E, topk_w, h, dgu, dtopk_w, d_e, L.n_pad_cap, s) == hipSuccess;
+    // dX per row, then per token over its slots (also zeroes dtopk_w of dropped slots)
+    ok = ok && launch_bwd_gemm_rows(dgu, 2 * d_e, nullptr, 1, w1t, 2 * d_e, (int64_t)2 * d_e * d_h, dxp, d_h, d_h,
+                                    2 * d_e, r.tile_expert, r.tile_row0, r.ctl, L.tile_cap, s) == hipSuccess;
+    ok = ok && launch_bwd_dx(dxp, r.ppos, topk_ids, dx, dtopk_w, (int)T, k, E, d_h, s) == hipSuccess;
+    // K-contiguous operands of the weight gradients (K = an expert's padded rows)
+    ok = ok && launch_transpose(dgu, 2 * d_e, 0, dgut, L.ldt, 0, R, 2 * d_e, 1, nullptr, 1, nullptr, poff + E, s) ==
+                   hipSuccess;
+    ok = ok && launch_transpose(xb, d_h, 0, xpt, L.ldt, 0, R, d_h, 1, r.row_src, k, nullptr, poff + E, s) ==
+                   hipSuccess;
+    ok = ok && launch_transpose(db, d_h, 0, dyt, L.ldt, 0, R, d_h, 1, r.row_src, k, topk_w, poff + E, s) ==
+                   hipSuccess;
+    ok = ok && launch_transpose(h, d_e, 0, ht, L.ldt, 0, R, d_e, 1, nullptr, 1, nullptr, poff + E, s) == hipSuccess;
+    // dW1[e] = [dg du]^T . x rows; dW2[e] = (w dout)^T . h rows
+    ok = ok && launch_bwd_gemm_experts(dgut, L.ldt, xpt, L.ldt, dw1, d_h, (int64_t)2 * d_e * d_h, E, 2 * d_e, d_h,
+                                       poff, s) == hipSuccess;
+    ok = ok && launch_bwd_gemm_experts(dyt, L.ldt, ht, L.ldt, dw2, d_e, (int64_t)d_h * d_e, E, d_h, d_e, poff, s) ==
+                   hipSuccess;
+    return ok ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_fused_forward_profiled(const moe_dims* dims, const void* x, const int32_t* topk_ids, const float* topk_w,

@@ -176,6 +176,25 @@ hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, h
                         hipEvent_t t1 = nullptr);
 hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);
+// Backward pass (BF16 mode; see moe_backward.hip).  Row GEMM: C rows are the
+// 16-row group blocks of the padded layout; expert GEMM: per expert, K over
+// its padded rows.
+hipError_t launch_bwd_gemm_rows(const uint16_t* A, int64_t lda, const int32_t* a_rows, int a_div, const uint16_t* B,
+                                int64_t ldb, int64_t b_estride, float* C, int64_t ldc, int N, int K,
+                                const int32_t* tile_expert, const int32_t* tile_row0, const int32_t* ctl,
+                                int64_t tile_cap, hipStream_t s);
+hipError_t launch_bwd_gemm_experts(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, float* C,
+                                   int64_t ldc, int64_t c_estride, int E, int M, int N, const int32_t* poff,
+                                   hipStream_t s);
+hipError_t launch_transpose(const uint16_t* in, int64_t ldi, int64_t in_bstride, uint16_t* out, int64_t ldo,
+                            int64_t out_bstride, int R, int C, int batch, const int32_t* rows, int map_div,
+                            const float* roww, const int32_t* n_used, hipStream_t s);
+hipError_t launch_bwd_act(const float* GU, const float* Q, const int32_t* row_src, const int32_t* poff_end,
+                          const float* topk_w, uint16_t* H, uint16_t* dGU, float* dtopk_w, int d_e, int64_t n_pad_cap,
+                          hipStream_t s);
+hipError_t launch_bwd_dx(const float* dXp, const int32_t* ppos, const int32_t* ids, float* dx, float* dtopk_w, int T,
+                         int k, int E, int d_h, hipStream_t s);
+
 // Resident workgroups per CU of the persistent GEMM kernels (occupancy query;
 // wide: the 8-wave FP8 GEMM-1).
 hipError_t gemm_occupancy(int mode, bool wide, int* g1_blocks_per_cu, int* g2_blocks_per_cu);

@@ -90,6 +90,10 @@ def lib():
                                              ctypes.c_size_t, vp, P(vp)]
     L.moe_fused_forward_noalloc.restype = ctypes.c_int
     L.moe_fused_forward_noalloc.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, P(moe_scales), vp, vp]
+    L.moe_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.moe_backward_workspace_bytes.argtypes = [P(moe_dims)]
+    L.moe_fused_backward.restype = ctypes.c_int
+    L.moe_fused_backward.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.moe_pack_weights.restype = ctypes.c_int
     L.moe_pack_weights.argtypes = [P(moe_dims), vp, vp, vp, vp, vp]
     L.moe_block_m.restype = ctypes.c_int32
@@ -136,6 +140,16 @@ def moe_fused_forward_profiled(dims, x, topk_ids, topk_w, w1, w2, scales, out, w
     return int(lib().moe_fused_forward_profiled(ctypes.byref(dims), x, topk_ids, topk_w, w1, w2,
                                                 ctypes.byref(scales) if scales is not None else None, out,
                                                 workspace, workspace_bytes, stream, ev))
+
+
+def moe_backward_workspace_bytes(dims: moe_dims) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(dims)))
+
+
+def moe_fused_backward(dims, x, topk_ids, topk_w, w1, w2, dout, dx, dw1, dw2, dtopk_w, workspace, workspace_bytes,
+                       stream) -> int:
+    return int(lib().moe_fused_backward(ctypes.byref(dims) if dims is not None else None, x, topk_ids, topk_w, w1, w2,
+                                        dout, dx, dw1, dw2, dtopk_w, workspace, workspace_bytes, stream))
 
 
 def moe_pack_weights(dims, w1, w2, w1_packed, w2_packed, stream) -> int:
@@ -291,3 +305,31 @@ def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=
     if rc:
         raise MoEError(rc, "moe_fused_forward")
     return out
+
+
+def fused_backward(x, topk_ids, topk_w, w1, w2, dout, workspace=None, stream=None):
+    """``moe_fused_backward`` on torch device tensors (bf16 x, w1, w2, dout; int32
+    ids; float32 weights): returns (dx, dw1, dw2, dtopk_w), float32."""
+    import torch
+    dims = make_dims(x, topk_ids, w1)
+    if dims.mode != MOE_MODE_BF16:
+        raise ValueError("the backward takes bf16 x and weights")
+    for name, t in (("x", x), ("topk_ids", topk_ids), ("topk_w", topk_w), ("w1", w1), ("w2", w2), ("dout", dout)):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if dout.dtype != torch.bfloat16 or tuple(dout.shape) != tuple(x.shape):
+        raise ValueError("dout must be bf16 with the shape of x")
+    T, d_h = x.shape
+    E, two_de, _ = w1.shape
+    dx = torch.empty(T, d_h, dtype=torch.float32, device=x.device)
+    dw1 = torch.empty(E, two_de, d_h, dtype=torch.float32, device=x.device)
+    dw2 = torch.empty(E, d_h, two_de // 2, dtype=torch.float32, device=x.device)
+    dtw = torch.empty(topk_w.shape, dtype=torch.float32, device=x.device)
+    need = moe_backward_workspace_bytes(dims)
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    rc = moe_fused_backward(dims, x.data_ptr(), topk_ids.data_ptr(), topk_w.data_ptr(), w1.data_ptr(), w2.data_ptr(),
+                            dout.data_ptr(), dx.data_ptr(), dw1.data_ptr(), dw2.data_ptr(), dtw.data_ptr(),
+                            ws.data_ptr(), ws.numel(), _stream_ptr(stream))
+    if rc:
+        raise MoEError(rc, "moe_fused_backward")
+    return dx, dw1, dw2, dtw

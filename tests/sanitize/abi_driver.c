@@ -81,6 +81,19 @@ int main(void) {
         EXPECT(moe_pack_weights(NULL, p, p, p, p, NULL) == MOE_ERR_INVALID_ARG);
     }
     {
+        moe_dims bd = {MOE_MODE_BF16, 100, 8, 2, 256, 128, 0, 0};
+        size_t bw = moe_backward_workspace_bytes(&bd);
+        EXPECT(bw > 0);
+        bd.mode = MOE_MODE_FP8;
+        EXPECT(moe_backward_workspace_bytes(&bd) == 0);
+        EXPECT(moe_fused_backward(&bd, p, p, p, p, p, p, p, p, p, p, p, bw, NULL) == MOE_ERR_UNSUPPORTED);
+        bd.mode = MOE_MODE_BF16;
+        EXPECT(moe_fused_backward(&bd, p, p, p, p, p, p, p, p, p, p, p, bw - 1, NULL) == MOE_ERR_WORKSPACE);
+        EXPECT(moe_fused_backward(&bd, p, p, p, p, p, NULL, p, p, p, p, p, bw, NULL) == MOE_ERR_INVALID_ARG);
+        EXPECT(moe_fused_backward(&bd, p, p, p, p, p, p, mis, p, p, p, p, bw, NULL) == MOE_ERR_INVALID_ARG);
+        EXPECT(moe_fused_backward(NULL, p, p, p, p, p, p, p, p, p, p, p, bw, NULL) == MOE_ERR_INVALID_ARG);
+    }
+    {
         moe_route_out ro;
         memset(&ro, 0, sizeof(ro));
         EXPECT(moe_route(10, 2, 4, p, &ro, NULL) == MOE_ERR_INVALID_ARG);

@@ -41,10 +41,11 @@ def test_library_host_code_under_sanitizers(tmp_path):
              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-sanitize-recover=all"]
     procs, objs = [], []
-    for name in ("moe_route", "moe_gemm", "moe_api"):
-        obj = str(tmp_path / f"{name}.o")
+    from skew_aware_grouped_amd import build
+    for name in build.SOURCES:
+        obj = str(tmp_path / name.replace(".hip", ".o"))
         objs.append(obj)
-        procs.append(subprocess.Popen([HIPCC, *flags, "-c", os.path.join(src, name + ".hip"), "-o", obj],
+        procs.append(subprocess.Popen([HIPCC, *flags, "-c", os.path.join(src, name), "-o", obj],
                                       stdout=subprocess.DEVNULL, stderr=subprocess.PIPE, text=True))
     for p in procs:
         _, err = p.communicate(timeout=900)
