@@ -19,6 +19,7 @@ The weights are rewritten once, before any timing, into the packed tile order
 row-major`` times the layer on the weights as given instead.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--weights packed|row-major] [--no-cpu]
+    python bench.py --pass backward --config qwen_bf16   (the backward with recompute)
 """
 import argparse
 import json
@@ -143,6 +144,86 @@ def copy_calibration(mb):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
+def backward_alg(w):
+    """FLOPs and bytes the backward with recompute must do: per valid assignment
+    16*d_h*d_e FLOPs (recomputed gate/up 4, q 2, dX 4, dW1 4, dW2 2); bytes: the
+    active experts' W1 and W2 read once (bf16), dW1 and dW2 of every expert
+    written (fp32), x and dout read, dx written (fp32), ids, weights and their
+    gradient."""
+    nv = w.valid_assignments()
+    flops = 16.0 * w.d_h * w.d_e * nv
+    wb = 3 * w.d_h * w.d_e
+    byts = w.active_experts() * wb * 2 + w.E * wb * 4 + w.T * w.d_h * (2 + 2 + 4) + w.T * w.k * 12
+    return flops, float(byts)
+
+
+def bench_backward(args):
+    """The backward pass with recompute (moe_fused_backward, BF16) on one
+    workload: cold and warm p50 of K calls between events on the library's
+    stream, TFLOP/s, and the whole pass against the HBM roofline (its bytes are
+    dominated by writing fp32 weight gradients).  A correctness gate against
+    the backward oracle runs first."""
+    import torch
+    from oracle import moe_oracle
+    from skew_aware_grouped_amd import device, moe, workloads as W
+    torch.cuda.set_device(0)
+    w = W.config(args.config)
+    if w.mode != W.MODE_BF16:
+        print("bench.py: the backward runs BF16 workloads (e.g. --config qwen_bf16)", file=sys.stderr)
+        sys.exit(2)
+    d = device.upload(w)
+    rng = np.random.default_rng(7)
+    dout_bits = W.to_bf16_bits(rng.standard_normal((w.T, w.d_h), dtype=np.float32))
+    dout = torch.from_numpy(dout_bits.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"])
+    ws = torch.empty(moe.moe_backward_workspace_bytes(dims), dtype=torch.uint8, device="cuda:0")
+    args_b = (d["x"], d["topk_ids"], d["topk_w"], d["w1"], d["w2"], dout)
+    got = moe.fused_backward(*args_b, workspace=ws)
+    torch.cuda.synchronize()
+    ref = moe_oracle.backward(w, dout_bits)
+    errs = {n: float(np.abs(g.cpu().numpy() - r).max() / max(np.abs(r).max(), 1e-30))
+            for n, g, r in zip(("dx", "dw1", "dw2", "dtopk_w"), got, ref)}
+    if not all(v <= 1e-2 for v in errs.values()):
+        print(f"bench.py: backward correctness gate failed {errs}", file=sys.stderr)
+        sys.exit(1)
+    for _ in range(args.warmup):
+        moe.fused_backward(*args_b, workspace=ws)
+    stream = torch.cuda.current_stream()
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+
+    def timed(n, cold):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            if cold:
+                flush.sum()
+            a.record(stream)
+            moe.fused_backward(*args_b, workspace=ws, stream=stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    cold_ms = timed(args.steps, True)
+    warm_ms = timed(args.steps, False)
+    p50 = float(np.median(cold_ms))
+    flops, byts = backward_alg(w)
+    gbs = byts / (p50 * 1e-3) / 1e9
+    res = {
+        "metric": "fused MoE layer backward with recompute p50 µs + TFLOP/s (% HBM roofline), 1 MI355X",
+        "value": round(flops / (p50 * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(p50, 5), "ms_per_step_is": "cold p50 (caches flushed before each step)",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "pass": "backward", "tokens": w.T, "experts": w.E, "top_k": w.k,
+                   "d_hidden": w.d_h, "d_expert": w.d_e, "active_experts": w.active_experts()},
+        "p50_us": round(p50 * 1e3, 2), "warm_p50_us": round(float(np.median(warm_ms)) * 1e3, 2),
+        "gflop": round(flops / 1e9, 4), "alg_mb": round(byts / 1e6, 3),
+        "roofline": {"kernel": "whole backward pass", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+        "gate_normwise_err": {k: round(v, 6) for k, v in errs.items()},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +233,8 @@ def main():
     ap.add_argument("--weights", choices=["packed", "row-major"], default="packed",
                     help="weight layout the layer reads (packing happens once, outside the timed region)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
+                    help="backward: time moe_fused_backward (BF16 workloads, e.g. --config qwen_bf16)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (for scaling profiler byte counters)")
     args = ap.parse_args()
@@ -160,6 +243,9 @@ def main():
               "parallel path is a design, not a build).", file=sys.stderr)
         sys.exit(2)
 
+    if args.which == "backward":
+        bench_backward(args)
+        return
     import torch
     from skew_aware_grouped_amd import device, moe, workloads as W
 

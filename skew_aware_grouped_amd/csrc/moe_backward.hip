@@ -163,18 +163,23 @@ struct TransArgs {
 };
 
 __global__ __launch_bounds__(256) void transpose_kernel(TransArgs a) {
-    __shared__ uint16_t t[64][65];
+    // 64 x 64 tile; every global access is 16 bytes (8 values): a thread loads
+    // two 8-value pieces of input rows and writes two 8-value pieces of output
+    // rows gathered from a column of the LDS tile
+    __shared__ __attribute__((aligned(16))) uint16_t t[64][72];
     const int r0 = 64 * blockIdx.y, c0 = 64 * blockIdx.x;
     const int64_t b = blockIdx.z;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const int nu = a.n_used ? *a.n_used : a.R;
-    for (int i = ty; i < 64; i += 4) {
-        const int r = r0 + i, c = c0 + tx;
-        uint16_t v = 0;
-        if (r < a.R && c < a.C && r < nu) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int piece = threadIdx.x + 256 * h;  // 512 pieces: 64 rows x 8
+        const int i = piece >> 3, c = 8 * (piece & 7);
+        const int r = r0 + i;
+        v4i v = {0, 0, 0, 0};
+        if (r < a.R && r < nu && c0 + c < a.C) {
             int64_t src = r;
-            float sc = 1.f;
             bool ok = true;
+            float sc = 1.f;
             if (a.rows) {
                 const int p = a.rows[r];
                 ok = p >= 0;
@@ -182,16 +187,37 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransArgs a) {
                 if (ok && a.roww) sc = a.roww[p];
             }
             if (ok) {
-                v = a.in[b * a.in_bstride + src * a.ldi + c];
-                if (a.roww) v = (uint16_t)f32_to_bf16(sc * bf16_to_f32(v));
+                v = *reinterpret_cast<const v4i*>(a.in + b * a.in_bstride + src * a.ldi + c0 + c);
+                if (a.roww) {
+                    unsigned wd[4] = {(unsigned)v.x, (unsigned)v.y, (unsigned)v.z, (unsigned)v.w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const unsigned lo = f32_to_bf16(sc * bf16_to_f32((uint16_t)(wd[q] & 0xffffu)));
+                        const unsigned hi = f32_to_bf16(sc * bf16_to_f32((uint16_t)(wd[q] >> 16)));
+                        wd[q] = lo | (hi << 16);
+                    }
+                    v = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+                }
             }
         }
-        t[i][tx] = v;
+        *reinterpret_cast<v4i*>(&t[i][c]) = v;
     }
     __syncthreads();
-    for (int i = ty; i < 64; i += 4) {
-        const int c = c0 + i, r = r0 + tx;
-        if (c < a.C && r < a.R) a.out[b * a.out_bstride + (int64_t)c * a.ldo + r] = t[tx][i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int piece = threadIdx.x + 256 * h;  // 64 output rows (c) x 8 pieces of 8 r's
+        const int ci = piece >> 3, rr = 8 * (piece & 7);
+        const int c = c0 + ci, r = r0 + rr;
+        if (c >= a.C || r >= a.R) continue;
+        uint16_t* dst = a.out + b * a.out_bstride + (int64_t)c * a.ldo + r;
+        if (r + 8 <= a.R) {
+            unsigned wd[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wd[q] = (unsigned)t[rr + 2 * q][ci] | ((unsigned)t[rr + 2 * q + 1][ci] << 16);
+            *reinterpret_cast<v4i*>(dst) = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+        } else {
+            for (int q = 0; q < 8 && r + q < a.R; ++q) dst[q] = t[rr + q][ci];
+        }
     }
 }
 
