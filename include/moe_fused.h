@@ -101,10 +101,36 @@ extern "C" {
 #define MOE_ACT_SWIGLU 0
 #define MOE_ACT_SWIGLU_CLAMPED 1
 
+/* Launch form of moe_fused_forward (moe_dims.launch):
+ *  MOE_LAUNCH_MULTI   routing, GEMM-1, GEMM-2 and the combine as four kernels
+ *                     (plus the conversion of x in the F32ACT and INT8 modes).
+ *  MOE_LAUNCH_SINGLE  the whole layer in one persistent kernel: GEMM-1 and
+ *                     GEMM-2 under one launch, their dependency resolved without
+ *                     a kernel barrier (tilelang.dataflow README, section 3.5,
+ *                     "Fused MoE: map -> reshared -> map").  Every workgroup
+ *                     derives the routing plan from the ids; tasks are claimed in
+ *                     order from one queue; a GEMM-2 task waits (bounded) on a
+ *                     completion counter of its M-tile's GEMM-1 tasks; the last
+ *                     GEMM-2 task to store a (token, 128-column block) sums that
+ *                     token's slots in ascending order.  The weighted rows stay in
+ *                     fp32 (no bf16 rounding before the sum), so the output may
+ *                     differ from MOE_LAUNCH_MULTI's in the last bf16 bit; it is
+ *                     bitwise identical across calls.  Envelope: MOE_MODE_BF16,
+ *                     MOE_MODE_FP8 or MOE_MODE_MXFP8, num_tokens*top_k <= 2048,
+ *                     num_tokens*(d_hidden/128) <= 65536; MOE_ERR_UNSUPPORTED
+ *                     otherwise.  The workspace's synchronisation block (its
+ *                     first MOE_SYNC_BYTES) must hold zeros before the first
+ *                     single-launch call on that workspace (moe_workspace_init, or
+ *                     any zero fill); every single-launch call leaves it zero, and
+ *                     MOE_LAUNCH_MULTI calls do not touch it. */
+#define MOE_LAUNCH_MULTI 0
+#define MOE_LAUNCH_SINGLE 1
+#define MOE_SYNC_BYTES 265216u
+
 /* Layer shape.  Supported envelope: 0 <= num_tokens, 1 <= num_experts <= 256,
  * 1 <= top_k <= 8, num_tokens*top_k < 2^31, d_hidden and d_expert positive
- * multiples of 128.  Zero-initialising weight_layout and activation selects
- * row-major weights and SwiGLU. */
+ * multiples of 128.  Zero-initialising weight_layout, activation and launch
+ * selects row-major weights, SwiGLU and the four-kernel launch. */
 typedef struct {
     int32_t mode;          /* MOE_MODE_* */
     int32_t num_tokens;    /* T */
@@ -114,6 +140,7 @@ typedef struct {
     int32_t d_expert;      /* d_e */
     int32_t weight_layout; /* MOE_WEIGHTS_* */
     int32_t activation;    /* MOE_ACT_* */
+    int32_t launch;        /* MOE_LAUNCH_* */
 } moe_dims;
 
 /* Scales of the quantised modes (dequantised value = code * scale).  Required
@@ -167,7 +194,8 @@ MOE_API size_t moe_workspace_bytes(const moe_dims* dims);
  * Steps enqueued on `stream`: routing (histogram, prefix scan, stable scatter,
  * block map and per-XCD task lists), grouped GEMM-1 with the SwiGLU epilogue,
  * grouped GEMM-2 with the routing-weight epilogue, and the top-k combine in
- * ascending slot order.  The result is bitwise identical across calls.
+ * ascending slot order; as four kernels, or as one with MOE_LAUNCH_SINGLE
+ * (see there).  The result is bitwise identical across calls.
  * Ownership: every buffer is the caller's; the call keeps no pointer past
  * the stream work it enqueues.  num_tokens == 0 returns MOE_OK and enqueues
  * nothing.  Errors: MOE_ERR_INVALID_ARG (null dims, a field of dims out of
@@ -211,13 +239,22 @@ MOE_API int moe_fused_forward_noalloc(const moe_dims* dims, const void* x, const
  * the caller with timing enabled) receive the start and end of the routing,
  * GEMM-1, GEMM-2 and combine kernels as their dispatches record them
  * (events[2i] start, events[2i+1] end of kernel i), so hipEventElapsedTime on
- * a pair gives that kernel's duration.  Same result and errors as
- * moe_fused_forward; MOE_ERR_INVALID_ARG if events or any of its 8 entries is
- * NULL. */
+ * a pair gives that kernel's duration.  With MOE_LAUNCH_SINGLE, events[0] and
+ * events[1] bracket the one kernel and events[2..7] are recorded right after
+ * it.  Same result and errors as moe_fused_forward; MOE_ERR_INVALID_ARG if
+ * events or any of its 8 entries is NULL. */
 MOE_API int moe_fused_forward_profiled(const moe_dims* dims, const void* x, const int32_t* topk_ids,
                                        const float* topk_w, const void* w1, const void* w2,
                                        const moe_scales* scales, void* out, void* workspace,
                                        size_t workspace_bytes, void* stream, void* const* events);
+
+/* Zero the synchronisation block of a workspace (its first MOE_SYNC_BYTES), as
+ * a single-launch call needs it before its first use of that workspace (see
+ * MOE_LAUNCH_SINGLE); enqueues one small kernel on `stream` (no memset, so the
+ * call can be captured in a graph).  MOE_ERR_WORKSPACE if workspace is null,
+ * not 256-byte aligned or smaller than MOE_SYNC_BYTES; MOE_ERR_HIP if the
+ * launch fails. */
+MOE_API int moe_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Rewrite row-major W1 and W2 (bf16 or e4m3 as dims->mode says) into the
@@ -334,10 +371,14 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
  * {expert, first padded row, row blocks, column block}; within a segment they
  * are ordered by descending expert row count, and all M-tiles of one
  * (expert, column block) sit in the same segment, next to each other.
+ * `sync` (always 0) is the synchronisation block of MOE_LAUNCH_SINGLE: its
+ * int32 word 64 counts the bounded waits of single-launch calls that ran out
+ * (each such call's output is not valid; 0 unless the grid could not make
+ * progress), and no call resets it.  y holds fp32 rows with MOE_LAUNCH_SINGLE.
  * Returns MOE_ERR_INVALID_ARG for invalid dims. */
 typedef struct {
     size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, row_w, tile_expert, tile_row0, stats;
-    size_t tasks1, tasks2, h, h_scale, y, zero, x_bf16, total;
+    size_t tasks1, tasks2, h, h_scale, y, zero, x_bf16, sync, total;
     int64_t n_pad_cap, tile_cap, task1_cap, task2_cap;
     int32_t block_n1, block_n2, max_row_blocks;
 } moe_ws_layout;

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_fused.so")
-SOURCES = ["moe_route.hip", "moe_gemm.hip", "moe_backward.hip", "moe_api.hip"]
+SOURCES = ["moe_route.hip", "moe_gemm.hip", "moe_layer.hip", "moe_backward.hip", "moe_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 ALU ops are switched off for every HIP translation unit.
@@ -22,8 +22,8 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hi
 # result right after the atomic, making the wave wait for it there.
 # MFMA results go to VGPRs: the FP8 promotion reads them with VALU
 # instructions, and from AGPRs each read would cost an extra move.
-SOURCE_FLAGS = {"moe_gemm.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-mllvm",
-                                 "-amdgpu-mfma-vgpr-form=1"]}
+_GEMM_FLAGS = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {"moe_gemm.hip": _GEMM_FLAGS, "moe_layer.hip": _GEMM_FLAGS}
 
 
 def build(verbose: bool = False) -> str:

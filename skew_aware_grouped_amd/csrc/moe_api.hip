@@ -22,7 +22,17 @@ bool dims_ok(const moe_dims* d) {
     if (d->d_hidden < 128 || d->d_hidden % 128 || d->d_expert < 128 || d->d_expert % 128) return false;
     if (d->weight_layout != MOE_WEIGHTS_ROW_MAJOR && d->weight_layout != MOE_WEIGHTS_PACKED) return false;
     if (d->activation != MOE_ACT_SWIGLU && d->activation != MOE_ACT_SWIGLU_CLAMPED) return false;
+    if (d->launch != MOE_LAUNCH_MULTI && d->launch != MOE_LAUNCH_SINGLE) return false;
     return true;
+}
+
+static_assert(MOE_SYNC_BYTES == 4u * kSyncWords, "synchronisation block size");
+
+// the single launch's envelope (dims already valid)
+bool single_ok(const moe_dims* d) {
+    const int64_t N = (int64_t)d->num_tokens * d->top_k;
+    return (d->mode == MOE_MODE_BF16 || d->mode == MOE_MODE_FP8 || d->mode == MOE_MODE_MXFP8) && N <= kLayerMaxN &&
+           (int64_t)d->num_tokens * (d->d_hidden / 128) <= kSyncArriveWords;
 }
 
 void route_caps(int64_t N, int64_t E, int64_t* n_pad_cap, int64_t* tile_cap) {
@@ -45,13 +55,16 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
     L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
     const size_t hb = mode_fp8(d->mode) ? 1 : 2;
-    const size_t yb = d->mode == MOE_MODE_F32ACT ? 4 : 2;
+    const size_t yb = d->mode == MOE_MODE_F32ACT || d->launch == MOE_LAUNCH_SINGLE ? 4 : 2;
     size_t o = 0;
     auto take = [&](size_t bytes) {
         const size_t at = o;
         o = align_up(o + (bytes ? bytes : 1));
         return at;
     };
+    // the synchronisation block of the single launch comes first, at the same
+    // place and size for all dims
+    L->sync = take(MOE_SYNC_BYTES);
     L->counts = take(4 * E);
     L->offsets = take(4 * (E + 1));
     L->padded_offsets = take(4 * (E + 1));
@@ -86,11 +99,13 @@ struct DeviceInfo {
     int cus = 0;
     int occ1[5] = {0, 0, 0, 0, 0};
     int occ2[5] = {0, 0, 0, 0, 0};
+    int occ_layer[4] = {0, 0, 0, 0};  // single-launch kernel, by mode (BF16, FP8, MXFP8)
 };
 std::mutex g_mu;
 DeviceInfo g_dev[64];
 
-hipError_t device_info(int mode, bool wide, int* cus, int* occ1, int* occ2) {
+// occ_layer (may be null): resident workgroups per CU of the single-launch kernel
+hipError_t device_info(int mode, bool wide, int* cus, int* occ1, int* occ2, int* occ_layer = nullptr) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
@@ -106,9 +121,15 @@ hipError_t device_info(int mode, bool wide, int* cus, int* occ1, int* occ2) {
             if (di.occ1[m] < 1) di.occ1[m] = 1;
             if (di.occ2[m] < 1) di.occ2[m] = 1;
         }
+        for (int m = MOE_MODE_BF16; m <= MOE_MODE_MXFP8; ++m) {
+            err = layer_occupancy(m, &di.occ_layer[m]);
+            if (err != hipSuccess) return err;
+            if (di.occ_layer[m] < 1) di.occ_layer[m] = 1;
+        }
         di.ready = true;
     }
     *cus = di.cus;
+    if (occ_layer) *occ_layer = di.occ_layer[mode_fp8(mode) ? mode : MOE_MODE_BF16];
     const int slot = wide ? 4 : gemm_mode(mode);
     *occ1 = di.occ1[slot];
     *occ2 = di.occ2[slot];
@@ -227,13 +248,16 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
         if (dims->mode < 0 || dims->mode > MOE_MODE_INT8 || dims->num_tokens < 0 || dims->num_experts < 1 || dims->top_k < 1 ||
             dims->d_hidden <= 0 || dims->d_expert <= 0 ||
             (dims->weight_layout != MOE_WEIGHTS_ROW_MAJOR && dims->weight_layout != MOE_WEIGHTS_PACKED) ||
-            (dims->activation != MOE_ACT_SWIGLU && dims->activation != MOE_ACT_SWIGLU_CLAMPED))
+            (dims->activation != MOE_ACT_SWIGLU && dims->activation != MOE_ACT_SWIGLU_CLAMPED) ||
+            (dims->launch != MOE_LAUNCH_MULTI && dims->launch != MOE_LAUNCH_SINGLE))
             return MOE_ERR_INVALID_ARG;
         return MOE_ERR_UNSUPPORTED;
     }
     const int mode = dims->mode;
     const int64_t T = dims->num_tokens;
     if (T == 0) return MOE_OK;
+    const bool single = dims->launch == MOE_LAUNCH_SINGLE;
+    if (single && !single_ok(dims)) return MOE_ERR_UNSUPPORTED;
     if (!x || !topk_ids || !topk_w || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out) || !aligned16(topk_ids) ||
         !aligned16(topk_w))
@@ -251,9 +275,56 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
 
     int cus = 0, occ1 = 1, occ2 = 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (single) {
+        int occ = 1;
+        if (device_info(mode, false, &cus, &occ1, &occ2, &occ) != hipSuccess) return MOE_ERR_HIP;
+        const int64_t N = T * dims->top_k;
+        const int64_t E = dims->num_experts;
+        const int mtb = layer_mtile_blocks(mode);
+        // at most one workgroup per task
+        const int64_t mtiles = L.tile_cap / mtb + std::min<int64_t>(E, N);
+        const int64_t tasks = mtiles * (dims->d_expert / L.block_n1 + dims->d_hidden / L.block_n2);
+        const int grid = (int)std::max<int64_t>(std::min<int64_t>(tasks, (int64_t)cus * occ), 1);
+        LayerArgs la{};
+        la.g1.x = x;
+        la.g1.x_scale = mode_fp8(mode) ? scales->x_scale : nullptr;
+        la.g1.w1 = w1;
+        la.g1.w1_scale = mode_fp8(mode) ? scales->w1_scale : nullptr;
+        la.g1.h = at<void>(workspace, L.h);
+        la.g1.h_scale = mode_fp8(mode) ? at<unsigned char>(workspace, L.h_scale) : nullptr;
+        la.g1.topk_w = topk_w;
+        la.g1.k = dims->top_k;
+        la.g1.d_h = dims->d_hidden;
+        la.g1.d_e = dims->d_expert;
+        la.g1.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
+        la.g1.act = dims->activation;
+        la.g2.h = la.g1.h;
+        la.g2.h_scale = la.g1.h_scale;
+        la.g2.w2 = w2;
+        la.g2.w2_scale = mode_fp8(mode) ? scales->w2_scale : nullptr;
+        la.g2.y = at<void>(workspace, L.y);
+        la.g2.d_h = dims->d_hidden;
+        la.g2.d_e = dims->d_expert;
+        la.g2.packed = la.g1.packed;
+        la.ids = topk_ids;
+        la.sync = at<int32_t>(workspace, L.sync);
+        la.out = out;
+        la.T = (int32_t)T;
+        la.N = (int32_t)N;
+        la.E = dims->num_experts;
+        la.k = dims->top_k;
+        la.nb1 = dims->d_expert / L.block_n1;
+        la.nb2 = dims->d_hidden / L.block_n2;
+        hipEvent_t e0 = events ? static_cast<hipEvent_t>(events[0]) : nullptr;
+        hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+        if (launch_layer(mode, la, grid, s, e0, e1) != hipSuccess) return MOE_ERR_HIP;
+        for (int i = 2; events && i < 8; ++i)
+            if (hipEventRecord(static_cast<hipEvent_t>(events[i]), s) != hipSuccess) return MOE_ERR_HIP;
+        return MOE_OK;
+    }
     const bool wide = fp8_wide(mode, T, dims->top_k, dims->d_hidden, dims->d_expert);
     if (device_info(mode, wide, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
-    hipStream_t s = static_cast<hipStream_t>(stream);
     // timing events of launch i (route, GEMM-1, GEMM-2, combine), or none
     auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
     const int32_t E = dims->num_experts, k = dims->top_k, d_h = dims->d_hidden, d_e = dims->d_expert;
@@ -398,6 +469,13 @@ static void bwd_layout_of(const moe_dims* d, BwdLayout* L) {
 static bool bwd_dims_ok(const moe_dims* d) {
     return dims_ok(d) && d->mode == MOE_MODE_BF16 && d->weight_layout == MOE_WEIGHTS_ROW_MAJOR &&
            d->activation == MOE_ACT_SWIGLU;
+}
+
+int moe_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace || workspace_bytes < MOE_SYNC_BYTES || ((uintptr_t)workspace & (kAlign - 1))) return MOE_ERR_WORKSPACE;
+    if (launch_sync_clear(static_cast<int32_t*>(workspace), static_cast<hipStream_t>(stream)) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
 }
 
 int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void* w1_packed, void* w2_packed,

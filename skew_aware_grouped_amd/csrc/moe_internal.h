@@ -91,7 +91,7 @@ __host__ __device__ inline int static_tasks(int grid, int x, int seg_len) {
 // a whole 128-column requantisation group of the intermediate and a single
 // block row of W1's scales; bf16 GEMM-1 uses 64; GEMM-2 uses 128 (one W2
 // scale block row).
-inline bool mode_fp8(int mode) { return mode == MOE_MODE_FP8 || mode == MOE_MODE_MXFP8; }  // e4m3 operands
+constexpr bool mode_fp8(int mode) { return mode == MOE_MODE_FP8 || mode == MOE_MODE_MXFP8; }  // e4m3 operands
 // The GEMM kernels of a mode: INT8 tokens run the bf16 GEMMs on their widened codes
 inline int gemm_mode(int mode) { return mode == MOE_MODE_INT8 ? MOE_MODE_BF16 : mode; }
 inline int gemm1_block_n(int mode) { return mode_fp8(mode) ? 128 : 64; }
@@ -151,6 +151,42 @@ struct Gemm2Args {
     int32_t packed;  // W2 in the packed tile order
 };
 
+// ---------------------------------------------------------- single launch
+// moe_dims.launch == MOE_LAUNCH_SINGLE: the whole layer in one persistent
+// kernel (moe_layer.hip).  Its envelope: BF16, FP8 or MXFP8 data, at most
+// kLayerMaxN routed assignments, T * (d_h / 128) at most kSyncArriveWords.
+constexpr int kLayerMaxN = 2048;
+// M-tiles of the single launch, in group blocks: 128 rows in the bf16 modes,
+// 64 in the FP8 ones (their GEMM-1 task requantises h, which costs more per
+// row at 128 rows)
+inline int layer_mtile_blocks(int mode) { return mode_fp8(mode) ? kSmallRowBlocks : kMaxRowBlocks1; }
+// Synchronisation block at the start of every workspace (int32 words), the
+// same size for all dims so that no call's other sections ever overlap it.
+// It holds zeros before the first single-launch call on a workspace and every
+// such call leaves it zero: the queue and exit counters and the M-tile
+// counters are reset by the last workgroup to finish, each arrival counter by
+// the workgroup that completes it.  The four-launch path never touches it.
+enum {
+    kSyncQueue = 0,        // task queue counter (own 128-byte line)
+    kSyncExit = 32,        // workgroups finished
+    kSyncTimeouts = 64,    // bounded waits that ran out (diagnostic, never reset by the kernel)
+    kSyncZero = 96,        // 256 bytes of zeros: padding rows read their operand here
+    kSyncDone = 256,       // [group block] GEMM-1 column blocks stored for the M-tile starting there
+    kSyncDoneWords = 512,  // >= (kLayerMaxN + kMaxExperts * 15) / 16
+    kSyncArrive = kSyncDone + kSyncDoneWords,  // [token * (d_h / 128) + column block] y rows stored
+    kSyncArriveWords = 65536,
+    kSyncWords = kSyncArrive + kSyncArriveWords
+};
+
+struct LayerArgs {
+    Gemm1Args g1;  // x, x_scale, w1, w1_scale, h, h_scale, topk_w, k, d_h, d_e, packed, act
+    Gemm2Args g2;  // h, h_scale, w2, w2_scale, y (fp32 [T*k, d_h]), d_h, d_e, packed
+    const int32_t* ids;
+    int32_t* sync;  // kSyncWords
+    void* out;      // bf16 [T, d_h]
+    int32_t T, N, E, k, nb1, nb2;
+};
+
 struct CombineArgs {
     const void* y;
     const int32_t* ids;
@@ -194,6 +230,13 @@ hipError_t launch_bwd_act(const float* GU, const float* Q, const int32_t* row_sr
                           hipStream_t s);
 hipError_t launch_bwd_dx(const float* dXp, const int32_t* ppos, const int32_t* ids, float* dx, float* dtopk_w, int T,
                          int k, int E, int d_h, hipStream_t s);
+
+// The single-launch layer kernel (grid: at most its resident capacity) and its
+// occupancy; sync_clear zeroes a synchronisation block.
+hipError_t launch_layer(int mode, const LayerArgs& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
+                        hipEvent_t t1 = nullptr);
+hipError_t layer_occupancy(int mode, int* blocks_per_cu);
+hipError_t launch_sync_clear(int32_t* sync, hipStream_t s);
 
 // Resident workgroups per CU of the persistent GEMM kernels (occupancy query;
 // wide: the 8-wave FP8 GEMM-1).

@@ -48,11 +48,11 @@ def upload(w: MoEWorkload, device="cuda:0", packed: bool = False) -> dict:
     return d
 
 
-def run(d: dict, out=None, workspace=None, stream=None, events=None):
+def run(d: dict, out=None, workspace=None, stream=None, events=None, launch=moe.MOE_LAUNCH_MULTI):
     return moe.fused_forward(d["x"], d["topk_ids"], d["topk_w"], d["w1"], d["w2"], out=out, x_scale=d["x_scale"],
                              w1_scale=d["w1_scale"], w2_scale=d["w2_scale"], workspace=workspace, stream=stream,
                              events=events, weight_layout=d.get("weight_layout", moe.MOE_WEIGHTS_ROW_MAJOR),
-                             activation=d.get("activation", moe.MOE_ACT_SWIGLU))
+                             activation=d.get("activation", moe.MOE_ACT_SWIGLU), launch=launch)
 
 
 def out_to_f64(out) -> np.ndarray:

@@ -37,11 +37,17 @@ MOE_WEIGHTS_PACKED = 1
 MOE_ACT_SWIGLU = 0
 MOE_ACT_SWIGLU_CLAMPED = 1
 
+MOE_LAUNCH_MULTI = 0
+MOE_LAUNCH_SINGLE = 1
+MOE_SYNC_BYTES = 265216
+# int32 word of the synchronisation block counting single-launch waits that ran out
+SYNC_TIMEOUTS_WORD = 64
+
 
 class moe_dims(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("num_tokens", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("d_hidden", ctypes.c_int32), ("d_expert", ctypes.c_int32),
-                ("weight_layout", ctypes.c_int32), ("activation", ctypes.c_int32)]
+                ("weight_layout", ctypes.c_int32), ("activation", ctypes.c_int32), ("launch", ctypes.c_int32)]
 
 
 class moe_scales(ctypes.Structure):
@@ -57,7 +63,7 @@ class moe_ws_layout(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_size_t) for n in ("counts", "offsets", "padded_offsets", "pos", "sorted_p", "ppos",
                                                  "row_src", "row_w", "tile_expert", "tile_row0", "stats", "tasks1",
                                                  "tasks2",
-                                                 "h", "h_scale", "y", "zero", "x_bf16", "total")]
+                                                 "h", "h_scale", "y", "zero", "x_bf16", "sync", "total")]
                 + [(n, ctypes.c_int64) for n in ("n_pad_cap", "tile_cap", "task1_cap", "task2_cap")]
                 + [(n, ctypes.c_int32) for n in ("block_n1", "block_n2", "max_row_blocks")])
 
@@ -94,6 +100,8 @@ def lib():
     L.moe_backward_workspace_bytes.argtypes = [P(moe_dims)]
     L.moe_fused_backward.restype = ctypes.c_int
     L.moe_fused_backward.argtypes = [P(moe_dims), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.moe_workspace_init.restype = ctypes.c_int
+    L.moe_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
     L.moe_pack_weights.restype = ctypes.c_int
     L.moe_pack_weights.argtypes = [P(moe_dims), vp, vp, vp, vp, vp]
     L.moe_block_m.restype = ctypes.c_int32
@@ -150,6 +158,10 @@ def moe_fused_backward(dims, x, topk_ids, topk_w, w1, w2, dout, dx, dw1, dw2, dt
                        stream) -> int:
     return int(lib().moe_fused_backward(ctypes.byref(dims) if dims is not None else None, x, topk_ids, topk_w, w1, w2,
                                         dout, dx, dw1, dw2, dtopk_w, workspace, workspace_bytes, stream))
+
+
+def moe_workspace_init(workspace, workspace_bytes, stream) -> int:
+    return int(lib().moe_workspace_init(workspace, workspace_bytes, stream))
 
 
 def moe_pack_weights(dims, w1, w2, w1_packed, w2_packed, stream) -> int:
@@ -214,7 +226,8 @@ def workspace_for(dims: moe_dims, device, stream=None):
     stream (the routing counters, task queues and intermediates in it are
     rewritten by every call), so two streams never get the same buffer.  The
     tensor is allocated on that stream, so torch's allocator does not reuse
-    its memory while work queued there may still read it."""
+    its memory while work queued there may still read it.  It starts zeroed,
+    which the single launch needs of its synchronisation block."""
     import torch
     need = moe_workspace_bytes(dims)
     dev = torch.device(device)
@@ -225,19 +238,19 @@ def workspace_for(dims: moe_dims, device, stream=None):
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
         with torch.cuda.stream(s):
-            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
 
 def make_dims(x, topk_ids, w1, mode: Optional[int] = None, weight_layout: int = MOE_WEIGHTS_ROW_MAJOR,
-              x_scale=None, activation: int = MOE_ACT_SWIGLU) -> moe_dims:
+              x_scale=None, activation: int = MOE_ACT_SWIGLU, launch: int = MOE_LAUNCH_MULTI) -> moe_dims:
     T, d_h = x.shape
     E, two_de, d_h2 = w1.shape
     assert d_h2 == d_h and two_de % 2 == 0, "w1 must be [E, 2*d_expert, d_hidden]"
     return moe_dims(mode=_mode_of(x, w1, x_scale) if mode is None else mode, num_tokens=T, num_experts=E,
                     top_k=topk_ids.shape[1], d_hidden=d_h, d_expert=two_de // 2, weight_layout=weight_layout,
-                    activation=activation)
+                    activation=activation, launch=launch)
 
 
 def pack_weights(w1, w2, stream=None):
@@ -262,16 +275,20 @@ def pack_weights(w1, w2, stream=None):
 
 def fused_forward(x, topk_ids, topk_w, w1, w2, out=None, x_scale=None, w1_scale=None, w2_scale=None,
                   workspace=None, stream=None, events=None, weight_layout=MOE_WEIGHTS_ROW_MAJOR,
-                  activation=MOE_ACT_SWIGLU):
+                  activation=MOE_ACT_SWIGLU, launch=MOE_LAUNCH_MULTI):
     """Run ``moe_fused_forward`` on torch device tensors; returns ``out``.  With
     ``events`` (8 torch.cuda.Event objects: start and end of the routing, GEMM-1,
     GEMM-2 and combine kernels) the kernel-timing variant is used.  With
     ``weight_layout=MOE_WEIGHTS_PACKED``, w1 and w2 are ``pack_weights`` outputs.
     e4m3 weights take fp32 block scales (FP8 mode) or uint8 E8M0 scales per 32
     values (MXFP8 mode); the dtype of ``x_scale`` selects the mode.  int8 ``x``
-    (INT8 mode) takes bf16 weights and one fp32 ``x_scale`` per token."""
+    (INT8 mode) takes bf16 weights and one fp32 ``x_scale`` per token.
+    ``launch=MOE_LAUNCH_SINGLE`` runs the layer as one kernel; a workspace
+    passed in must then have had its synchronisation block zeroed once
+    (``moe_workspace_init``; the cached workspaces are allocated zeroed)."""
     import torch
-    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout, x_scale=x_scale, activation=activation)
+    dims = make_dims(x, topk_ids, w1, weight_layout=weight_layout, x_scale=x_scale, activation=activation,
+                     launch=launch)
     if out is None:
         odt = torch.float32 if dims.mode == MOE_MODE_F32ACT else torch.bfloat16
         out = torch.empty(x.shape[0], x.shape[1], dtype=odt, device=x.device)

@@ -24,17 +24,18 @@ def test_block_m_and_caps():
 
 
 def _dims(mode=moe.MOE_MODE_FP8, T=1024, E=32, k=2, d_h=7168, d_e=2048, layout=moe.MOE_WEIGHTS_ROW_MAJOR,
-          act=moe.MOE_ACT_SWIGLU):
+          act=moe.MOE_ACT_SWIGLU, launch=moe.MOE_LAUNCH_MULTI):
     return moe.moe_dims(mode=mode, num_tokens=T, num_experts=E, top_k=k, d_hidden=d_h, d_expert=d_e,
-                        weight_layout=layout, activation=act)
+                        weight_layout=layout, activation=act, launch=launch)
 
 
 def test_workspace_layout_is_disjoint_and_aligned():
     for mode in (0, 1, 2, 3, 4):
         d = _dims(mode=mode)
         L = moe.moe_workspace_layout(d)
-        offs = [L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.row_w, L.tile_expert,
-                L.tile_row0, L.stats, L.tasks1, L.tasks2, L.h, L.h_scale, L.y, L.zero, L.x_bf16, L.total]
+        offs = [L.sync, L.counts, L.offsets, L.padded_offsets, L.pos, L.sorted_p, L.ppos, L.row_src, L.row_w,
+                L.tile_expert, L.tile_row0, L.stats, L.tasks1, L.tasks2, L.h, L.h_scale, L.y, L.zero, L.x_bf16,
+                L.total]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
         N = 2048
         assert L.pos - L.ppos <= 0 and L.sorted_p - L.pos >= 4 * N
@@ -123,3 +124,28 @@ def test_noalloc_rejects_oversize_before_any_device_call():
     assert rc == moe.MOE_ERR_SCRATCH
     assert "scratch" in moe.moe_error_string(rc)
     assert moe.moe_fused_forward_noalloc(None, p, p, p, p, p, None, p, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_single_launch_layout_and_envelope():
+    """The synchronisation block sits first, at the same place and size for all
+    dims; the single launch keeps y in fp32; outside its envelope (F32ACT and
+    INT8 modes, more than 2048 assignments, T * d_h / 128 above 65536) the call
+    is rejected before any pointer or device is touched."""
+    for mode in (1, 2, 3):
+        for T, d_h in ((64, 256), (1024, 7168)):
+            m = moe.moe_workspace_layout(_dims(mode=mode, T=T, d_h=d_h))
+            s = moe.moe_workspace_layout(_dims(mode=mode, T=T, d_h=d_h, launch=moe.MOE_LAUNCH_SINGLE))
+            assert m.sync == s.sync == 0 and m.counts == s.counts == moe.MOE_SYNC_BYTES
+            assert s.x_bf16 - s.zero == m.x_bf16 - m.zero
+            N = T * 2
+            assert m.zero - m.y >= 2 * N * d_h and s.zero - s.y >= 4 * N * d_h
+    null = (None,) * 6 + (None, None, None, 0, None)
+    for mode, T, d_h in ((0, 64, 256), (4, 64, 256), (1, 1025, 256), (2, 1024, 8320)):
+        d = _dims(mode=mode, T=T, d_h=d_h, launch=moe.MOE_LAUNCH_SINGLE)
+        assert moe.moe_fused_forward(d, *null[1:]) == moe.MOE_ERR_UNSUPPORTED, (mode, T, d_h)
+    d = _dims(launch=2)
+    assert moe.moe_workspace_bytes(d) == 0
+    assert moe.moe_fused_forward(d, *null[1:]) == moe.MOE_ERR_INVALID_ARG
+    assert moe.moe_workspace_init(None, moe.MOE_SYNC_BYTES, None) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_workspace_init(256, moe.MOE_SYNC_BYTES - 4, None) == moe.MOE_ERR_WORKSPACE
+    assert moe.moe_workspace_init(256 + 16, moe.MOE_SYNC_BYTES, None) == moe.MOE_ERR_WORKSPACE
