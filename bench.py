@@ -18,7 +18,12 @@ The weights are rewritten once, before any timing, into the packed tile order
 (moe_pack_weights), as a deployment does when it loads them; ``--weights
 row-major`` times the layer on the weights as given instead.
 
+``--launch single`` times the single-launch form (the whole layer in one
+persistent kernel, moe_dims.launch = MOE_LAUNCH_SINGLE); the roofline is then
+the whole layer's, that kernel being the only one.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--weights packed|row-major] [--no-cpu]
+                    [--launch multi|single]
     python bench.py --pass backward --config qwen_bf16   (the backward with recompute)
 """
 import argparse
@@ -58,7 +63,7 @@ def gemm1_alg_bytes(w):
     return float(b)
 
 
-KERNEL_SOURCES = ["moe_gemm.hip", "moe_internal.h", "moe_route.hip"]
+KERNEL_SOURCES = ["moe_gemm.hip", "moe_gemm_task.h", "moe_internal.h", "moe_route.hip", "moe_layer.hip"]
 
 
 def kernel_source_hash():
@@ -235,6 +240,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline leg")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward",
                     help="backward: time moe_fused_backward (BF16 workloads, e.g. --config qwen_bf16)")
+    ap.add_argument("--launch", choices=["multi", "single"], default="multi",
+                    help="single: the whole layer as one persistent kernel (BF16/FP8/MXFP8, <= 2048 assignments)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="only run a plain copy of this many MiB (for scaling profiler byte counters)")
     args = ap.parse_args()
@@ -254,15 +261,21 @@ def main():
         copy_calibration(args.copy_calibration_mb)
         return
     w = W.config(args.config)
+    single = args.launch == "single"
+    launch = moe.MOE_LAUNCH_SINGLE if single else moe.MOE_LAUNCH_MULTI
     d = device.upload(w, packed=args.weights == "packed")
-    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], weight_layout=d["weight_layout"], x_scale=d["x_scale"])
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], weight_layout=d["weight_layout"], x_scale=d["x_scale"],
+                         launch=launch)
     ws = moe.workspace_for(dims, "cuda:0")
+
+    def run(**kw):
+        return device.run(d, out=out, workspace=ws, launch=launch, **kw)
     odt = torch.float32 if w.mode == W.MODE_F32ACT else torch.bfloat16
     out = torch.empty(w.T, w.d_h, dtype=odt, device="cuda:0")
 
     # correctness gate before timing: a few sampled rows against the oracle
     from oracle import moe_oracle
-    device.run(d, out=out, workspace=ws)
+    run()
     torch.cuda.synchronize()
     rows = sorted(set(np.random.default_rng(1).choice(w.T, size=min(8, w.T), replace=False).tolist()))
     acc, _ = moe_oracle.forward(w, rows=rows)
@@ -274,7 +287,7 @@ def main():
         sys.exit(1)
 
     for _ in range(args.warmup):
-        device.run(d, out=out, workspace=ws)
+        run()
     stream = torch.cuda.current_stream()
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
 
@@ -290,7 +303,7 @@ def main():
             if cold:
                 flush.sum()
             a.record(stream)
-            device.run(d, out=out, workspace=ws, stream=stream)
+            run(stream=stream)
             b.record(stream)
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in evs]), time.perf_counter() - t0
@@ -302,7 +315,7 @@ def main():
         for i in range(n):
             if cold:
                 flush.sum()
-            device.run(d, out=out, workspace=ws, stream=stream, events=ev[i])
+            run(stream=stream, events=ev[i])
         torch.cuda.synchronize()
         return np.array([[e[2 * j].elapsed_time(e[2 * j + 1]) for j in range(4)] for e in ev])
 
@@ -318,28 +331,31 @@ def main():
     flops = W.flops(w)
     alg_bytes = W.algorithmic_bytes(w)
     tflops = flops / (p50 * 1e-3) / 1e12
-    stages = {n: round(float(np.mean(stage_ms[:, j])) * 1e3, 2) for j, n in
-              enumerate(["route", "gemm1_swiglu", "gemm2_weight", "combine"])}
+    names = ["layer_kernel"] if single else ["route", "gemm1_swiglu", "gemm2_weight", "combine"]
+    stages = {n: round(float(np.mean(stage_ms[:, j])) * 1e3, 2) for j, n in enumerate(names)}
     layer_gbs = alg_bytes / (p50 * 1e-3) / 1e9
-    # dominant kernel: GEMM-1 (gate|up + SwiGLU), two thirds of the weights and FLOPs
-    k_us = float(np.mean(stage_ms[:, 1])) * 1e3
-    g1_bytes = gemm1_alg_bytes(w)
-    g1_flops = 4.0 * w.d_h * w.d_e * w.valid_assignments()
+    # dominant kernel: GEMM-1 (gate|up + SwiGLU), two thirds of the weights and
+    # FLOPs; in the single launch, the one kernel and the whole layer's work
+    kj = 0 if single else 1
+    kname = "layer_kernel" if single else "gemm1_kernel"
+    k_us = float(np.mean(stage_ms[:, kj])) * 1e3
+    g1_bytes = alg_bytes if single else gemm1_alg_bytes(w)
+    g1_flops = flops if single else 4.0 * w.d_h * w.d_e * w.valid_assignments()
     k_gbs = g1_bytes / (k_us * 1e-6) / 1e9
     k_tflops = g1_flops / (k_us * 1e-6) / 1e12
     peak_f = PEAK_TFLOPS[w.mode]
     if g1_flops / (peak_f * 1e12) > g1_bytes / (PEAK_HBM_GBS * 1e9):
-        roof = {"kernel": "gemm1_kernel", "bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak_f,
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(k_tflops, 2), "peak": peak_f,
                 "unit": "TFLOP/s", "frac": round(k_tflops / peak_f, 4)}
     else:
-        roof = {"kernel": "gemm1_kernel", "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(k_gbs, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(k_gbs / PEAK_HBM_GBS, 4)}
-    roof.update({"traffic": measured_traffic("gemm1_kernel", w.name, args.weights), "alg_bytes_per_launch": g1_bytes,
+    roof.update({"traffic": measured_traffic(kname, w.name, args.weights), "alg_bytes_per_launch": g1_bytes,
                  "alg_flops_per_launch": g1_flops, "avg_launch_us": round(k_us, 2),
                  "avg_launch_source": f"mean of {len(stage_ms)} dispatch-event durations on the library's "
                                       f"stream ({args.steps} after a cache flush, {args.steps} warm)",
-                 "avg_launch_us_cold": round(float(np.mean(stage_ms[:args.steps, 1])) * 1e3, 2),
-                 "avg_launch_us_warm": round(float(np.mean(stage_ms[args.steps:, 1])) * 1e3, 2)})
+                 "avg_launch_us_cold": round(float(np.mean(stage_ms[:args.steps, kj])) * 1e3, 2),
+                 "avg_launch_us_warm": round(float(np.mean(stage_ms[args.steps:, kj])) * 1e3, 2)})
     res = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -357,7 +373,7 @@ def main():
         "config": {"workload": w.name, "tokens": w.T, "experts": w.E, "top_k": w.k, "d_hidden": w.d_h,
                    "d_expert": w.d_e, "active_experts": w.active_experts(),
                    "valid_assignments": w.valid_assignments(), "routing": str(w.meta.get("routing")),
-                   "weight_layout": args.weights},
+                   "weight_layout": args.weights, "launch": args.launch},
         "p50_us": round(p50 * 1e3, 2),
         "p10_us": round(float(np.percentile(cold_ms, 10)) * 1e3, 2),
         "p90_us": round(float(np.percentile(cold_ms, 90)) * 1e3, 2),

@@ -436,106 +436,22 @@ struct Cfg {
 //     epilogue scales by topk_w[row_src[r]] and writes y[row_src[r]][cb*kBN ..].
 // K is the contraction length (d_h or d_e); N_out is d_e (GATED) or d_h.
 // Single-launch form (FUSED): the task runs inside the one persistent grid of
-// the layer.  GEMM-1 stores h (and its scales) with device-scope stores, waits
-// for them and then adds 1 to done1 at its M-tile's first group block; GEMM-2
-// first requests its weight stages, waits (bounded) until that counter equals
-// the number of GEMM-1 column blocks, then loads h with device-scope loads,
-// keeps y in fp32, and after its y stores have completed counts each row's
-// arrival at (token, column block): the workgroup that brings a count to the
-// token's number of valid slots sums that token's y rows in ascending slot
-// order and writes the output columns (tilelang.dataflow README section 3.5:
-// GEMM-1 and GEMM-2 under one wrapper launch, the dependency resolved without
-// a kernel boundary).
+// the layer (tilelang.dataflow README section 3.5: GEMM-1 and GEMM-2 under one
+// wrapper launch, the dependency resolved without a kernel boundary).  GEMM-1
+// stores h (and its scales) with device-scope stores, waits for them, then adds
+// 1 to the counter of the GEMM-2 M-tile its rows belong to.  GEMM-2 first
+// requests its weight stages, waits (bounded) until that counter reaches every
+// column block of every GEMM-1 M-tile in it, then loads h with device-scope
+// loads; it keeps y in fp32 and returns once its y stores are complete (the
+// layer kernel then combines).
 struct FusedCtx {
-    int32_t* done1;     // [group block]: GEMM-1 column blocks stored for the M-tile starting there
-    int32_t* arrive;    // [token * nb2 + column block]: y rows stored; back to 0 once combined
+    int32_t* done;      // this task's GEMM-2 M-tile counter: GEMM-1 column blocks that stored their h rows
+    int32_t target;     // GEMM-2: the count that means all of its h rows are stored
     int32_t* timeouts;  // waits that ran out (diagnostic; each such task went on)
-    const uint64_t* bad;  // LDS: bit p set when assignment p's id is outside [0, E)
-    void* out;            // bf16 [T, d_h]
-    int32_t nb1, nb2, k, d_h;
 };
 // polls of a bounded wait (each a device-scope load and a short sleep):
 // far longer than any GEMM-1 task, so only a broken schedule reaches it
 constexpr int kSpinLimit = 1 << 18;
-
-// The combine step of a single-launch GEMM-2 task (see FusedCtx): the y rows
-// of every token this task completed, for column block cb, come into LDS with
-// device-scope direct-to-LDS loads (one 16-byte piece per lane, 32 pieces of a
-// 128-column fp32 row), then each (token, 4 columns) is summed in ascending
-// slot order from +0.0, rounded once to bf16 and stored; the arrival counters
-// go back to 0.
-template <int NSUB, int RING>
-__device__ __forceinline__ void fused_combine(const FusedCtx* fx, const int* rows, int cb, const float* y,
-                                              const unsigned char* zero, unsigned char* smem) {
-    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int k = fx->k;
-    int* s_n = reinterpret_cast<int*>(smem);
-    int* s_list = s_n + 16;  // up to 16 * NSUB tokens
-    if (tid == 0) *s_n = 0;
-    lds_barrier();
-    if (tid < 16 * NSUB) {
-        const int p = rows[tid];
-        if (p >= 0) {
-            const int t = p / k;
-            int nv = 0;
-            for (int j = 0; j < k; ++j) {
-                const int q = t * k + j;
-                nv += !((fx->bad[q >> 6] >> (q & 63)) & 1ull);
-            }
-            const int old = __hip_atomic_fetch_add(fx->arrive + (int64_t)t * fx->nb2 + cb, 1, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (old + 1 == nv) s_list[atomicAdd(s_n, 1)] = t;
-        }
-    }
-    lds_barrier();
-    const int n = *s_n;
-    // pieces: (token u of the list, slot j, 16-byte piece c) -> LDS slot (u*k + j)*32 + c
-    constexpr int kListBytes = 64 + 4 * 16 * NSUB;
-    unsigned char* buf = smem + (kListBytes + 15) / 16 * 16;
-    // tokens per batch; a wave's load fills 64 pieces, so a batch keeps 64
-    // pieces of room past its last one
-    const int per_batch = (RING - (int)(buf - smem) - 64 * 16) / (k * 512);
-    for (int u0 = 0; u0 < n; u0 += per_batch) {
-        const int nu = n - u0 < per_batch ? n - u0 : per_batch;
-        const int slots = nu * k * 32;
-        for (int s0 = 64 * w; s0 < slots; s0 += 64 * kGemmWaves) {
-            const int sl = s0 + lane;
-            const void* src = zero;
-            if (sl < slots) {
-                const int tj = sl >> 5, c = sl & 31;
-                const int t = s_list[u0 + tj / k], j = tj - tj / k * k;
-                const int q = t * k + j;
-                if (!((fx->bad[q >> 6] >> (q & 63)) & 1ull))
-                    src = y + (int64_t)q * fx->d_h + cb * 128 + 4 * c;
-            }
-            g2l16c(src, lds_offset(buf + 16 * s0));
-        }
-        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
-        lds_barrier();
-        for (int i = tid; i < nu * 32; i += kGemmThreads) {
-            const int uu = i >> 5, c = i & 31;
-            const int t = s_list[u0 + uu];
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-            for (int j = 0; j < k; ++j) {
-                const int q = t * k + j;
-                if ((fx->bad[q >> 6] >> (q & 63)) & 1ull) continue;
-                const float4 v = *reinterpret_cast<const float4*>(buf + 16 * ((uu * k + j) * 32 + c));
-                a0 += v.x;
-                a1 += v.y;
-                a2 += v.z;
-                a3 += v.w;
-            }
-            uint2 o;
-            o.x = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
-            o.y = f32_to_bf16(a2) | (f32_to_bf16(a3) << 16);
-            *reinterpret_cast<uint2*>(static_cast<unsigned short*>(fx->out) + (int64_t)t * fx->d_h + cb * 128 + 4 * c) = o;
-        }
-        lds_barrier();
-    }
-    for (int i = tid; i < n; i += kGemmThreads)
-        __hip_atomic_store(fx->arrive + (int64_t)s_list[i] * fx->nb2 + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();  // the list is read before the next task's loads land in the ring
-}
 
 template <int MODE, bool GATED, int NSUB, int RING, bool FUSED = false, class SCH = Sched>
 __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scale_v, const int32_t* row_src,
@@ -543,11 +459,14 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
                                           int e, int row0, int cb, int K, int N_out, bool packed,
                                           unsigned char* smem, const Gemm1Args* g1, const Gemm2Args* g2,
                                           SCH& sch, const int* rows, const float* roww, int par,
-                                          const FusedCtx* fx = nullptr) {
+                                          const FusedCtx* fx = nullptr, bool h_ready = false) {
     using C = Cfg<MODE, GATED, FUSED && !GATED>;
     constexpr bool kFP8 = C::kFP8, kBS = C::kBS, kMX = C::kMX;
-    // single-launch GEMM-2: weight loads first, h loads after the wait
+    // single-launch GEMM-2: h is read at device scope, and unless it was
+    // already complete when the task was claimed, the weight loads go first
+    // and the h loads after the wait
     constexpr bool kSplit = FUSED && !GATED;
+    const bool split = kSplit && !h_ready;
     const float* a_scale = static_cast<const float*>(a_scale_v);  // FP8 mode
     const float* w_scale = static_cast<const float*>(w_scale_v);
     constexpr int S = C::stages(NSUB, RING);
@@ -777,16 +696,15 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
 
     const int swz = lr & 7;
     const int npro = nk < S - 1 ? nk : S - 1;
-    if constexpr (kSplit) {
+    if (split) {
         for (int kc = 0; kc < npro; ++kc) issue_b(kc);
         // the scheduler wave (no stage loads of its own) waits until every
         // GEMM-1 column block of this M-tile has stored its h rows
         if (w == kSchedWave) {
-            const int32_t* flag = fx->done1 + row0 / kBlockM;
             for (int it = 0;; ++it) {
                 const int v = __builtin_amdgcn_readfirstlane(
-                    __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-                if (v >= fx->nb1) break;
+                    __hip_atomic_load(fx->done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+                if (v >= fx->target) break;
                 if (it >= kSpinLimit) {
                     if (lane == 0) __hip_atomic_fetch_add(fx->timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     break;
@@ -807,7 +725,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
         // (each loading wave waits for its own; the barrier covers the rest)
         if (loader) {
             int younger;
-            if (kSplit && kc < npro) {
+            if (split && kc < npro) {
                 // the prologue's A parts went out after all its weight parts:
                 // younger than stage kc are the A parts of the later prologue
                 // stages and the whole stages issued since
@@ -1138,10 +1056,7 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
     lds_barrier();  // the ring and the staging area are refilled by the next task
     if constexpr (FUSED) {
         if constexpr (GATED) {
-            if (threadIdx.x == 0)
-                __hip_atomic_fetch_add(fx->done1 + row0 / kBlockM, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            fused_combine<NSUB, RING>(fx, rows, cb, static_cast<const float*>(g2->y), zero, smem);
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(fx->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -171,7 +171,7 @@ enum {
     kSyncExit = 32,        // workgroups finished
     kSyncTimeouts = 64,    // bounded waits that ran out (diagnostic, never reset by the kernel)
     kSyncZero = 96,        // 256 bytes of zeros: padding rows read their operand here
-    kSyncDone = 256,       // [group block] GEMM-1 column blocks stored for the M-tile starting there
+    kSyncDone = 256,       // [group block] GEMM-1 column blocks stored for the GEMM-2 M-tile starting there
     kSyncDoneWords = 512,  // >= (kLayerMaxN + kMaxExperts * 15) / 16
     kSyncArrive = kSyncDone + kSyncDoneWords,  // [token * (d_h / 128) + column block] y rows stored
     kSyncArriveWords = 65536,

@@ -7,63 +7,70 @@
 //
 // Every workgroup first derives the routing plan itself, in LDS, from the ids
 // (section 3.5 step 1: group sizes, padded offsets, the expert of each group
-// block): the batches this form serves have at most kLayerMaxN assignments, so
-// reading them all per workgroup costs less than any grid-wide step.  The plan:
-//   counts per expert, 16-row group blocks, padded offsets in expert order (h
-//   rows live there, as in the four-launch layout), M-tiles of MT group blocks,
-//   experts ranked by descending count (ties by id), and one task list: every
-//   GEMM-1 task (rank, column block, M-tile), then every GEMM-2 task in the same
-//   order.
+// block, and the stable scatter): the batches this form serves have at most
+// kLayerMaxN assignments, so reading them all per workgroup costs less than
+// any grid-wide step.  The plan: counts per expert, 16-row group blocks,
+// padded offsets in expert order (h rows live there, as in the four-launch
+// layout), the assignment of every padded row, M-tiles of group blocks,
+// experts ranked by descending count (ties by id: the longest work first),
+// and one task list: every GEMM-1 task, then every GEMM-2 task, each by
+// rank, then column block, then M-tile.
 // Tasks are claimed in list order from one queue counter (the claim for a
 // workgroup's next task goes out during its current task's last K blocks).
 // GEMM-1 tasks never wait; a GEMM-2 task waits only on the GEMM-1 tasks of its
 // M-tile, all of lower index.  So the lowest unfinished claimed task can
 // always proceed, whether or not every workgroup of the grid is resident, and
-// each wait is bounded anyway.  The protocol (with the combine and the exit
-// reset described at FusedCtx and in the kernel) is modelled on the CPU and
-// checked there for coverage, dependency order and termination.
-//
-// The rows of a task are found by the scheduler wave: a ballot scan of the ids
-// kept in LDS (rank of each assignment within its expert, ascending p).
+// each wait is bounded anyway.  The combine needs no waiting at all: after its
+// y stores, a GEMM-2 task counts each row's arrival at (token, column block),
+// and the task whose arrival completes a token sums that token's slots.  The
+// protocol is modelled on the CPU and checked there for coverage, dependency
+// order and termination.
 #include "moe_gemm_task.h"
+#include "moe_wave.h"
 
 namespace moe {
 namespace {
 
 // routing plan of the call, the same in every workgroup
 struct FusedPlan {
-    uint64_t bad[kLayerMaxN / 64];    // bit p: assignment p's id is outside [0, E) (or p >= N)
-    unsigned char id8[kLayerMaxN];    // low 8 bits of each id (E <= 256)
-    short cnt[kMaxExperts];           // rows routed to each expert
-    short poff[kMaxExperts + 2];      // padded offsets, expert order
-    short moff[kMaxExperts + 2];      // M-tiles of the ranks before each rank
-    unsigned char order[kMaxExperts]; // expert of each rank
+    uint64_t bad[kLayerMaxN / 64];                          // bit p: id of p outside [0, E) (or p >= N)
+    int row_src[kLayerMaxN + kMaxExperts * (kBlockM - 1)];  // padded rows: assignment p, -1 on padding
+    int poff[kMaxExperts + 2];                              // padded offsets, expert order
+    int moff[2][kMaxExperts + 2];                           // per GEMM: M-tiles of the ranks before each rank
+    short cnt[kMaxExperts];                                 // rows routed to each expert
+    unsigned char order[kMaxExperts];                       // expert of each rank
 };
 
-// the workgroup's current task and the rows of the current and next task
+// the workgroup's current task and the routing weights of the current and next task's rows
 struct FusedQ {
     int slot;
-    int list;  // 0: GEMM-1, 1: GEMM-2
-    int pad[2];
+    int list;   // 0: GEMM-1, 1: GEMM-2
+    int ready;  // GEMM-2: its h was complete when the task was claimed
+    int pad;
     int4 task;  // {expert, first padded row, row blocks, column block}
-    int rows[2][kRowsLds];
     float roww[2][kRowsLds];
 };
 
-// ring of the layer kernel: the larger of its two GEMMs' rings, less what the
-// plan and the queue state take (two workgroups per CU in the bf16 modes, one
-// in the FP8 ones)
+// One workgroup per CU in every mode: the ring takes what the plan and the
+// queue state leave of the CU's LDS (up to eight stages of a one-block bf16
+// task, three of a 64-row FP8 GEMM-1 task): the loads a workgroup keeps in
+// flight are what bounds its streaming rate.
+//
+// M-tiles in group blocks: GEMM-1 128 rows in the bf16 modes, 64 in the FP8
+// ones (their requantising epilogue costs more per row at 128); GEMM-2 always
+// 128 rows, so a GEMM-2 M-tile holds one or two GEMM-1 M-tiles, aligned.
 template <int MODE>
 struct LayerCfg {
-    static constexpr int kMT = mode_fp8(MODE) ? kSmallRowBlocks : kMaxRowBlocks1;
-    static constexpr int kRing = mode_fp8(MODE) ? 153 * 1024 : Cfg<MODE, true>::kRing;
-    static_assert(kRing + (int)sizeof(FusedPlan) + (int)sizeof(FusedQ) <= (mode_fp8(MODE) ? 160 : 80) * 1024,
-                  "LDS budget");
+    static constexpr int kMT1 = mode_fp8(MODE) ? kSmallRowBlocks : kMaxRowBlocks1;
+    static constexpr int kMT2 = kMaxRowBlocks2;
+    static_assert(kMT2 % kMT1 == 0, "GEMM-1 M-tiles nest in GEMM-2 M-tiles");
+    static constexpr int kRing = 131 * 1024;
+    static_assert(kRing + (int)sizeof(FusedPlan) + (int)sizeof(FusedQ) <= 160 * 1024, "LDS budget");
 };
 
 // Largest r in [0, n) with off[r] <= v (off non-decreasing, v < off[n]):
 // never an entry without tasks
-__device__ __forceinline__ int upper_rank(const short* off, int n, int v) {
+__device__ __forceinline__ int upper_rank(const int* off, int n, int v) {
     int lo = 0, hi = n - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -79,77 +86,57 @@ __device__ __forceinline__ int upper_rank(const short* off, int n, int v) {
 // lane 0, then settle, load_rows and publish on the scheduler wave).
 struct FusedSched {
     int32_t* queue;
+    const int32_t* done1;
     const FusedPlan* pl;
     FusedQ* q;
     const float* topk_w;
-    int total, n1, nb1, nb2, mtb, E, Np;
+    int n1, total, nb1, nb2, mt1, mt2, E;
     int raw = -1;  // lane 0: the claimed index
     int slot = -1;
-    int e = 0, row0 = 0, nsub = 0, cb = 0, m = 0, list = 0;
+    int e = 0, row0 = 0, nsub = 0, cb = 0, list = 0, done = 0, need = 0;
 
     __device__ __forceinline__ void claim() {
         raw = __hip_atomic_fetch_add(queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // GEMM-1 column blocks that store the h rows of a GEMM-2 M-tile of ns
+    // group blocks: every column block of each GEMM-1 M-tile in it
+    __device__ __forceinline__ int done_target(int ns) const { return nb1 * ((ns + mt1 - 1) / mt1); }
     __device__ __forceinline__ void settle(bool) {
-        int s = __builtin_amdgcn_readfirstlane(raw);
+        const int s = __builtin_amdgcn_readfirstlane(raw);
         slot = (s >= 0 && s < total) ? s : -1;
         if (slot < 0) return;
+        // list 0 (GEMM-1) or 1 (GEMM-2); rank r owns the list's tasks
+        // [moff[r] * nb, moff[r + 1] * nb): column blocks, each with its
+        // M-tiles next to each other
         list = slot < n1 ? 0 : 1;
         const int j = list ? slot - n1 : slot;
         const int nb = list ? nb2 : nb1;
-        const int r = upper_rank(pl->moff, E, j / nb);
-        const int mt = pl->moff[r + 1] - pl->moff[r];
-        const int local = j - pl->moff[r] * nb;
+        const int* moff = pl->moff[list];
+        const int r = upper_rank(moff, E, j / nb);
+        const int mt = moff[r + 1] - moff[r];
+        const int local = j - moff[r] * nb;
         cb = local / mt;
-        m = local - cb * mt;
+        const int m = local - cb * mt;
         e = pl->order[r];
+        const int mtb = list ? mt2 : mt1;
         const int tiles = (pl->cnt[e] + kBlockM - 1) / kBlockM;
         row0 = pl->poff[e] + kBlockM * mtb * m;
         nsub = min(mtb, tiles - mtb * m);
-    }
-    // rows of the task: ranks [lo, lo + 16 nsub) of expert e's assignments
-    // (ascending p), -1 past its count; GEMM-2 also its routing weights
-    __device__ __forceinline__ void load_rows(int par) {
-        if (slot < 0) return;
-        const int lane = threadIdx.x & 63;
-        int* rows = q->rows[par];
-        const int lo = kBlockM * mtb * m, n = kBlockM * nsub;
-        const int cnt = pl->cnt[e];
-        const int hi = min(lo + n, cnt);
-        const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
-        int base = 0;
-        for (int p0 = 0; p0 < Np && base < hi; p0 += 256) {
-            const int p = p0 + 4 * lane;
-            const unsigned w4 = *reinterpret_cast<const unsigned*>(&pl->id8[p]);
-            const unsigned b4 = (unsigned)(pl->bad[p >> 6] >> (p & 63)) & 0xFu;
-            unsigned mine = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                mine |= ((((w4 >> (8 * i)) & 0xFFu) == (unsigned)e) && !((b4 >> i) & 1u)) ? (1u << i) : 0u;
-            int below = 0, all = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint64_t bal = __ballot((mine >> i) & 1u);
-                below += __popcll(bal & lt);
-                all += __popcll(bal);
-            }
-            int r = base + below;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if ((mine >> i) & 1u) {
-                    if (r >= lo && r < hi) rows[r - lo] = p + i;
-                    ++r;
-                }
-            base += all;
-        }
-        for (int r = lane; r < n; r += 64)
-            if (lo + r >= cnt) rows[r] = -1;
         if (list == 1) {
-            // routing weight of each row (direct-to-LDS; padding rows read entry 0, never used)
-            for (int j = 0; j < n; j += 64) {
-                const int p = j + lane < n ? rows[j + lane] : -1;
-                g2l4(topk_w + (p > 0 ? p : 0), lds_offset(&q->roww[par][j]));
-            }
+            need = done_target(nsub);
+            done = __hip_atomic_load(done1 + row0 / kBlockM, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // the task's rows are the plan's padded rows [row0, row0 + 16 nsub); a
+    // GEMM-2 task also needs their routing weights (direct-to-LDS; padding
+    // rows read entry 0, never used)
+    __device__ __forceinline__ void load_rows(int par) {
+        if (slot < 0 || list != 1) return;
+        const int lane = threadIdx.x & 63;
+        const int n = kBlockM * nsub;
+        for (int j = 0; j < n; j += 64) {
+            const int p = j + lane < n ? pl->row_src[row0 + j + lane] : -1;
+            g2l4(topk_w + (p > 0 ? p : 0), lds_offset(&q->roww[par][j]));
         }
     }
     __device__ __forceinline__ void publish() {
@@ -158,79 +145,207 @@ struct FusedSched {
         if ((threadIdx.x & 63) == 0) {
             q->slot = slot;
             q->list = list;
+            q->ready = list == 1 && done >= need;
             if (slot >= 0) q->task = make_int4(e, row0, nsub, cb);
         }
     }
 };
 
+// The combine, at the end of a GEMM-2 task whose y rows (fp32, column block
+// cb) are stored: each row's arrival is counted at (token, cb); the task that
+// brings a token's count to its number of valid slots sums that token's y rows
+// in ascending slot order from +0.0 (tilelang.dataflow README section 3.5
+// step 5) and rounds once to bf16.  Those rows come into LDS with device-scope
+// direct-to-LDS loads (a lane per 16-byte piece, 32 pieces per row) in batches
+// of tokens; the arrival counter of each combined token goes back to 0.
+template <int NSUB, int RING>
+__device__ __forceinline__ void combine_rows(const FusedPlan* pl, const int* rows, int cb, int32_t* arrive, int nb2,
+                                             const float* y, void* out, const unsigned char* zero, int k, int d_h,
+                                             unsigned char* smem) {
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int* s_n = reinterpret_cast<int*>(smem);
+    int* s_list = s_n + 16;  // up to 16 * NSUB tokens
+    if (tid == 0) *s_n = 0;
+    lds_barrier();
+    if (tid < 16 * NSUB) {
+        const int p = rows[tid];
+        if (p >= 0) {
+            const int t = p / k;
+            int nv = 0;
+            for (int j = 0; j < k; ++j) {
+                const int q = t * k + j;
+                nv += !((pl->bad[q >> 6] >> (q & 63)) & 1ull);
+            }
+            const int old =
+                __hip_atomic_fetch_add(arrive + (int64_t)t * nb2 + cb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old + 1 == nv) s_list[atomicAdd(s_n, 1)] = t;
+        }
+    }
+    lds_barrier();
+    const int n = *s_n;
+    // pieces: (token u of the list, slot j, 16-byte piece c) -> LDS slot (u k + j) 32 + c
+    constexpr int kListBytes = 64 + 4 * 16 * NSUB;
+    unsigned char* buf = smem + (kListBytes + 15) / 16 * 16;
+    // tokens per batch; a wave's load fills 64 pieces, so a batch keeps 64
+    // pieces of room past its last one
+    const int per_batch = (RING - (int)(buf - smem) - 64 * 16) / (k * 512);
+    for (int u0 = 0; u0 < n; u0 += per_batch) {
+        const int nu = min(n - u0, per_batch);
+        const int pieces = nu * k * 32;
+        for (int s0 = 64 * w; s0 < pieces; s0 += 64 * kGemmWaves) {
+            const int sl = s0 + lane;
+            const void* src = zero;
+            if (sl < pieces) {
+                const int tj = sl >> 5, c = sl & 31;
+                const int t = s_list[u0 + tj / k], j = tj - tj / k * k;
+                const int q = t * k + j;
+                if (!((pl->bad[q >> 6] >> (q & 63)) & 1ull)) src = y + (int64_t)q * d_h + cb * 128 + 4 * c;
+            }
+            g2l16c(src, lds_offset(buf + 16 * s0));
+        }
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+        lds_barrier();
+        for (int i = tid; i < nu * 32; i += kGemmThreads) {
+            const int uu = i >> 5, c = i & 31;
+            const int t = s_list[u0 + uu];
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            for (int j = 0; j < k; ++j) {
+                const int q = t * k + j;
+                if ((pl->bad[q >> 6] >> (q & 63)) & 1ull) continue;
+                const float4 v = *reinterpret_cast<const float4*>(buf + 16 * ((uu * k + j) * 32 + c));
+                a0 += v.x;
+                a1 += v.y;
+                a2 += v.z;
+                a3 += v.w;
+            }
+            uint2 o;
+            o.x = f32_to_bf16(a0) | (f32_to_bf16(a1) << 16);
+            o.y = f32_to_bf16(a2) | (f32_to_bf16(a3) << 16);
+            *reinterpret_cast<uint2*>(static_cast<unsigned short*>(out) + (int64_t)t * d_h + cb * 128 + 4 * c) = o;
+        }
+        lds_barrier();  // the batch is read before the next one lands
+    }
+    for (int i = tid; i < n; i += kGemmThreads)
+        __hip_atomic_store(arrive + (int64_t)s_list[i] * nb2 + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();  // the list is read before the next task's loads land in the ring
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
     using L = LayerCfg<MODE>;
     constexpr int RING = L::kRing;
-    constexpr int MT = L::kMT;
+    constexpr int MT1 = L::kMT1, MT2 = L::kMT2;
     __shared__ __attribute__((aligned(16))) unsigned char smem[RING];
     __shared__ FusedQ q;
     __shared__ FusedPlan pl;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = a.N, E = a.E, k = a.k;
-    const int Np = (N + 255) / 256 * 256;
     int32_t* sync = a.sync;
     const unsigned char* zero = reinterpret_cast<const unsigned char*>(sync + kSyncZero);
 
-    FusedSched sch0{sync + kSyncQueue, &pl, &q, a.g1.topk_w, 0, 0, a.nb1, a.nb2, MT, E, Np};
+    FusedSched sch0{sync + kSyncQueue, sync + kSyncDone, &pl, &q, a.g1.topk_w, 0, 0, a.nb1, a.nb2, MT1, MT2, E};
     // the first claim goes out before the plan is built
     if (w == kSchedWave && lane == 0) sch0.claim();
 
-    // ---- plan: ids into LDS, histogram (in the ring, free until the first task)
-    int* hist = reinterpret_cast<int*>(smem);
-    for (int i = tid; i < E; i += kGemmThreads) hist[i] = 0;
-    lds_barrier();
-    for (int p0 = 64 * w; p0 < Np; p0 += 64 * kGemmWaves) {
-        const int p = p0 + lane;
-        const int id = p < N ? a.ids[p] : -1;
-        const bool ok = (unsigned)id < (unsigned)E;
-        pl.id8[p] = (unsigned char)(ok ? id : 0);
-        const uint64_t badm = __ballot(!ok);
-        if (lane == 0) pl.bad[p0 >> 6] = badm;
-        if (ok) atomicAdd(&hist[id], 1);
-    }
-    lds_barrier();
-    // counts, then each expert's rank (descending count, ties by id)
-    for (int e = tid; e < E; e += kGemmThreads) {
-        const int c = hist[e];
-        pl.cnt[e] = (short)c;
-        int r = 0;
-        for (int f = 0; f < E; ++f) {
-            const int cf = hist[f];
-            r += (cf > c) || (cf == c && f < e);
-        }
-        pl.order[r] = (unsigned char)e;
-    }
-    lds_barrier();
-    // padded offsets (expert order) and M-tile offsets (rank order): one wave each
-    if (w < 2) {
-        int run = 0;
-        for (int i0 = 0; i0 < E; i0 += 64) {
-            const int i = i0 + lane;
-            int v = 0;
-            if (i < E) {
-                const int tiles = (hist[w == 0 ? i : pl.order[i]] + kBlockM - 1) / kBlockM;
-                v = w == 0 ? kBlockM * tiles : (tiles + MT - 1) / MT;
-            }
-            int incl = v;
+    // ---- plan (tilelang.dataflow README section 3.5 step 1), in LDS.  Wave w
+    // owns the contiguous chunk [w C, w C + C) of the assignments (C a multiple
+    // of 64, 4 C = N rounded up to 256): ranks follow ascending p across waves,
+    // then across the wave's 64-wide steps, then across lanes.
+    constexpr int kSteps = kLayerMaxN / (64 * kGemmWaves);  // 64-wide steps of a chunk, at most
+    const int C = ((N + kGemmWaves - 1) / kGemmWaves + 63) / 64 * 64;
+    const int c_lo = w * C;
+    int* wcnt = reinterpret_cast<int*>(smem);  // [waves][E]: per-wave counts, then bases (ring free until the first task)
+    for (int i = tid; i < kGemmWaves * E; i += kGemmThreads) wcnt[i] = 0;
+    // every id load goes out before the first is used (one memory round trip)
+    int idv[kSteps];
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int o = __shfl_up(incl, d, 64);
-                if (lane >= d) incl += o;
-            }
-            if (i < E) (w == 0 ? pl.poff : pl.moff)[i] = (short)(run + incl - v);
-            run += __shfl(incl, 63, 64);
-        }
-        if (lane == 0) (w == 0 ? pl.poff : pl.moff)[E] = (short)run;
+    for (int u = 0; u < kSteps; ++u) {
+        const int p = c_lo + 64 * u + lane;
+        idv[u] = (64 * u < C && p < N) ? a.ids[p] : -1;
     }
     lds_barrier();
-    const int n_mt = pl.moff[E];
-    const int n1 = n_mt * a.nb1, total = n1 + n_mt * a.nb2;
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+        if (64 * u >= C) break;
+        const int p = c_lo + 64 * u + lane;
+        const bool ok = (unsigned)idv[u] < (unsigned)E;
+        const uint64_t badm = __ballot(!ok);
+        if (lane == 0) pl.bad[p >> 6] = badm;
+        if (ok) atomicAdd(&wcnt[w * E + idv[u]], 1);
+    }
+    lds_barrier();
+    // counts; the per-wave counts become each wave's rank base within the expert
+    for (int e = tid; e < E; e += kGemmThreads) {
+        int run = 0;
+#pragma unroll
+        for (int ww = 0; ww < kGemmWaves; ++ww) {
+            const int c = wcnt[ww * E + e];
+            wcnt[ww * E + e] = run;
+            run += c;
+        }
+        pl.cnt[e] = (short)run;
+    }
+    lds_barrier();
+    // padded offsets (wave 0); every wave ranks a share of the experts: lane l
+    // holds the counts of experts l, l + 64, ...; the experts before e (more
+    // rows, or as many and a lower id) are a popcount of ballots
+    auto tiles_of = [&](int e) { return (pl.cnt[e] + kBlockM - 1) / kBlockM; };
+    if (w == 0) wave_exclusive_scan256([&](int e) { return kBlockM * tiles_of(e); }, pl.poff, E, lane);
+    {
+        constexpr int kJ = kMaxExperts / 64;
+        int cj[kJ];
+#pragma unroll
+        for (int j = 0; j < kJ; ++j) cj[j] = lane + 64 * j < E ? pl.cnt[lane + 64 * j] : -1;
+        for (int e = w; e < E; e += kGemmWaves) {
+            int c = 0;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j)
+                if (j == (e >> 6)) c = __builtin_amdgcn_readlane(cj[j], e & 63);
+            int r = 0;
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) {
+                const int e2 = lane + 64 * j;
+                r += __popcll(__ballot(e2 < E && (cj[j] > c || (cj[j] == c && e2 < e))));
+            }
+            if (lane == 0) pl.order[r] = (unsigned char)e;
+        }
+    }
+    lds_barrier();
+    // the M-tile offsets of both GEMMs in rank order (waves 1, 2), the padding
+    // rows of each expert's group, and the stable scatter: each wave walks its
+    // chunk; lanes with the same expert find each other with one ballot per
+    // bit of the key (the id, or E for an invalid one: 9 bits), and the lowest
+    // lane of each group advances the wave's base
+    if (w == 1)
+        wave_exclusive_scan256([&](int r) { return (tiles_of(pl.order[r]) + MT1 - 1) / MT1; }, pl.moff[0], E, lane);
+    if (w == 2)
+        wave_exclusive_scan256([&](int r) { return (tiles_of(pl.order[r]) + MT2 - 1) / MT2; }, pl.moff[1], E, lane);
+    for (int e = tid; e < E; e += kGemmThreads)
+        for (int r = pl.poff[e] + pl.cnt[e]; r < pl.poff[e + 1]; ++r) pl.row_src[r] = -1;
+    {
+        const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+        for (int u = 0; u < kSteps; ++u) {
+            if (64 * u >= C) break;
+            const int p = c_lo + 64 * u + lane;
+            const int id = idv[u];
+            const bool valid = (unsigned)id < (unsigned)E;
+            const int key = valid ? id : 256;
+            uint64_t m = ~0ull;
+#pragma unroll
+            for (int b = 0; b < 9; ++b) {
+                const bool bit = (key >> b) & 1;
+                const uint64_t bal = __ballot(bit);
+                m &= bit ? bal : ~bal;
+            }
+            const int wrank = __popcll(m & lt);
+            if (valid) pl.row_src[pl.poff[id] + wcnt[w * E + id] + wrank] = p;
+            // every lane has read its base above (a wave's LDS accesses stay in order)
+            if (valid && wrank == 0) wcnt[w * E + id] += __popcll(m);
+        }
+    }
+    lds_barrier();
+    const int n1 = pl.moff[0][E] * a.nb1, total = n1 + pl.moff[1][E] * a.nb2;
 
     // tokens without a valid slot: zero output rows (token t by workgroup t mod grid)
     for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
@@ -247,16 +362,15 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
 
     // ---- the first task
     if (w == kSchedWave) {
-        sch0.total = total;
         sch0.n1 = n1;
+        sch0.total = total;
         sch0.settle(true);
         sch0.load_rows(0);
         sch0.publish();
     }
     lds_barrier();
 
-    FusedCtx fx{sync + kSyncDone, sync + kSyncArrive, sync + kSyncTimeouts, pl.bad, a.out, a.nb1, a.nb2, k,
-                a.g1.d_h};
+    FusedCtx fx{nullptr, 0, sync + kSyncTimeouts};
     for (int par = 0;; par ^= 1) {
         // uniform task fields (readfirstlane: see gemm1_kernel)
         const int t = __builtin_amdgcn_readfirstlane(q.slot);
@@ -264,9 +378,15 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
         const int list = __builtin_amdgcn_readfirstlane(q.list);
         const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
         const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
-        FusedSched sch{sync + kSyncQueue, &pl, &q, a.g1.topk_w, total, n1, a.nb1, a.nb2, MT, E, Np};
-        const int* rows = q.rows[par];
+        const bool ready = __builtin_amdgcn_readfirstlane(q.ready) != 0;
+        FusedSched sch{sync + kSyncQueue, sync + kSyncDone, &pl, &q, a.g1.topk_w, n1, total, a.nb1, a.nb2, MT1, MT2, E};
+        const int* rows = pl.row_src + row0;
         const float* roww = q.roww[par];
+        // the completion counter of a task's GEMM-2 M-tile, at its first group
+        // block: GEMM-1 adds to it, GEMM-2 waits for done_target
+        const int g2_tile = (pl.poff[e] + (row0 - pl.poff[e]) / (kBlockM * MT2) * (kBlockM * MT2)) / kBlockM;
+        fx.done = sync + kSyncDone + g2_tile;
+        fx.target = sch.done_target(nsub);
 #define MOE_L1(NS)                                                                                                 \
     gemm_task<MODE, true, NS, RING, true, FusedSched>(a.g1.x, a.g1.x_scale, nullptr, k, a.g1.w1, a.g1.w1_scale,     \
                                                       zero, e, row0, cb, a.g1.d_h, a.g1.d_e, a.g1.packed != 0,     \
@@ -274,10 +394,12 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
 #define MOE_L2(NS)                                                                                                 \
     gemm_task<MODE, false, NS, RING, true, FusedSched>(a.g2.h, a.g2.h_scale, nullptr, 1, a.g2.w2, a.g2.w2_scale,   \
                                                        zero, e, row0, cb, a.g2.d_e, a.g2.d_h, a.g2.packed != 0,    \
-                                                       smem, nullptr, &a.g2, sch, rows, roww, par, &fx)
-        // one body per row-block count (M-tiles of MT blocks: nsub in [1, MT])
+                                                       smem, nullptr, &a.g2, sch, rows, roww, par, &fx, ready);   \
+    combine_rows<NS, RING>(&pl, rows, cb, sync + kSyncArrive, a.nb2, static_cast<const float*>(a.g2.y), a.out, zero, k, \
+                           a.g1.d_h, smem)
+        // one body per row-block count (nsub in [1, MT1] or [1, MT2])
         if (list == 0) {
-            if constexpr (MT == 8) {
+            if constexpr (MT1 == 8) {
                 switch (nsub) {
                     case 1: MOE_L1(1); break;
                     case 2: MOE_L1(2); break;
@@ -297,24 +419,16 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
                 }
             }
         } else {
-            if constexpr (MT == 8) {
-                switch (nsub) {
-                    case 1: MOE_L2(1); break;
-                    case 2: MOE_L2(2); break;
-                    case 3: MOE_L2(3); break;
-                    case 4: MOE_L2(4); break;
-                    case 5: MOE_L2(5); break;
-                    case 6: MOE_L2(6); break;
-                    case 7: MOE_L2(7); break;
-                    default: MOE_L2(8); break;
-                }
-            } else {
-                switch (nsub) {
-                    case 1: MOE_L2(1); break;
-                    case 2: MOE_L2(2); break;
-                    case 3: MOE_L2(3); break;
-                    default: MOE_L2(4); break;
-                }
+            static_assert(MT2 == 8, "GEMM-2 bodies for 1..8 row blocks");
+            switch (nsub) {
+                case 1: MOE_L2(1); break;
+                case 2: MOE_L2(2); break;
+                case 3: MOE_L2(3); break;
+                case 4: MOE_L2(4); break;
+                case 5: MOE_L2(5); break;
+                case 6: MOE_L2(6); break;
+                case 7: MOE_L2(7); break;
+                default: MOE_L2(8); break;
             }
         }
 #undef MOE_L1
@@ -333,7 +447,7 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
     }
     lds_barrier();
     if (*s_last) {
-        const int n_blocks = pl.poff[E] / kBlockM;
+        const int n_blocks = pl.poff[E] / kBlockM;  // every counter this call may have raised
         for (int i = tid; i < n_blocks; i += kGemmThreads)
             __hip_atomic_store(sync + kSyncDone + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (tid == 0) {

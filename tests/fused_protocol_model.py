@@ -8,17 +8,17 @@ that its properties can be checked on the CPU under random skews before and
 besides any GPU run:
 
 * Plan.  Every workgroup derives the same plan from the routing ids: per-expert
-  counts, 16-row group blocks, padded offsets in expert order, M-tiles of MT
-  group blocks, experts ranked by descending count (ties by id), and one task
-  list: every GEMM-1 task (rank, column block, M-tile), then every GEMM-2 task in
-  the same order.
+  counts, 16-row group blocks, padded offsets in expert order, M-tiles of MT1
+  group blocks for GEMM-1 and of MT2 (a multiple of MT1) for GEMM-2, experts
+  ranked by descending count (ties by id), and one task list: every GEMM-1
+  task, then every GEMM-2 task, each by (rank, column block, M-tile).
 * Queue.  One counter; a workgroup claims the next index with a fetch-add, the
   claim for its next task going out while its current task still runs.  An
   index past the list means no task is left.
 * Flags.  A GEMM-1 task stores its rows of h, waits for the stores, then adds 1
-  to the counter of its M-tile.  A GEMM-2 task may load its weights first, then
-  waits (bounded) until its M-tile's counter reaches the number of GEMM-1 column
-  blocks, then reads h.
+  to the counter of the GEMM-2 M-tile its rows belong to.  A GEMM-2 task may
+  load its weights first, then waits (bounded) until that counter reaches the
+  number of GEMM-1 column blocks times the GEMM-1 M-tiles it holds, then reads h.
 * Combine.  A GEMM-2 task stores its y rows, waits for them, then adds 1 per
   row to the arrival counter of (token, column block); the workgroup that
   brings it to the token's number of valid slots sums that token's y rows in
@@ -49,12 +49,12 @@ class Plan:
     counts: np.ndarray
     tiles: np.ndarray
     poff: np.ndarray
-    mt: np.ndarray
+    mt: list        # per list: M-tiles of each expert
     order: np.ndarray
     toff: list
     n1: int
     n2: int
-    mt_blocks: int
+    mtb: tuple      # group blocks per M-tile: (GEMM-1, GEMM-2)
     nb1: int
     nb2: int
 
@@ -70,35 +70,47 @@ class Plan:
         off = self.toff[lst]
         r = int(np.searchsorted(off, j, side="right")) - 1  # the last rank starting at or before j: never empty
         e = int(self.order[r])
-        mt = int(self.mt[e])
-        local = j - int(off[r])
-        cb, m = divmod(local, mt)
+        mt = int(self.mt[lst][e])
+        cb, m = divmod(j - int(off[r]), mt)
         assert 0 <= cb < nb
-        row0 = int(self.poff[e]) + BLOCK_M * self.mt_blocks * m
-        nsub = min(self.mt_blocks, int(self.tiles[e]) - self.mt_blocks * m)
+        mtb = self.mtb[lst]
+        row0 = int(self.poff[e]) + BLOCK_M * mtb * m
+        nsub = min(mtb, int(self.tiles[e]) - mtb * m)
         return lst, e, row0, nsub, cb, m
 
+    def g2_tile(self, e, row0):
+        """First group block of the GEMM-2 M-tile holding padded row row0 of expert e: its counter."""
+        span = BLOCK_M * self.mtb[1]
+        return (int(self.poff[e]) + (row0 - int(self.poff[e])) // span * span) // BLOCK_M
 
-def make_plan(ids, E, mt_blocks, nb1, nb2):
+    def target(self, nsub2):
+        """GEMM-1 column blocks that store the h rows of a GEMM-2 M-tile of nsub2 group blocks."""
+        return self.nb1 * -(-nsub2 // self.mtb[0])
+
+
+def make_plan(ids, E, mtb, nb1, nb2):
+    """mtb: group blocks per M-tile, an int (both GEMMs) or (GEMM-1, GEMM-2) with GEMM-2's a multiple."""
+    mtb = (mtb, mtb) if isinstance(mtb, int) else tuple(mtb)
+    assert mtb[1] % mtb[0] == 0
     ids = np.asarray(ids).ravel()
     valid = (ids >= 0) & (ids < E)
     counts = np.bincount(ids[valid], minlength=E).astype(np.int64)
     tiles = (counts + BLOCK_M - 1) // BLOCK_M
     poff = np.concatenate([[0], np.cumsum(BLOCK_M * tiles)])
-    mt = (tiles + mt_blocks - 1) // mt_blocks
+    mt = [(tiles + b - 1) // b for b in mtb]
     order = np.array(sorted(range(E), key=lambda e: (-counts[e], e)), dtype=np.int64)
     toff = []
-    for nb in (nb1, nb2):
-        per = mt[order] * nb
+    for lst, nb in enumerate((nb1, nb2)):
+        per = mt[lst][order] * nb
         toff.append(np.concatenate([[0], np.cumsum(per)]))
-    return Plan(counts, tiles, poff, mt, order, toff, int(toff[0][-1]), int(toff[1][-1]), mt_blocks, nb1, nb2)
+    return Plan(counts, tiles, poff, mt, order, toff, int(toff[0][-1]), int(toff[1][-1]), mtb, nb1, nb2)
 
 
-def rows_of(ids, E, plan, e, m, nsub):
+def rows_of(ids, E, plan, e, m, nsub, nsub_list=0):
     """Assignments of the M-tile's rows (ascending p within the expert), -1 on padding rows."""
     ids = np.asarray(ids).ravel()
     ps = np.nonzero(ids == e)[0]
-    lo = BLOCK_M * plan.mt_blocks * m
+    lo = BLOCK_M * plan.mtb[1 if nsub_list else 0] * m
     out = np.full(BLOCK_M * nsub, -1, dtype=np.int64)
     take = ps[lo:lo + BLOCK_M * nsub]
     out[:len(take)] = take
@@ -128,11 +140,11 @@ class Sim:
     """Discrete-event run of one call.  Times are arbitrary units; every atomic
     happens at one instant, in event order."""
 
-    def __init__(self, ids, T, k, E, nb1, nb2, mt_blocks, grid, resident, rng, faults=None, state=None,
+    def __init__(self, ids, T, k, E, nb1, nb2, mtb, grid, resident, rng, faults=None, state=None,
                  spin_limit=200000, poll=1.0):
         self.ids = np.asarray(ids).reshape(T, k)
         self.T, self.k, self.E = T, k, E
-        self.plan = make_plan(self.ids, E, mt_blocks, nb1, nb2)
+        self.plan = make_plan(self.ids, E, mtb, nb1, nb2)
         self.grid, self.resident = grid, resident
         self.rng = rng
         self.f = faults or Faults()
@@ -158,7 +170,7 @@ class Sim:
     def task(self, i):
         p = self.plan
         if self.f.g2_first:
-            # planted: the GEMM-2 half first
+            # planted: the GEMM-2 part of the list first
             i = i + p.n1 if i < p.n2 else i - p.n2
         return p.decode(i)
 
@@ -193,6 +205,7 @@ class Sim:
             self.errors.append(f"task {slot} executed twice")
         self.executed[slot] = b
         rb = row0 // BLOCK_M
+        g2 = self.plan.g2_tile(e, row0)  # counter of the GEMM-2 M-tile
         length = self.dur(10.0)
         nxt = {}
 
@@ -205,19 +218,19 @@ class Sim:
             self.push(self.now + length * claim_frac, do_claim)
             def g1_end():
                 if self.f.flag_before_store:
-                    self.st.done1[rb] = self.st.done1.get(rb, 0) + 1
-                    self.push(self.now + self.dur(0.5), lambda: self.h_store(rb, cb))
+                    self.st.done1[g2] = self.st.done1.get(g2, 0) + 1
+                    self.push(self.now + self.dur(0.5), lambda: self.h_store(rb, nsub, cb))
                 else:
-                    self.h_store(rb, cb)
-                    self.st.done1[rb] = self.st.done1.get(rb, 0) + 1
+                    self.h_store(rb, nsub, cb)
+                    self.st.done1[g2] = self.st.done1.get(g2, 0) + 1
                 self.push(self.now + self.dur(0.2), lambda: self.run_task(b, nxt["slot"]))
             self.push(self.now + length, g1_end)
         else:
-            target = self.plan.nb1 - (1 if self.f.short_wait else 0)
+            target = self.plan.target(nsub) - (1 if self.f.short_wait else 0)
             polls = {"n": 0}
 
             def wait():
-                if self.st.done1.get(rb, 0) >= target:
+                if self.st.done1.get(g2, 0) >= target:
                     return self.g2_body(b, slot, e, row0, nsub, cb, m, rb, length, nxt, claim_frac, do_claim)
                 polls["n"] += 1
                 if polls["n"] > self.spin_limit:
@@ -228,20 +241,24 @@ class Sim:
             # the weight stages are requested before the wait
             self.push(self.now + self.dur(0.5), wait)
 
-    def h_store(self, rb, cb):
-        self.h_ready[(rb, cb)] = self.now
+    def h_store(self, rb, nsub, cb):
+        for i in range(nsub):  # every group block of the GEMM-1 M-tile
+            self.h_ready[(rb + i, cb)] = self.now
 
     def g2_body(self, b, slot, e, row0, nsub, cb, m, rb, length, nxt, claim_frac, do_claim):
         self.push(self.now + length * claim_frac, do_claim)
-        for c1 in range(self.plan.nb1):
-            if (rb, c1) not in self.h_ready:
-                self.errors.append(f"task {slot} read h of row block {rb}, column block {c1} before it was stored")
-        rows = rows_of(self.ids, self.E, self.plan, e, m, nsub)
+        for i in range(nsub):
+            for c1 in range(self.plan.nb1):
+                if (rb + i, c1) not in self.h_ready:
+                    self.errors.append(f"task {slot} read h of row block {rb + i}, column block {c1} before it was stored")
+        rows = rows_of(self.ids, self.E, self.plan, e, m, nsub, nsub_list=1)
 
         def g2_end():
             for p in rows:
                 if p >= 0:
                     self.y_ready[(int(p), cb)] = self.now
+            # the y stores are complete: one arrival per row at (token, column
+            # block); the arrival that completes a token combines it
             last = []
             for p in rows:
                 if p < 0:

@@ -27,13 +27,14 @@ def zipf_ids(rng, T, k, E, s, empty=0, drop=0.0):
 
 
 CASES = [
-    # T, k, E, nb1, nb2, mt_blocks, grid, resident, zipf s, empty experts, dropped fraction
-    (128, 2, 32, 12, 16, 8, 64, 64, 1.1, 0, 0.0),
-    (256, 2, 32, 6, 16, 4, 40, 40, 1.2, 4, 0.0),
-    (300, 4, 16, 3, 5, 4, 24, 7, 1.0, 2, 0.05),
-    (64, 2, 8, 2, 2, 8, 16, 1, 0.8, 0, 0.2),
-    (97, 3, 20, 4, 3, 4, 32, 5, 1.5, 3, 0.1),
-    (40, 1, 4, 2, 3, 8, 12, 12, 2.0, 1, 0.5),
+    # T, k, E, nb1, nb2, (GEMM-1, GEMM-2 M-tile blocks), grid, resident, zipf s, empty experts, dropped fraction
+    (128, 2, 32, 12, 16, (8, 8), 64, 64, 1.1, 0, 0.0),
+    (256, 2, 32, 6, 16, (4, 8), 40, 40, 1.2, 4, 0.0),
+    (300, 4, 16, 3, 5, (4, 8), 24, 7, 1.0, 2, 0.05),
+    (64, 2, 8, 2, 2, (8, 8), 16, 1, 0.8, 0, 0.2),
+    (97, 3, 20, 4, 3, (4, 4), 32, 5, 1.5, 3, 0.1),
+    (40, 1, 4, 2, 3, (2, 8), 12, 12, 2.0, 1, 0.5),
+    (400, 2, 6, 3, 4, (4, 8), 48, 48, 1.0, 0, 0.0),
 ]
 
 
@@ -55,7 +56,7 @@ def test_plan_covers_every_routed_row_once():
     rng = np.random.default_rng(5)
     T, k, E = 200, 3, 24
     ids = zipf_ids(rng, T, k, E, 1.3, 3, 0.05)
-    for mtb in (4, 8):
+    for mtb in ((4, 8), (8, 8)):
         plan = make_plan(ids, E, mtb, 5, 7)
         seen = {}
         for i in range(plan.n1):
@@ -70,12 +71,22 @@ def test_plan_covers_every_routed_row_once():
         valid = [p for p in range(T * k) if 0 <= ids.ravel()[p] < E]
         assert set(seen) == {(p, cb) for p in valid for cb in range(5)}
         assert all(v == 1 for v in seen.values())
-        # GEMM-2 tasks mirror GEMM-1's M-tiles, and the experts are in descending count order
-        counts = [plan.counts[plan.decode(i)[1]] for i in range(plan.n1)]
-        assert counts == sorted(counts, reverse=True)
-        g1 = {(plan.decode(i)[1], plan.decode(i)[5]) for i in range(plan.n1)}
-        g2 = {(plan.decode(plan.n1 + i)[1], plan.decode(plan.n1 + i)[5]) for i in range(plan.n2)}
-        assert g1 == g2
+        # both lists go by descending expert row count (ties by id)
+        for lo, n in ((0, plan.n1), (plan.n1, plan.n2)):
+            keys = [(-plan.counts[plan.decode(lo + i)[1]], plan.decode(lo + i)[1]) for i in range(n)]
+            assert keys == sorted(keys)
+        # every GEMM-1 M-tile sits in exactly one GEMM-2 M-tile, whose counter
+        # target counts all of the GEMM-1 tasks that feed it
+        feed = {}
+        for i in range(plan.n1):
+            _, e, row0, nsub, cb, _ = plan.decode(i)
+            feed[plan.g2_tile(e, row0)] = feed.get(plan.g2_tile(e, row0), 0) + 1
+        g2 = {}
+        for i in range(plan.n2):
+            _, e, row0, nsub, cb, _ = plan.decode(plan.n1 + i)
+            assert plan.g2_tile(e, row0) == row0 // 16
+            g2[row0 // 16] = plan.target(nsub)
+        assert feed == g2
 
 
 @pytest.mark.parametrize("fault", ["g2_first", "short_wait", "flag_before_store", "no_reset", "arrive_off_by_one"])
@@ -89,7 +100,7 @@ def test_planted_protocol_mistakes_are_caught(fault):
     for resident in (3, 16):
         st = State()
         for call in range(4):
-            sim = Sim(ids, T, k, E, 3, 4, 4, 16, resident, rng, faults=Faults(**{fault: True}), state=st,
+            sim = Sim(ids, T, k, E, 3, 4, (4, 8), 16, resident, rng, faults=Faults(**{fault: True}), state=st,
                       spin_limit=2000).run()
             if sim.check():
                 caught = True

@@ -20,22 +20,28 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
 
 
-@pytest.mark.parametrize("mode", [W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8])
-def test_graph_replays_match_eager(mode):
+CASES = [(m, moe.MOE_LAUNCH_MULTI) for m in (W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8, W.MODE_INT8)] + \
+        [(m, moe.MOE_LAUNCH_SINGLE) for m in (W.MODE_BF16, W.MODE_FP8, W.MODE_MXFP8)]
+
+
+@pytest.mark.parametrize("mode,launch", CASES)
+def test_graph_replays_match_eager(mode, launch):
+    """Both launch forms; the single launch's workspace starts zeroed (its
+    synchronisation block), and every replay must leave that block zero again."""
     shape = (200, 8, 2, 256, 256)
     d = device.upload(W.custom(*shape, mode, seed=31))
-    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], x_scale=d["x_scale"])
-    ws_graph = torch.empty(moe.moe_workspace_bytes(dims), dtype=torch.uint8, device="cuda:0")
+    dims = moe.make_dims(d["x"], d["topk_ids"], d["w1"], x_scale=d["x_scale"], launch=launch)
+    ws_graph = torch.zeros(moe.moe_workspace_bytes(dims), dtype=torch.uint8, device="cuda:0")
     out_graph = torch.empty((shape[0], shape[3]), dtype=torch.bfloat16, device="cuda:0")
-    device.run(d, out=out_graph, workspace=ws_graph)  # eager warm-up on the graph's buffers
+    device.run(d, out=out_graph, workspace=ws_graph, launch=launch)  # eager warm-up on the graph's buffers
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        device.run(d, out=out_graph, workspace=ws_graph)
+        device.run(d, out=out_graph, workspace=ws_graph, launch=launch)
     torch.cuda.synchronize()
 
-    ws_eager = torch.empty_like(ws_graph)
+    ws_eager = torch.zeros_like(ws_graph)
     for i, seed in enumerate((32, 33, 34, 33)):
         # new routing, weights and activations (the last replay repeats an earlier input)
         new = device.upload(W.custom(*shape, mode, seed=seed))
@@ -45,8 +51,10 @@ def test_graph_replays_match_eager(mode):
         out_graph.fill_(float("nan"))
         g.replay()
         torch.cuda.synchronize()
-        eager = device.run(d, workspace=ws_eager)
+        eager = device.run(d, workspace=ws_eager, launch=launch)
         torch.cuda.synchronize()
-        print(f"graph replay {i} (seed {seed}) mode={mode}", flush=True)
+        print(f"graph replay {i} (seed {seed}) mode={mode} launch={launch}", flush=True)
         assert torch.isfinite(out_graph.float()).all()
         assert torch.equal(_bits(out_graph), _bits(eager)), f"replay {i} differs from the eager call"
+        if launch == moe.MOE_LAUNCH_SINGLE:
+            assert not ws_graph[:moe.MOE_SYNC_BYTES].any(), "synchronisation block not zero after a replay"
