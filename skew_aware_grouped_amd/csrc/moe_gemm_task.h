@@ -442,12 +442,15 @@ struct Cfg {
 // 1 to the counter of the GEMM-2 M-tile its rows belong to.  GEMM-2 first
 // requests its weight stages, waits (bounded) until that counter reaches every
 // column block of every GEMM-1 M-tile in it, then loads h with device-scope
-// loads; it keeps y in fp32 and returns once its y stores are complete (the
-// layer kernel then combines).
+// loads; it keeps y in fp32 and, once its y stores are complete, adds 1 per
+// row to the arrival counter of the row's (token, column block), which the
+// layer kernel's combine waits on.
 struct FusedCtx {
     int32_t* done;      // this task's GEMM-2 M-tile counter: GEMM-1 column blocks that stored their h rows
     int32_t target;     // GEMM-2: the count that means all of its h rows are stored
     int32_t* timeouts;  // waits that ran out (diagnostic; each such task went on)
+    int32_t* arrive;    // [token * nb2 + column block]: y rows stored
+    int32_t k, nb2;
 };
 // polls of a bounded wait (each a device-scope load and a short sleep):
 // far longer than any GEMM-1 task, so only a broken schedule reaches it
@@ -1057,6 +1060,11 @@ __device__ __forceinline__ void gemm_task(const void* a_base, const void* a_scal
     if constexpr (FUSED) {
         if constexpr (GATED) {
             if (threadIdx.x == 0) __hip_atomic_fetch_add(fx->done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (threadIdx.x < 16 * NSUB) {
+            const int p = rows[threadIdx.x];
+            if (p >= 0)
+                __hip_atomic_fetch_add(fx->arrive + (int64_t)(p / fx->k) * fx->nb2 + cb, 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }

@@ -20,11 +20,13 @@
 // GEMM-1 tasks never wait; a GEMM-2 task waits only on the GEMM-1 tasks of its
 // M-tile, all of lower index.  So the lowest unfinished claimed task can
 // always proceed, whether or not every workgroup of the grid is resident, and
-// each wait is bounded anyway.  The combine needs no waiting at all: after its
-// y stores, a GEMM-2 task counts each row's arrival at (token, column block),
-// and the task whose arrival completes a token sums that token's slots.  The
-// protocol is modelled on the CPU and checked there for coverage, dependency
-// order and termination.
+// each wait is bounded anyway.  After its y stores, a GEMM-2 task counts each
+// row's arrival at (token, column block).  The combine comes last: once its
+// queue is empty, workgroup b sums the (token, column block) outputs b, b +
+// grid, ..., waiting (bounded) until each has all its arrivals; those come
+// from GEMM-2 tasks, every one of them already claimed.  The protocol is
+// modelled on the CPU and checked there for coverage, dependency order and
+// termination.
 #include "moe_gemm_task.h"
 #include "moe_wave.h"
 
@@ -151,68 +153,74 @@ struct FusedSched {
     }
 };
 
-// The combine, at the end of a GEMM-2 task whose y rows (fp32, column block
-// cb) are stored: each row's arrival is counted at (token, cb); the task that
-// brings a token's count to its number of valid slots sums that token's y rows
-// in ascending slot order from +0.0 (tilelang.dataflow README section 3.5
-// step 5) and rounds once to bf16.  Those rows come into LDS with device-scope
-// direct-to-LDS loads (a lane per 16-byte piece, 32 pieces per row) in batches
-// of tokens; the arrival counter of each combined token goes back to 0.
-template <int NSUB, int RING>
-__device__ __forceinline__ void combine_rows(const FusedPlan* pl, const int* rows, int cb, int32_t* arrive, int nb2,
-                                             const float* y, void* out, const unsigned char* zero, int k, int d_h,
-                                             unsigned char* smem) {
+// The combine (tilelang.dataflow README section 3.5 step 5), once this
+// workgroup's queue is empty: outputs i = blockIdx + grid * j of the T * nb2
+// (token t, 128-column block cb) pieces, i = t nb2 + cb.  A batch of them
+// waits (bounded, on the scheduler wave) until each has an arrival from every
+// valid slot of its token, then their fp32 y rows come into LDS with
+// device-scope direct-to-LDS loads (a lane per 16-byte piece, 32 pieces per
+// row), and each (token, 4 columns) is summed in ascending slot order from +0.0
+// and rounded once to bf16; a token without a valid slot gets zeros.  Each
+// arrival counter goes back to 0.
+template <int RING>
+__device__ __forceinline__ void combine_share(const FusedPlan* pl, int32_t* arrive, int32_t* timeouts, int T, int nb2,
+                                              int k, int d_h, const float* y, void* out, const unsigned char* zero,
+                                              unsigned char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int* s_n = reinterpret_cast<int*>(smem);
-    int* s_list = s_n + 16;  // up to 16 * NSUB tokens
-    if (tid == 0) *s_n = 0;
-    lds_barrier();
-    if (tid < 16 * NSUB) {
-        const int p = rows[tid];
-        if (p >= 0) {
-            const int t = p / k;
-            int nv = 0;
-            for (int j = 0; j < k; ++j) {
-                const int q = t * k + j;
-                nv += !((pl->bad[q >> 6] >> (q & 63)) & 1ull);
+    const int items = T * nb2, G = gridDim.x;
+    const int mine = items > (int)blockIdx.x ? (items - 1 - (int)blockIdx.x) / G + 1 : 0;
+    // pieces a batch takes in LDS: item u, slot j, 16-byte piece c -> (u k + j) 32 + c;
+    // a wave's load fills 64 pieces, so a batch keeps 64 pieces of room past its last one
+    const int per_batch = min((RING - 64 * 16) / (k * 512), 64);
+    auto valid = [&](int q) { return !((pl->bad[q >> 6] >> (q & 63)) & 1ull); };
+    auto nvalid = [&](int t) {
+        int nv = 0;
+        for (int j = 0; j < k; ++j) nv += valid(t * k + j);
+        return nv;
+    };
+    for (int u0 = 0; u0 < mine; u0 += per_batch) {
+        const int nu = min(mine - u0, per_batch);
+        if (w == kSchedWave) {
+            // lane u: item u0 + u of the batch
+            const int i = blockIdx.x + G * (u0 + lane);
+            const int need = lane < nu ? nvalid(i / nb2) : 0;
+            for (int it = 0;; ++it) {
+                const int got = lane < nu ? __hip_atomic_load(arrive + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                          : 0;
+                if (__ballot(got < need) == 0) break;
+                if (it >= kSpinLimit) {
+                    if (lane == 0)
+                        __hip_atomic_fetch_add(timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
             }
-            const int old =
-                __hip_atomic_fetch_add(arrive + (int64_t)t * nb2 + cb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (old + 1 == nv) s_list[atomicAdd(s_n, 1)] = t;
         }
-    }
-    lds_barrier();
-    const int n = *s_n;
-    // pieces: (token u of the list, slot j, 16-byte piece c) -> LDS slot (u k + j) 32 + c
-    constexpr int kListBytes = 64 + 4 * 16 * NSUB;
-    unsigned char* buf = smem + (kListBytes + 15) / 16 * 16;
-    // tokens per batch; a wave's load fills 64 pieces, so a batch keeps 64
-    // pieces of room past its last one
-    const int per_batch = (RING - (int)(buf - smem) - 64 * 16) / (k * 512);
-    for (int u0 = 0; u0 < n; u0 += per_batch) {
-        const int nu = min(n - u0, per_batch);
+        lds_barrier();
         const int pieces = nu * k * 32;
         for (int s0 = 64 * w; s0 < pieces; s0 += 64 * kGemmWaves) {
             const int sl = s0 + lane;
             const void* src = zero;
             if (sl < pieces) {
-                const int tj = sl >> 5, c = sl & 31;
-                const int t = s_list[u0 + tj / k], j = tj - tj / k * k;
+                const int uj = sl >> 5, c = sl & 31;
+                const int u = uj / k, j = uj - u * k;
+                const int i = blockIdx.x + G * (u0 + u);
+                const int t = i / nb2, cb = i - t * nb2;
                 const int q = t * k + j;
-                if (!((pl->bad[q >> 6] >> (q & 63)) & 1ull)) src = y + (int64_t)q * d_h + cb * 128 + 4 * c;
+                if (valid(q)) src = y + (int64_t)q * d_h + cb * 128 + 4 * c;
             }
-            g2l16c(src, lds_offset(buf + 16 * s0));
+            g2l16c(src, lds_offset(smem + 16 * s0));
         }
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
         lds_barrier();
-        for (int i = tid; i < nu * 32; i += kGemmThreads) {
-            const int uu = i >> 5, c = i & 31;
-            const int t = s_list[u0 + uu];
+        for (int x = tid; x < nu * 32; x += kGemmThreads) {
+            const int u = x >> 5, c = x & 31;
+            const int i = blockIdx.x + G * (u0 + u);
+            const int t = i / nb2, cb = i - t * nb2;
             float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
             for (int j = 0; j < k; ++j) {
-                const int q = t * k + j;
-                if ((pl->bad[q >> 6] >> (q & 63)) & 1ull) continue;
-                const float4 v = *reinterpret_cast<const float4*>(buf + 16 * ((uu * k + j) * 32 + c));
+                if (!valid(t * k + j)) continue;
+                const float4 v = *reinterpret_cast<const float4*>(smem + 16 * ((u * k + j) * 32 + c));
                 a0 += v.x;
                 a1 += v.y;
                 a2 += v.z;
@@ -223,11 +231,10 @@ __device__ __forceinline__ void combine_rows(const FusedPlan* pl, const int* row
             o.y = f32_to_bf16(a2) | (f32_to_bf16(a3) << 16);
             *reinterpret_cast<uint2*>(static_cast<unsigned short*>(out) + (int64_t)t * d_h + cb * 128 + 4 * c) = o;
         }
+        for (int u = tid; u < nu; u += kGemmThreads)
+            __hip_atomic_store(arrive + blockIdx.x + G * (u0 + u), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         lds_barrier();  // the batch is read before the next one lands
     }
-    for (int i = tid; i < n; i += kGemmThreads)
-        __hip_atomic_store(arrive + (int64_t)s_list[i] * nb2 + cb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();  // the list is read before the next task's loads land in the ring
 }
 
 template <int MODE>
@@ -347,19 +354,6 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
     lds_barrier();
     const int n1 = pl.moff[0][E] * a.nb1, total = n1 + pl.moff[1][E] * a.nb2;
 
-    // tokens without a valid slot: zero output rows (token t by workgroup t mod grid)
-    for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
-        bool none = true;
-        for (int j = 0; j < k; ++j) {
-            const int p = t * k + j;
-            none = none && ((pl.bad[p >> 6] >> (p & 63)) & 1ull);
-        }
-        if (none) {
-            uint4* dst = reinterpret_cast<uint4*>(static_cast<unsigned short*>(a.out) + (int64_t)t * a.g1.d_h);
-            for (int c = tid; c < a.g1.d_h / 8; c += kGemmThreads) dst[c] = make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
-
     // ---- the first task
     if (w == kSchedWave) {
         sch0.n1 = n1;
@@ -370,7 +364,7 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
     }
     lds_barrier();
 
-    FusedCtx fx{nullptr, 0, sync + kSyncTimeouts};
+    FusedCtx fx{nullptr, 0, sync + kSyncTimeouts, sync + kSyncArrive, k, a.nb2};
     for (int par = 0;; par ^= 1) {
         // uniform task fields (readfirstlane: see gemm1_kernel)
         const int t = __builtin_amdgcn_readfirstlane(q.slot);
@@ -394,9 +388,7 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
 #define MOE_L2(NS)                                                                                                 \
     gemm_task<MODE, false, NS, RING, true, FusedSched>(a.g2.h, a.g2.h_scale, nullptr, 1, a.g2.w2, a.g2.w2_scale,   \
                                                        zero, e, row0, cb, a.g2.d_e, a.g2.d_h, a.g2.packed != 0,    \
-                                                       smem, nullptr, &a.g2, sch, rows, roww, par, &fx, ready);   \
-    combine_rows<NS, RING>(&pl, rows, cb, sync + kSyncArrive, a.nb2, static_cast<const float*>(a.g2.y), a.out, zero, k, \
-                           a.g1.d_h, smem)
+                                                       smem, nullptr, &a.g2, sch, rows, roww, par, &fx, ready)
         // one body per row-block count (nsub in [1, MT1] or [1, MT2])
         if (list == 0) {
             if constexpr (MT1 == 8) {
@@ -434,6 +426,9 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
 #undef MOE_L1
 #undef MOE_L2
     }
+
+    combine_share<RING>(&pl, sync + kSyncArrive, sync + kSyncTimeouts, a.T, a.nb2, k, a.g1.d_h,
+                        static_cast<const float*>(a.g2.y), a.out, zero, smem);
 
     // ---- exit: every memory operation of this workgroup is complete, then
     // it is counted; the last one resets the queue, the exit counter and the

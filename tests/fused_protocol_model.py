@@ -20,10 +20,11 @@ besides any GPU run:
   load its weights first, then waits (bounded) until that counter reaches the
   number of GEMM-1 column blocks times the GEMM-1 M-tiles it holds, then reads h.
 * Combine.  A GEMM-2 task stores its y rows, waits for them, then adds 1 per
-  row to the arrival counter of (token, column block); the workgroup that
-  brings it to the token's number of valid slots sums that token's y rows in
-  ascending slot order, writes the output columns and resets the counter.
-  Tokens without a valid slot get zero rows from workgroup (token mod grid).
+  row to the arrival counter of (token, column block).  Once its queue is
+  empty, workgroup b takes the (token, column block) outputs b, b + grid, ...:
+  it waits (bounded) until each counter reaches the token's number of valid
+  slots, sums the token's y rows in ascending slot order (zeros for a token
+  without a valid slot), writes the output columns and resets the counter.
 * Exit.  Each workgroup adds 1 to an exit counter after its last memory
   operation; the one that sees grid - 1 resets the queue, the exit counter and
   the M-tile counters, so the next call starts from zeros.
@@ -31,7 +32,8 @@ besides any GPU run:
 Deadlock freedom does not assume that all workgroups are resident: tasks are
 claimed in list order by running workgroups, GEMM-1 tasks never wait, and a
 GEMM-2 task waits only on GEMM-1 tasks of lower index, so the lowest unfinished
-claimed task can always proceed.  The simulation checks this with a resident
+claimed task can always proceed; the combine of a workgroup whose queue is
+empty waits only on GEMM-2 tasks, all claimed by then.  The simulation checks this with a resident
 capacity below the grid size.
 """
 from __future__ import annotations
@@ -124,7 +126,7 @@ class Faults:
     short_wait: bool = False        # GEMM-2 waits for one column block fewer
     flag_before_store: bool = False  # the M-tile counter is raised before h is stored
     no_reset: bool = False          # the last workgroup does not reset the counters
-    arrive_off_by_one: bool = False  # the combine fires one arrival early
+    arrive_off_by_one: bool = False  # the combine waits for one arrival fewer
 
 
 @dataclass
@@ -190,16 +192,13 @@ class Sim:
     def start_wg(self, b):
         self.running += 1
         self.started += 1
-        # prologue: the plan, zero rows of tokens without a valid slot, first claim
-        for t in range(b, self.T, self.grid):
-            if self.nvalid[t] == 0:
-                self.zero_rows[t] = self.zero_rows.get(t, 0) + 1
+        # prologue: the plan, then the first claim
         slot = self.claim()
         self.push(self.now + self.dur(1.0), lambda: self.run_task(b, slot))
 
     def run_task(self, b, slot):
         if slot < 0:
-            return self.finish_wg(b)
+            return self.combine_share(b)
         lst, e, row0, nsub, cb, m = self.task(slot)
         if slot in self.executed:
             self.errors.append(f"task {slot} executed twice")
@@ -257,28 +256,44 @@ class Sim:
             for p in rows:
                 if p >= 0:
                     self.y_ready[(int(p), cb)] = self.now
-            # the y stores are complete: one arrival per row at (token, column
-            # block); the arrival that completes a token combines it
-            last = []
+            # the y stores are complete: one arrival per row at (token, column block)
             for p in rows:
-                if p < 0:
-                    continue
-                t = int(p) // self.k
-                key = (t, cb)
-                old = self.st.arrive.get(key, 0)
-                self.st.arrive[key] = old + 1
-                need = self.nvalid[t] - (1 if self.f.arrive_off_by_one else 0)
-                if old + 1 == need:
-                    last.append(t)
-            for t in last:
+                if p >= 0:
+                    key = (int(p) // self.k, cb)
+                    self.st.arrive[key] = self.st.arrive.get(key, 0) + 1
+            self.push(self.now + self.dur(0.2), lambda: self.run_task(b, nxt.get("slot", -1)))
+
+        self.push(self.now + length, g2_end)
+
+    def combine_share(self, b):
+        nb2 = self.plan.nb2
+        items = list(range(b, self.T * nb2, self.grid))
+        polls = {"n": 0}
+
+        def need(i):
+            return int(self.nvalid[i // nb2]) - (1 if self.f.arrive_off_by_one else 0)
+
+        def wait():
+            if all(self.st.arrive.get((i // nb2, i % nb2), 0) >= need(i) for i in items):
+                return body()
+            polls["n"] += 1
+            if polls["n"] > self.spin_limit:
+                self.st.timeouts += 1
+                self.errors.append(f"combine of workgroup {b} timed out")
+                return body()
+            self.push(self.now + self.poll, wait)
+
+        def body():
+            for i in items:
+                t, cb = divmod(i, nb2)
                 for j in range(self.k):
                     if self.valid[t, j] and (t * self.k + j, cb) not in self.y_ready:
                         self.errors.append(f"combine of token {t}, column block {cb} read slot {j} before it was stored")
                 self.out_written[(t, cb)] = self.out_written.get((t, cb), 0) + 1
                 self.st.arrive[(t, cb)] = 0
-            self.push(self.now + self.dur(0.2), lambda: self.run_task(b, nxt.get("slot", -1)))
+            self.push(self.now + self.dur(0.3), lambda: self.finish_wg(b))
 
-        self.push(self.now + length, g2_end)
+        self.push(self.now + self.dur(0.2), wait)
 
     def finish_wg(self, b):
         old = self.st.exit
@@ -321,10 +336,6 @@ class Sim:
         if got != want:
             err.append(f"tasks executed {len(got)} of {len(want)}")
         for t in range(self.T):
-            if self.nvalid[t] == 0:
-                if self.zero_rows.get(t, 0) != 1:
-                    err.append(f"token {t} without a valid slot: zero row written {self.zero_rows.get(t, 0)} times")
-                continue
             for cb in range(self.plan.nb2):
                 c = self.out_written.get((t, cb), 0)
                 if c != 1:
