@@ -281,28 +281,51 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
         if (ok) atomicAdd(&wcnt[w * E + idv[u]], 1);
     }
     lds_barrier();
-    // counts; the per-wave counts become each wave's rank base within the expert
-    for (int e = tid; e < E; e += kGemmThreads) {
+    // Every wave reads all the per-wave counts at once and keeps, in lane l,
+    // those of experts l, l + 64, ...: the expert counts, this wave's rank base
+    // within each expert, and (a DPP scan) the padded offsets.  It writes
+    // padded offset + base into its own row of wcnt, which only it reads: the
+    // scatter below then needs no further barrier.  Wave 0 also publishes the
+    // counts and padded offsets; every wave ranks a share of the experts (the
+    // experts before e, with more rows or as many and a lower id, are a
+    // popcount of ballots).
+    constexpr int kJ = kMaxExperts / 64;
+    int cj[kJ], bj[kJ];
+#pragma unroll
+    for (int j = 0; j < kJ; ++j) {
+        const int e = lane + 64 * j;
+        int c = 0, base = 0;
+        if (64 * j < E) {
+#pragma unroll
+            for (int ww = 0; ww < kGemmWaves; ++ww) {
+                const int v = e < E ? wcnt[ww * E + e] : 0;
+                if (ww < w) base += v;
+                c += v;
+            }
+        }
+        cj[j] = e < E ? c : -1;
+        bj[j] = base;
+    }
+    lds_barrier();  // every wave has read the counts before any row is overwritten
+    {
         int run = 0;
 #pragma unroll
-        for (int ww = 0; ww < kGemmWaves; ++ww) {
-            const int c = wcnt[ww * E + e];
-            wcnt[ww * E + e] = run;
-            run += c;
+        for (int j = 0; j < kJ; ++j) {
+            if (64 * j >= E) break;
+            const int e = lane + 64 * j;
+            const int padded = e < E ? kBlockM * ((cj[j] + kBlockM - 1) / kBlockM) : 0;
+            const int incl = wave_inclusive_scan(padded, lane);
+            const int off = run + incl - padded;
+            if (e < E) {
+                wcnt[w * E + e] = off + bj[j];
+                if (w == 0) {
+                    pl.poff[e] = off;
+                    pl.cnt[e] = (short)cj[j];
+                }
+            }
+            run += __builtin_amdgcn_readlane(incl, 63);
         }
-        pl.cnt[e] = (short)run;
-    }
-    lds_barrier();
-    // padded offsets (wave 0); every wave ranks a share of the experts: lane l
-    // holds the counts of experts l, l + 64, ...; the experts before e (more
-    // rows, or as many and a lower id) are a popcount of ballots
-    auto tiles_of = [&](int e) { return (pl.cnt[e] + kBlockM - 1) / kBlockM; };
-    if (w == 0) wave_exclusive_scan256([&](int e) { return kBlockM * tiles_of(e); }, pl.poff, E, lane);
-    {
-        constexpr int kJ = kMaxExperts / 64;
-        int cj[kJ];
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) cj[j] = lane + 64 * j < E ? pl.cnt[lane + 64 * j] : -1;
+        if (w == 0 && lane == 0) pl.poff[E] = run;
         for (int e = w; e < E; e += kGemmWaves) {
             int c = 0;
 #pragma unroll
@@ -311,24 +334,21 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
             int r = 0;
 #pragma unroll
             for (int j = 0; j < kJ; ++j) {
+                if (64 * j >= E) break;
                 const int e2 = lane + 64 * j;
                 r += __popcll(__ballot(e2 < E && (cj[j] > c || (cj[j] == c && e2 < e))));
             }
             if (lane == 0) pl.order[r] = (unsigned char)e;
         }
     }
-    lds_barrier();
-    // the M-tile offsets of both GEMMs in rank order (waves 1, 2), the padding
-    // rows of each expert's group, and the stable scatter: each wave walks its
-    // chunk; lanes with the same expert find each other with one ballot per
-    // bit of the key (the id, or E for an invalid one: 9 bits), and the lowest
-    // lane of each group advances the wave's base
-    if (w == 1)
-        wave_exclusive_scan256([&](int r) { return (tiles_of(pl.order[r]) + MT1 - 1) / MT1; }, pl.moff[0], E, lane);
-    if (w == 2)
-        wave_exclusive_scan256([&](int r) { return (tiles_of(pl.order[r]) + MT2 - 1) / MT2; }, pl.moff[1], E, lane);
-    for (int e = tid; e < E; e += kGemmThreads)
-        for (int r = pl.poff[e] + pl.cnt[e]; r < pl.poff[e + 1]; ++r) pl.row_src[r] = -1;
+    // the stable scatter (no LDS atomics: the plan must come out the same in
+    // every workgroup, since a GEMM-2 task reads the h rows that another
+    // workgroup's GEMM-1 task placed by its own copy): each wave walks its chunk; lanes with the same expert
+    // find each other with one ballot per bit of the key (the id, or 256 for an
+    // invalid one: 9 bits); a lane's padded row is its wave's running position
+    // for the expert plus the lanes before it in the group, and the group's
+    // first lane advances that position (read once per step: a wave's LDS
+    // accesses stay in order)
     {
         const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
@@ -346,10 +366,24 @@ __global__ __launch_bounds__(kGemmThreads) void layer_kernel(LayerArgs a) {
                 m &= bit ? bal : ~bal;
             }
             const int wrank = __popcll(m & lt);
-            if (valid) pl.row_src[pl.poff[id] + wcnt[w * E + id] + wrank] = p;
-            // every lane has read its base above (a wave's LDS accesses stay in order)
-            if (valid && wrank == 0) wcnt[w * E + id] += __popcll(m);
+            if (valid) {
+                const int pos = wcnt[w * E + id];
+                pl.row_src[pos + wrank] = p;
+                if (wrank == 0) wcnt[w * E + id] = pos + __popcll(m);
+            }
         }
+    }
+    lds_barrier();
+    // the M-tile offsets of both GEMMs in rank order (waves 1, 2) and the
+    // padding rows of each expert's group
+    auto tiles_of = [&](int e) { return (pl.cnt[e] + kBlockM - 1) / kBlockM; };
+    if (w == 1)
+        wave_exclusive_scan256([&](int r) { return (tiles_of(pl.order[r]) + MT1 - 1) / MT1; }, pl.moff[0], E, lane);
+    if (w == 2)
+        wave_exclusive_scan256([&](int r) { return (tiles_of(pl.order[r]) + MT2 - 1) / MT2; }, pl.moff[1], E, lane);
+    for (int e = tid; e < E; e += kGemmThreads) {
+        const int r1 = pl.poff[e + 1];
+        for (int r = pl.poff[e] + pl.cnt[e]; r < r1; ++r) pl.row_src[r] = -1;
     }
     lds_barrier();
     const int n1 = pl.moff[0][E] * a.nb1, total = n1 + pl.moff[1][E] * a.nb2;
