@@ -337,7 +337,9 @@ def main():
     # dominant kernel: GEMM-1 (gate|up + SwiGLU), two thirds of the weights and
     # FLOPs; in the single launch, the one kernel and the whole layer's work
     kj = 0 if single else 1
-    kname = "layer_kernel" if single else "gemm1_kernel"
+    # the FP8 GEMM-1 of large batches is its own 8-wave kernel (the library's fp8_wide rule)
+    wide = (w.mode == W.MODE_FP8 and w.T * w.k >= 8192 and w.T * w.d_h < 2 ** 31 and 2 * w.d_e * w.d_h < 2 ** 31)
+    kname = "layer_kernel" if single else ("gemm1_fp8_kernel" if wide else "gemm1_kernel")
     k_us = float(np.mean(stage_ms[:, kj])) * 1e3
     g1_bytes = alg_bytes if single else gemm1_alg_bytes(w)
     g1_flops = flops if single else 4.0 * w.d_h * w.d_e * w.valid_assignments()
