@@ -117,14 +117,18 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
 // rows (2 KB per group block) and their row scales; 256-row tasks bring in 64
 // KB per 16.8 MFLOP, where 128-row ones bring 48 KB per 8.4: the per-CU rate
 // of direct-to-LDS loads (about 66-74 GB/s with eight issuing waves, measured)
-// bounds this kernel before HBM or the MFMAs do.  Seven waves issue the
-// stage loads; the last one is the scheduler (as in gemm_task) and computes.
+// bounds this kernel before HBM or the MFMAs do.  The four waves of wave row
+// 0, one per SIMD, issue the stage loads: a wave that issues direct-to-LDS
+// loads waits while the CU's address unit works through them (about 1 KB
+// per 16 cycles), and on each SIMD the other wave's MFMAs run meanwhile.  The
+// last wave is the scheduler (as in gemm_task) and computes.
 struct G1F8 {
     static constexpr int kWaves = kGemm1Fp8Waves;
     static constexpr int kSched = kWaves - 1;
-    static constexpr int kLoaders = kWaves - 1;
+    static constexpr int kLoaders = 4;  // waves 0..3: one per SIMD
     static constexpr int kStoreThreads = 64 * kSched;
     static constexpr int kMaxRows = 16 * kMaxRowBlocksFp8G1;
+    static_assert((kMaxRows + 63) / 64 <= kLoaders, "one row-scale load of 64 rows per loading wave");
     static constexpr int kBN = 128;
     static constexpr int kBRows = 2 * kBN;
     static constexpr int kBAll = kBRows / 8;                         // B loads per stage
@@ -228,12 +232,12 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
     const float* a_scale = static_cast<const float*>(g.x_scale);
     const float* w_scale = static_cast<const float*>(g.w1_scale);
     const bool loader = w < C::kLoaders;
-    // vector-memory loads per stage of this wave: B instructions w, w+7, ...,
-    // A instructions the same way, row-scale chunk c by wave (c == 0 ? 0 : c + 1),
-    // the block scales by wave 1
+    // vector-memory loads per stage of this wave: B instructions w, w+4, ...,
+    // A instructions the same way, row-scale chunk c by wave c, the block
+    // scales by wave 1
     const int n_b = loader ? (C::kBAll - 1 - w) / C::kLoaders + 1 : 0;
     const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / C::kLoaders + 1 : 0;
-    const int my_chunk = w == 0 ? 0 : (w >= 2 ? w - 1 : -1);  // row-scale chunk of this wave, or -1
+    const int my_chunk = w < C::kLoaders ? w : -1;  // row-scale chunk of this wave, or -1
     const bool s_rows = my_chunk >= 0 && my_chunk < kScaleChunks;
     const int n_s = (s_rows ? 1 : 0) + (w == 1 ? 1 : 0);
     const int loads_per_stage = n_b + n_a + n_s;
@@ -253,19 +257,19 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
         wbase = static_cast<const unsigned char*>(g.w1) + (int64_t)e * 2 * N_out * ld_bytes;
         b_step = kRowBytes;
     }
-    unsigned boff[C::kBMax];
-#pragma unroll
-    for (int j = 0; j < C::kBMax; ++j) {
-        const int b = w + C::kLoaders * j;  // B instruction: tile rows 8*b .. 8*b+7
-        if (g.packed) {
-            boff[j] = (unsigned)((b * 64 + lane) * 16);
-        } else {
-            const int r = 8 * b + (lane >> 3);
-            const int c = (lane & 7) ^ (r & 7);
-            const int wrow = r < C::kBN ? cb * C::kBN + r : N_out + cb * C::kBN + (r - C::kBN);
-            boff[j] = (unsigned)wrow * (unsigned)ld_bytes + (unsigned)(c * 16);
-        }
-    }
+    // B instruction b loads tile rows 8b .. 8b+7: a uniform part (b_row(b),
+    // scalar arithmetic) plus one per-lane offset shared by every b, since
+    // the 8 rows of an instruction sit on one side of the gate/up split and
+    // the swizzle depends only on the row mod 8
+    const unsigned b_lane = g.packed ? (unsigned)(lane * 16)
+                                     : (unsigned)(lane >> 3) * (unsigned)ld_bytes +
+                                           (unsigned)((((lane & 7) ^ ((lane >> 3) & 7))) * 16);
+    auto b_row = [&](int b) -> int64_t {
+        if (g.packed) return (int64_t)b * 1024;
+        const int r = 8 * b;
+        const int wrow = r < C::kBN ? cb * C::kBN + r : N_out + cb * C::kBN + (r - C::kBN);
+        return (int64_t)wrow * ld_bytes;
+    };
     const unsigned char* xbase = static_cast<const unsigned char*>(g.x);
     unsigned aoff[C::kAMax];
 #pragma unroll
@@ -315,7 +319,7 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
 #pragma unroll
         for (int j = 0; j < C::kBMax; ++j) {
             const int b = w + C::kLoaders * j;
-            if (b < C::kBAll) g2l16s(wbase, boff[j] + kboff, st + (unsigned)(b * 1024));
+            if (b < C::kBAll) g2l16s(wbase + b_row(b), b_lane + kboff, st + (unsigned)(b * 1024));
         }
 #pragma unroll
         for (int j = 0; j < C::kAMax; ++j) {
