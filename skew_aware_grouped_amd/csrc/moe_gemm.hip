@@ -384,42 +384,52 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
                 for (int j = 0; j < 4; ++j)
                     hv[i][f][j] = clamped ? clamped_act(acc[i][f][0][j], acc[i][f][1][j])
                                           : silu_mul(acc[i][f][0][j], acc[i][f][1][j]);
+        // Tile row of (i, j) in this lane: 32 i + 16 wm + 4 lg + j.  Every
+        // address below is one per-lane base plus a compile-time offset, so
+        // the loops keep no per-row addresses in registers.
+        const int row_l = 16 * wm + 4 * lg;
+        float* amax_w = s_amax + wn * C::kMaxRows + row_l;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int s = 2 * i + wm;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 float m = fmaxf(fabsf(hv[i][0][j]), fabsf(hv[i][1][j]));
                 m = row16_max(m);  // the 16 lanes of a row group hold one tile row
-                if (lr == 0) s_amax[wn * C::kMaxRows + 16 * s + 4 * lg + j] = m;
+                if (lr == 0) amax_w[32 * i + j] = m;
             }
         }
         lds_barrier();
-        float* hs = static_cast<float*>(g.h_scale);
+        const int nq = N_out / kQ;
+        float* hs_l = static_cast<float*>(g.h_scale) + (int64_t)(row0 + row_l) * nq + cb;
+        const float* amax_r = s_amax + row_l;
+        unsigned char* stage_l = stage + row_l * C::kEpiRow + 32 * wn + lr;
+        float sc_keep[NA][4];  // row scales, stored after the loop (no store waits inside it)
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const int s = 2 * i + wm;
-            float4 m = *reinterpret_cast<const float4*>(&s_amax[16 * s + 4 * lg]);
+            float4 m = *reinterpret_cast<const float4*>(&amax_r[32 * i]);
 #pragma unroll
             for (int ww = 1; ww < 4; ++ww) {
-                const float4 o = *reinterpret_cast<const float4*>(&s_amax[ww * C::kMaxRows + 16 * s + 4 * lg]);
+                const float4 o = *reinterpret_cast<const float4*>(&amax_r[ww * C::kMaxRows + 32 * i]);
                 m = make_float4(fmaxf(m.x, o.x), fmaxf(m.y, o.y), fmaxf(m.z, o.z), fmaxf(m.w, o.w));
             }
             const float am4[4] = {m.x, m.y, m.z, m.w};
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int rr = 16 * s + 4 * lg + j;
                 const float am = am4[j];
                 // scale amax/448; values are multiplied by its reciprocal
-                const float sc = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
+                sc_keep[i][j] = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
                 const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
                 const unsigned q2 =
                     (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][0][j] * inv, hv[i][1][j] * inv, 0, false);
-                stage[rr * C::kEpiRow + 32 * wn + lr] = (unsigned char)(q2 & 0xffu);
-                stage[rr * C::kEpiRow + 32 * wn + 16 + lr] = (unsigned char)((q2 >> 8) & 0xffu);
-                if (wn == 0 && lr == 0) hs[(int64_t)(row0 + rr) * (N_out / kQ) + cb] = sc;
+                stage_l[(32 * i + j) * C::kEpiRow] = (unsigned char)(q2 & 0xffu);
+                stage_l[(32 * i + j) * C::kEpiRow + 16] = (unsigned char)((q2 >> 8) & 0xffu);
             }
         }
+        if (wn == 0 && lr == 0)
+#pragma unroll
+            for (int i = 0; i < NW; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) hs_l[(int64_t)(32 * i + j) * nq] = sc_keep[i][j];
         lds_barrier();
         // h[row0 + r][cb*128 ...]: 128 bytes per row
         constexpr int kChunks = C::kEpiRow / 16;
