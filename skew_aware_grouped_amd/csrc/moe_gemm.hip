@@ -155,12 +155,14 @@ struct G1F8Rows {
 };
 
 // One K block of the FP8 GEMM-1 for a wave owning NW row blocks
-// (2 i + wm, i < NW): MFMAs of each row block against the wave's four B
-// fragments (two columns x gate/up), each promoted into acc[i].  The A
-// fragment and row scales of block i + 1 are read from LDS while block i's
-// MFMAs run; the promotion then waits for block i's results, during which
-// the other wave on the SIMD issues its MFMAs (registers do not allow a
-// second set of MFMA results in flight).
+// (2 i + wm, i < NW), with the weight fragment as the MFMA's first operand:
+// lane (lr, lg) of a 16x16 result holds token row lr of the row block and
+// weight columns 4 lg .. 4 lg + 3 of the fragment, so each lane promotes
+// with one row scale per row block (times the K block's gate or up block
+// scale).  The row scales of the wave's row blocks sit at stage positions
+// 16 lr + 8 wm + i (the loads place them so): two 16-byte reads per K block.
+// The A fragment of block i + 1 is read while block i's MFMAs run; the
+// other wave of the SIMD issues its MFMAs while this one promotes.
 template <int NW, int NA>
 __device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_rows_bytes, int wm, int wn, int lr,
                                             int lg, int swz, v4f (&acc)[NA][2][2]) {
@@ -177,36 +179,30 @@ __device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_ro
             Bf[f][0] = lds_frag32(sb + brow * kRowBytes, lg, swz);
             Bf[f][1] = lds_frag32(sb + (G1F8::kBN + brow) * kRowBytes, lg, swz);
         }
+        const float4 s0 = *reinterpret_cast<const float4*>(sc + 16 * lr + 8 * wm);
+        const float4 s1 = *reinterpret_cast<const float4*>(sc + 16 * lr + 8 * wm + 4);
+        const float sxr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         v8i A = lds_frag32(sa + (16 * wm + lr) * kRowBytes, lg, swz);
-        float4 sx = *reinterpret_cast<const float4*>(sc + 16 * wm + 4 * lg);
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
             v4f t[2][2];
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
-                for (int g = 0; g < 2; ++g) t[f][g] = mfma_fp8(A, Bf[f][g], zero4);
+                for (int g = 0; g < 2; ++g) t[f][g] = mfma_fp8(Bf[f][g], A, zero4);
             v8i An = A;
-            float4 sxn = sx;
-            if (i + 1 < NW) {
-                const int s = 2 * (i + 1) + wm;
-                An = lds_frag32(sa + (16 * s + lr) * kRowBytes, lg, swz);
-                sxn = *reinterpret_cast<const float4*>(sc + 16 * s + 4 * lg);
-            }
+            if (i + 1 < NW) An = lds_frag32(sa + (16 * (2 * (i + 1) + wm) + lr) * kRowBytes, lg, swz);
             __builtin_amdgcn_sched_barrier(0);
-            const float sxa[4] = {sx.x, sx.y, sx.z, sx.w};
+            const float pg = sxr[i] * swg, pu = sxr[i] * swu;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float pg = sxa[j] * swg, pu = sxa[j] * swu;
+            for (int f = 0; f < 2; ++f)
 #pragma unroll
-                for (int f = 0; f < 2; ++f) {
+                for (int j = 0; j < 4; ++j) {
                     acc[i][f][0][j] += t[f][0][j] * pg;
                     acc[i][f][1][j] += t[f][1][j] * pu;
                 }
-            }
             __builtin_amdgcn_sched_barrier(0);
             A = An;
-            sx = sxn;
         }
     }
 }
@@ -220,7 +216,6 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
     constexpr int kStageA = 16 * NSUB * kRowBytes;
     constexpr int kAInstr = 2 * NSUB;  // A loads per stage: 8 rows each
     constexpr int kRows = 16 * NSUB;
-    constexpr int kScaleChunks = (kRows + 63) / 64;  // row-scale loads: 64 rows each
     const int K = g.d_h, N_out = g.d_e;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -238,7 +233,7 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
     const int n_b = loader ? (C::kBAll - 1 - w) / C::kLoaders + 1 : 0;
     const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / C::kLoaders + 1 : 0;
     const int my_chunk = w < C::kLoaders ? w : -1;  // row-scale chunk of this wave, or -1
-    const bool s_rows = my_chunk >= 0 && my_chunk < kScaleChunks;
+    const bool s_rows = my_chunk >= 0;  // all four chunks: the positions are permuted
     const int n_s = (s_rows ? 1 : 0) + (w == 1 ? 1 : 0);
     const int loads_per_stage = n_b + n_a + n_s;
 
@@ -283,13 +278,16 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
             aoff[j] = (unsigned)(p >= 0 ? p / g.k : 0) * (unsigned)ld_bytes + (unsigned)(c * 16);
         }
     }
-    // row scale of tile row 64 * my_chunk + lane (row 0's past the task's rows
-    // and on padding rows), or in wave 1 lanes 0 and 1 the gate and up block
-    // scales of W1; byte offsets
+    // row scales: stage position p = 64 * my_chunk + lane holds the scale of
+    // tile row 16 (2 (p & 7) + ((p >> 3) & 1)) + (p >> 4), which is where
+    // g1f8_kblock reads it (position 16 lr + 8 wm + i for row block 2 i + wm);
+    // row 0's past the task's rows and on padding rows.  Or in wave 1 lanes
+    // 0 and 1 the gate and up block scales of W1; byte offsets
     const int kq = K / kQ;
     unsigned soff = 0;
     if (s_rows) {
-        const int srow = 64 * my_chunk + lane;
+        const int pos = 64 * my_chunk + lane;
+        const int srow = 16 * (2 * (pos & 7) + ((pos >> 3) & 1)) + (pos >> 4);
         const int p = srow < kRows ? rows[srow] : -1;
         soff = (unsigned)(p >= 0 ? p / g.k : 0) * (unsigned)(4 * kq);
     }
@@ -384,52 +382,49 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
                 for (int j = 0; j < 4; ++j)
                     hv[i][f][j] = clamped ? clamped_act(acc[i][f][0][j], acc[i][f][1][j])
                                           : silu_mul(acc[i][f][0][j], acc[i][f][1][j]);
-        // Tile row of (i, j) in this lane: 32 i + 16 wm + 4 lg + j.  Every
-        // address below is one per-lane base plus a compile-time offset, so
-        // the loops keep no per-row addresses in registers.
-        const int row_l = 16 * wm + 4 * lg;
+        // Row block i of this lane: tile row 32 i + 16 wm + lr, columns
+        // 32 wn + 16 f + 4 lg + j.  Every address below is one per-lane base
+        // plus a compile-time offset, so the loops keep no per-row addresses
+        // in registers.
+        const int row_l = 16 * wm + lr;
         float* amax_w = s_amax + wn * C::kMaxRows + row_l;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
+            float m = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float m = fmaxf(fabsf(hv[i][0][j]), fabsf(hv[i][1][j]));
-                m = row16_max(m);  // the 16 lanes of a row group hold one tile row
-                if (lr == 0) amax_w[32 * i + j] = m;
-            }
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(hv[i][f][j]));
+            // the four lane groups hold the row's other columns of this wave
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            if (lg == 0) amax_w[32 * i] = m;
         }
         lds_barrier();
         const int nq = N_out / kQ;
         float* hs_l = static_cast<float*>(g.h_scale) + (int64_t)(row0 + row_l) * nq + cb;
         const float* amax_r = s_amax + row_l;
-        unsigned char* stage_l = stage + row_l * C::kEpiRow + 32 * wn + lr;
-        float sc_keep[NA][4];  // row scales, stored after the loop (no store waits inside it)
+        unsigned* stage_l = reinterpret_cast<unsigned*>(stage + row_l * C::kEpiRow + 32 * wn + 4 * lg);
+        float sc_keep[NA];  // row scales, stored after the loop (no store waits inside it)
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            float4 m = *reinterpret_cast<const float4*>(&amax_r[32 * i]);
+            float am = amax_r[32 * i];
 #pragma unroll
-            for (int ww = 1; ww < 4; ++ww) {
-                const float4 o = *reinterpret_cast<const float4*>(&amax_r[ww * C::kMaxRows + 32 * i]);
-                m = make_float4(fmaxf(m.x, o.x), fmaxf(m.y, o.y), fmaxf(m.z, o.z), fmaxf(m.w, o.w));
-            }
-            const float am4[4] = {m.x, m.y, m.z, m.w};
+            for (int ww = 1; ww < 4; ++ww) am = fmaxf(am, amax_r[ww * C::kMaxRows + 32 * i]);
+            // scale amax/448; values are multiplied by its reciprocal
+            sc_keep[i] = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
+            const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float am = am4[j];
-                // scale amax/448; values are multiplied by its reciprocal
-                sc_keep[i][j] = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
-                const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
-                const unsigned q2 =
-                    (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(hv[i][0][j] * inv, hv[i][1][j] * inv, 0, false);
-                stage_l[(32 * i + j) * C::kEpiRow] = (unsigned char)(q2 & 0xffu);
-                stage_l[(32 * i + j) * C::kEpiRow + 16] = (unsigned char)((q2 >> 8) & 0xffu);
+            for (int f = 0; f < 2; ++f) {
+                // four e4m3 codes, columns 4 lg .. 4 lg + 3 in byte order
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(hv[i][f][0] * inv, hv[i][f][1] * inv, 0, false);
+                word = __builtin_amdgcn_cvt_pk_fp8_f32(hv[i][f][2] * inv, hv[i][f][3] * inv, word, true);
+                stage_l[(32 * i * C::kEpiRow + 16 * f) / 4] = (unsigned)word;
             }
         }
-        if (wn == 0 && lr == 0)
+        if (wn == 0 && lg == 0)
 #pragma unroll
-            for (int i = 0; i < NW; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) hs_l[(int64_t)(32 * i + j) * nq] = sc_keep[i][j];
+            for (int i = 0; i < NW; ++i) hs_l[(int64_t)(32 * i) * nq] = sc_keep[i];
         lds_barrier();
         // h[row0 + r][cb*128 ...]: 128 bytes per row
         constexpr int kChunks = C::kEpiRow / 16;

@@ -94,8 +94,13 @@ __device__ __forceinline__ void wait_vm_le_tree(int n) {
 __device__ __forceinline__ void wait_vm_le(int n) { wait_vm_le_tree<0, 63>(n < 63 ? n : 63); }
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, const v4f& c) {
-    // format 0 = E4M3 for both operands; E8M0 scale 127 = 1.0 (no MX scaling)
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    // format 0 = E4M3 for both operands, no MX scaling.  With zero scale
+    // operands clang lowers this builtin to the unscaled
+    // v_mfma_f32_16x16x128_f8f6f4 (it has no builtin of its own), which is
+    // about a tenth faster on gfx950 than the scaled form with unit (127)
+    // scales and gives bit-identical results; the FP8 parity tests against
+    // the oracle pin that lowering
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // scale_a / scale_b: E8M0 byte (low 8 bits) that lane (r, g) supplies for row
