@@ -50,7 +50,8 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     const int64_t mtile_cap1 = L->tile_cap / kSmallRowBlocks + (E < N ? E : N);
     const int64_t mtile_cap2 = mtile_cap1;
     L->block_n1 = gemm1_block_n(d->mode);
-    L->block_n2 = gemm2_block_n(d->mode);
+    L->block_n2 = gemm2_block_n(
+        d->mode, fp8_wide2(d->mode, d->launch, d->num_tokens, d->top_k, d->num_experts, d->d_hidden, d->d_expert));
     L->max_row_blocks = gemm1_max_row_blocks(d->mode, d->num_tokens, d->top_k, d->d_hidden, d->d_expert);
     L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
     L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
@@ -93,7 +94,7 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
 }
 
 // Per-device cache of the chip size and of the GEMM kernels' occupancy.
-// Slot 4 holds the 8-wave FP8 GEMM-1 (fp8_wide).
+// Slot 4 holds the 8-wave FP8 GEMM-1 and GEMM-2 (fp8_wide, fp8_wide2).
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
@@ -105,7 +106,7 @@ std::mutex g_mu;
 DeviceInfo g_dev[64];
 
 // occ_layer (may be null): resident workgroups per CU of the single-launch kernel
-hipError_t device_info(int mode, bool wide, int* cus, int* occ1, int* occ2, int* occ_layer = nullptr) {
+hipError_t device_info(int mode, bool wide, bool wide2, int* cus, int* occ1, int* occ2, int* occ_layer = nullptr) {
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
@@ -130,9 +131,8 @@ hipError_t device_info(int mode, bool wide, int* cus, int* occ1, int* occ2, int*
     }
     *cus = di.cus;
     if (occ_layer) *occ_layer = di.occ_layer[mode_fp8(mode) ? mode : MOE_MODE_BF16];
-    const int slot = wide ? 4 : gemm_mode(mode);
-    *occ1 = di.occ1[slot];
-    *occ2 = di.occ2[slot];
+    *occ1 = di.occ1[wide ? 4 : gemm_mode(mode)];
+    *occ2 = di.occ2[wide2 ? 4 : gemm_mode(mode)];
     return hipSuccess;
 }
 
@@ -278,7 +278,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (single) {
         int occ = 1;
-        if (device_info(mode, false, &cus, &occ1, &occ2, &occ) != hipSuccess) return MOE_ERR_HIP;
+        if (device_info(mode, false, false, &cus, &occ1, &occ2, &occ) != hipSuccess) return MOE_ERR_HIP;
         const int64_t N = T * dims->top_k;
         const int64_t E = dims->num_experts;
         const int mtb = layer_mtile_blocks(mode);
@@ -324,7 +324,9 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
         return MOE_OK;
     }
     const bool wide = fp8_wide(mode, T, dims->top_k, dims->d_hidden, dims->d_expert);
-    if (device_info(mode, wide, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
+    const bool wide2 =
+        fp8_wide2(mode, dims->launch, T, dims->top_k, dims->num_experts, dims->d_hidden, dims->d_expert);
+    if (device_info(mode, wide, wide2, &cus, &occ1, &occ2) != hipSuccess) return MOE_ERR_HIP;
     // timing events of launch i (route, GEMM-1, GEMM-2, combine), or none
     auto ev = [&](int i) -> hipEvent_t { return events ? static_cast<hipEvent_t>(events[i]) : nullptr; };
     const int32_t E = dims->num_experts, k = dims->top_k, d_h = dims->d_hidden, d_e = dims->d_expert;
@@ -339,11 +341,12 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.nb2 = d_h / L.block_n2;
     r.min_tasks1 = cus * occ1;
     r.mb1_max = wide ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
-    r.mb2 = gemm2_row_blocks(mode);
+    r.mb2 = gemm2_row_blocks(mode, wide2);
     r.mix1 = mode != MOE_MODE_FP8;
     // GEMM-2's tasks are short: 128-row tiles only when every workgroup slot
-    // still gets two tasks (Qwen shapes at 1024 tokens stay at 64-row tiles)
-    r.min_tasks2 = 2 * cus * occ2;
+    // still gets two tasks (Qwen shapes at 1024 tokens stay at 64-row tiles);
+    // the 8-wave FP8 kernel's 256-row tiles when every slot gets one
+    r.min_tasks2 = (wide2 ? 1 : 2) * cus * occ2;
     // persistent grids: at most one workgroup per task, at most what fits on the chip
     const int grid1 = (int)std::max<int64_t>(std::min<int64_t>(L.task1_cap, (int64_t)cus * occ1), 1);
     const int grid2 = (int)std::max<int64_t>(std::min<int64_t>(L.task2_cap, (int64_t)cus * occ2), 1);
@@ -409,7 +412,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     g2.d_h = d_h;
     g2.d_e = d_e;
     g2.packed = dims->weight_layout == MOE_WEIGHTS_PACKED;
-    if (launch_gemm2(gemm_mode(mode), g2, grid2, s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_gemm2(gemm_mode(mode), wide2, g2, grid2, s, ev(4), ev(5)) != hipSuccess) return MOE_ERR_HIP;
 
     CombineArgs c{};
     c.y = g2.y;
@@ -499,7 +502,7 @@ int moe_pack_weights(const moe_dims* dims, const void* w1, const void* w2, void*
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (launch_pack(w1, w1_packed, E, d_e, d_h * eb, gemm1_block_n(d.mode), true, s) != hipSuccess)
         return MOE_ERR_HIP;
-    if (launch_pack(w2, w2_packed, E, d_h, d_e * eb, gemm2_block_n(d.mode), false, s) != hipSuccess)
+    if (launch_pack(w2, w2_packed, E, d_h, d_e * eb, gemm2_block_n(d.mode, false), false, s) != hipSuccess)
         return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -490,6 +490,258 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a
     }
 }
 
+// ------------------------------------------------------- FP8 GEMM-2 (8 waves)
+// Block-scaled FP8 GEMM-2 for tasks of up to 16 group blocks (256 rows of h)
+// by 256 output columns, on the geometry of the 8-wave GEMM-1: a stage holds
+// 256 rows of W2 (32 KB), the task's h rows and their row scales; wave
+// (wm, wn) owns output columns [64 wn, 64 wn + 64) (four 16-column fragments)
+// of row blocks wm, wm + 2, ...; the weight fragment is the MFMA's first
+// operand, so each lane promotes with one row scale of h per row block times
+// the K block's W2 block scale (the 256 columns span two 128x128 scale
+// blocks: waves 0, 1, 4, 5 take the first, the others the second).  The
+// stage loads come from the four waves of wave row 0, one per SIMD.  Output:
+// y[p] = bf16(acc * routing weight of the row), for the task's rows with a
+// source assignment p (padding rows store nothing).
+namespace g2w {
+constexpr int kBRows = 256;  // output columns per task = W2 rows per stage
+constexpr int kOutRow = 2 * kBRows;  // bytes of one staged output row (bf16)
+static_assert(kOutRow * 16 * kMaxRowBlocksFp8G1 <= G1F8::kRing, "output staging must fit in the ring");
+}  // namespace g2w
+
+template <int NW, int NA>
+__device__ __forceinline__ void g2f8_kblock(const unsigned char* st, int nsub_rows_bytes, int wm, int wn, int lr,
+                                            int lg, int swz, v4f (&acc)[NA][4]) {
+    if constexpr (NW > 0) {
+        const unsigned char* sb = st;
+        const unsigned char* sa = st + G1F8::kStageB;
+        const float* sc = reinterpret_cast<const float*>(st + G1F8::kStageB + nsub_rows_bytes);
+        const float sw = sc[G1F8::kScaleBlk / 4 + (wn >> 1)];
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+        v8i Bf[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) Bf[f] = lds_frag32(sb + (64 * wn + 16 * f + lr) * kRowBytes, lg, swz);
+        const float4 s0 = *reinterpret_cast<const float4*>(sc + 16 * lr + 8 * wm);
+        const float4 s1 = *reinterpret_cast<const float4*>(sc + 16 * lr + 8 * wm + 4);
+        const float sxr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        v8i A = lds_frag32(sa + (16 * wm + lr) * kRowBytes, lg, swz);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            v4f t[4];
+#pragma unroll
+            for (int f = 0; f < 4; ++f) t[f] = mfma_fp8(Bf[f], A, zero4);
+            v8i An = A;
+            if (i + 1 < NW) An = lds_frag32(sa + (16 * (2 * (i + 1) + wm) + lr) * kRowBytes, lg, swz);
+            __builtin_amdgcn_sched_barrier(0);
+            const float pw = sxr[i] * sw;
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][f][j] += t[f][j] * pw;
+            __builtin_amdgcn_sched_barrier(0);
+            A = An;
+        }
+    }
+}
+
+template <int NSUB>
+__device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, int cb, unsigned char* smem,
+                                          SchedT<kRowsLdsFp8G1>& sch, const int* rows, const float* roww, int par) {
+    using C = G1F8;
+    constexpr int S = C::stages(NSUB);
+    constexpr int kStage = C::stage_bytes(NSUB);
+    constexpr int kStageA = 16 * NSUB * kRowBytes;
+    constexpr int kAInstr = 2 * NSUB;  // A loads per stage: 8 rows each
+    constexpr int kRows = 16 * NSUB;
+    constexpr int kBAll = g2w::kBRows / 8;  // B loads per stage
+    constexpr int kLoaders = 4;             // waves 0..3, one per SIMD
+    constexpr int kBMax = (kBAll + kLoaders - 1) / kLoaders;
+    constexpr int kAMax = (2 * kMaxRowBlocksFp8G1 + kLoaders - 1) / kLoaders;
+    const int K = g.d_e, N_out = g.d_h;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = w >> 2, wn = w & 3;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nk = K / 128;
+    const unsigned smem_lds = lds_offset(smem);
+    const int64_t ld_bytes = K;  // bytes per operand row (h and W2 rows)
+    const bool loader = w < kLoaders;
+    // loads per stage of a loading wave: B and A instructions w, w+4, ...,
+    // one 64-position chunk of row scales, and in wave 1 the two block scales
+    const int n_b = loader ? (kBAll - 1 - w) / kLoaders + 1 : 0;
+    const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / kLoaders + 1 : 0;
+    const int n_s = (loader ? 1 : 0) + (w == 1 ? 1 : 0);
+    const int loads_per_stage = n_b + n_a + n_s;
+
+    // Addresses: a uniform part per instruction (scalar arithmetic) plus one
+    // per-lane offset shared by all instructions of an operand: the 8 rows of
+    // an instruction are consecutive and the swizzle depends on the row mod 8
+    // only.  h rows are the task's own padded rows (GEMM-1 wrote zeros into
+    // the padding rows, with scale 1).
+    const unsigned lane_rm = (unsigned)(lane >> 3) * (unsigned)ld_bytes +
+                             (unsigned)((((lane & 7) ^ ((lane >> 3) & 7))) * 16);
+    const unsigned b_lane = g.packed ? (unsigned)(lane * 16) : lane_rm;
+    const unsigned char* w2 = static_cast<const unsigned char*>(g.w2);
+    const int64_t tiles_per_expert = N_out / 128;  // packed W2: 128-row tiles, nk stages of 16 KB each
+    auto b_row = [&](int b) -> int64_t {
+        if (g.packed) {
+            const int64_t tile = (int64_t)e * tiles_per_expert + 2 * cb + (b >> 4);
+            return tile * nk * 16384 + (int64_t)(b & 15) * 1024;
+        }
+        return ((int64_t)e * N_out + (int64_t)cb * g2w::kBRows + 8 * b) * ld_bytes;
+    };
+    const unsigned b_step = g.packed ? 16384u : (unsigned)kRowBytes;
+    const unsigned char* hbase = static_cast<const unsigned char*>(g.h) + (int64_t)row0 * ld_bytes;
+    const float* h_scale = static_cast<const float*>(g.h_scale);
+    const float* w_scale = static_cast<const float*>(g.w2_scale);
+    // row scales: stage position p = 64 w + lane holds the scale of tile row
+    // 16 (2 (p & 7) + ((p >> 3) & 1)) + (p >> 4), where g2f8_kblock reads it
+    // (row 0's past the task's rows); wave 1 lanes 0 and 1: the two W2 block
+    // scales of the task's columns; byte offsets
+    const int kq = K / kQ;
+    unsigned soff = 0;
+    if (loader) {
+        const int pos = 64 * w + lane;
+        const int srow = 16 * (2 * (pos & 7) + ((pos >> 3) & 1)) + (pos >> 4);
+        soff = (unsigned)(row0 + (srow < kRows ? srow : 0)) * (unsigned)(4 * kq);
+    }
+    unsigned bsoff = 0;
+    if (w == 1 && lane < 2) bsoff = (unsigned)(((int64_t)e * (N_out / kQ) + 2 * cb + lane) * kq) * 4u;
+
+    auto issue = [&](int kc) {
+        const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
+        const unsigned koff = (unsigned)kc * kRowBytes;
+        const unsigned kboff = (unsigned)kc * b_step;
+        if (!loader) return;
+#pragma unroll
+        for (int j = 0; j < kBMax; ++j) {
+            const int b = w + kLoaders * j;
+            if (b < kBAll) g2l16s(w2 + b_row(b), b_lane + kboff, st + (unsigned)(b * 1024));
+        }
+#pragma unroll
+        for (int j = 0; j < kAMax; ++j) {
+            const int ai = w + kLoaders * j;
+            if (ai < kAInstr)
+                g2l16s(hbase + (int64_t)(8 * ai) * ld_bytes, lane_rm + koff, st + (unsigned)(C::kStageB + ai * 1024));
+        }
+        const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
+        g2l4s(h_scale, soff + 4u * (unsigned)kc, ss + (unsigned)(256 * w));
+        // lanes 0 and 1 only: the other lanes would land past the stage
+        if (w == 1 && lane < 2) g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)C::kScaleBlk);
+    };
+
+    const int swz = lr & 7;
+    const int npro = nk < S - 1 ? nk : S - 1;
+    for (int kc = 0; kc < npro; ++kc) issue(kc);
+    const int claim_at = nk > kClaimLead ? nk - kClaimLead : 0;
+    const int settle_at = nk > kClaimLead - 2 ? nk - (kClaimLead - 2) : 0;
+    const int rows_at = nk > kClaimLead - 4 ? nk - (kClaimLead - 4) : 0;
+    unsigned char* stage = smem;  // [kRows][kOutRow]
+
+    auto body = [&](auto nw_c) {
+        constexpr int NW = decltype(nw_c)::value;
+        constexpr int NA = NW > 0 ? NW : 1;
+        v4f acc[NA][4];
+        const v4f zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[i][f] = zero4;
+        for (int kc = 0; kc < nk; ++kc) {
+            if (loader) {
+                const int younger = (nk - 1 - kc) < (S - 2) ? (nk - 1 - kc) : (S - 2);
+                wait_vm_le(younger * loads_per_stage);
+            }
+            lds_barrier();
+            if (kc + S - 1 < nk) issue(kc + S - 1);
+            if (w == C::kSched) {
+                if (kc == claim_at && lane == 0) sch.claim();
+                if (kc == settle_at) sch.settle(true);
+                if (kc == rows_at) sch.load_rows(par ^ 1);
+            }
+            g2f8_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
+        }
+        __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
+
+        // ---- epilogue: routing weight, bf16, staged rows, 16-byte stores.
+        // Row block i of this lane: tile row 32 i + 16 wm + lr, columns
+        // 64 wn + 16 f + 4 lg + j (four consecutive bf16 = 8 bytes)
+        lds_barrier();
+        const int row_l = 16 * wm + lr;
+        unsigned char* stage_l = stage + row_l * g2w::kOutRow + 2 * (64 * wn + 4 * lg);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const float wt = roww[row_l + 32 * i];  // 0 on padding rows
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const unsigned lo = f32_to_bf16(acc[i][f][0] * wt) | (f32_to_bf16(acc[i][f][1] * wt) << 16);
+                const unsigned hi = f32_to_bf16(acc[i][f][2] * wt) | (f32_to_bf16(acc[i][f][3] * wt) << 16);
+                *reinterpret_cast<uint2*>(stage_l + 32 * i * g2w::kOutRow + 2 * 16 * f) = make_uint2(lo, hi);
+            }
+        }
+        lds_barrier();
+        constexpr int kChunks = g2w::kOutRow / 16;
+        unsigned char* y = static_cast<unsigned char*>(g.y);
+        const int64_t yrow_bytes = (int64_t)N_out * 2;
+        if (w != C::kSched)
+            for (int i = threadIdx.x; i < kRows * kChunks; i += C::kStoreThreads) {
+                const int r = i / kChunks, c = i - r * kChunks;
+                const int p = rows[r];
+                if (p < 0) continue;
+                *reinterpret_cast<v4i*>(y + (int64_t)p * yrow_bytes + (int64_t)cb * g2w::kOutRow + c * 16) =
+                    *reinterpret_cast<const v4i*>(stage + r * g2w::kOutRow + c * 16);
+            }
+        if (w == C::kSched) sch.publish();
+        lds_barrier();  // the ring and the staging area are refilled by the next task
+    };
+    if (wm == 0)
+        body(std::integral_constant<int, G1F8Rows<NSUB, 0>::n>{});
+    else
+        body(std::integral_constant<int, G1F8Rows<NSUB, 1>::n>{});
+}
+
+__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm2_fp8_kernel(Gemm2Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
+    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+    const int xcd = my_xcd();
+    if (threadIdx.x <= kXcds) q.seg[threadIdx.x] = a.ctl[kCtlSeg2 + threadIdx.x];
+    if (threadIdx.x == 0) q.mask = 0;
+    lds_barrier();
+    if (threadIdx.x >= 64 * G1F8::kSched) {
+        SchedT<kRowsLdsFp8G1> sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
+        sch.first();
+        sch.load_rows(0);
+        sch.publish();
+    }
+    lds_barrier();
+    for (int par = 0;; par ^= 1) {
+        const int t = __builtin_amdgcn_readfirstlane(q.slot);  // uniform, as in gemm1_fp8_kernel
+        if (t < 0) break;
+        const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
+        const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
+        SchedT<kRowsLdsFp8G1> sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
+#define MOE_G2F8(NS) g2f8_task<NS>(a, e, row0, cb, smem, sch, q.rows[par], q.roww[par], par)
+        switch (nsub) {
+            case 1: MOE_G2F8(1); break;
+            case 2: MOE_G2F8(2); break;
+            case 3: MOE_G2F8(3); break;
+            case 4: MOE_G2F8(4); break;
+            case 5: MOE_G2F8(5); break;
+            case 6: MOE_G2F8(6); break;
+            case 7: MOE_G2F8(7); break;
+            case 8: MOE_G2F8(8); break;
+            case 9: MOE_G2F8(9); break;
+            case 10: MOE_G2F8(10); break;
+            case 11: MOE_G2F8(11); break;
+            case 12: MOE_G2F8(12); break;
+            case 13: MOE_G2F8(13); break;
+            case 14: MOE_G2F8(14); break;
+            case 15: MOE_G2F8(15); break;
+            default: MOE_G2F8(16); break;
+        }
+#undef MOE_G2F8
+    }
+}
+
 // ---------------------------------------------------------------- combine
 // out[t, c..c+8) = sum_j y[t*k + j, c..c+8) in ascending j from +0.0, fp32,
 // one final rounding.  Dropped assignments have no y row and are skipped.
@@ -653,8 +905,11 @@ hipError_t launch_gemm1(int mode, bool wide, const Gemm1Args& a, int grid, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    if (mode == MOE_MODE_MXFP8)
+hipError_t launch_gemm2(int mode, bool wide, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0,
+                        hipEvent_t t1) {
+    if (mode == MOE_MODE_FP8 && wide)
+        hipExtLaunchKernelGGL(gemm2_fp8_kernel, dim3(grid), dim3(kGemm1Fp8Threads), 0, s, t0, t1, 0, a);
+    else if (mode == MOE_MODE_MXFP8)
         hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_MXFP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_FP8)
         hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_FP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
@@ -684,7 +939,8 @@ hipError_t gemm_occupancy(int mode, bool wide, int* g1, int* g2) {
     } else if (mode == MOE_MODE_FP8) {
         e1 = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_fp8_kernel, kGemm1Fp8Threads, 0)
                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
-        e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
+        e2 = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_fp8_kernel, kGemm1Fp8Threads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_FP8>, kGemmThreads, 0);
     } else if (mode == MOE_MODE_BF16) {
         e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_BF16>, kGemmThreads, 0);
         e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_BF16>, kGemmThreads, 0);

@@ -46,6 +46,16 @@ inline bool fp8_wide(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
 inline int gemm1_max_row_blocks(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
     return fp8_wide(mode, T, k, d_h, d_e) ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
 }
+// FP8 GEMM-2 at the same batches (four launches only: the single launch keeps
+// its own task shapes) runs an 8-wave kernel on the same geometry: tasks of
+// up to 16 group blocks by 256 output columns, so it also needs d_h a
+// multiple of 256 and n_pad*d_e below 2^31 (32-bit offsets into h).
+inline bool fp8_wide2(int mode, int launch, int64_t T, int64_t k, int64_t E, int64_t d_h, int64_t d_e) {
+    const int64_t n_pad = T * k + (E < T * k ? E : T * k) * (kBlockM - 1);
+    return launch == MOE_LAUNCH_MULTI && fp8_wide(mode, T, k, d_h, d_e) && d_h % 256 == 0 &&
+           n_pad * d_e < ((int64_t)1 << 31);
+}
+constexpr int kMaxRowBlocksFp8G2 = 16;
 // Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = 64 * kGemmWaves;
@@ -95,8 +105,10 @@ constexpr bool mode_fp8(int mode) { return mode == MOE_MODE_FP8 || mode == MOE_M
 // The GEMM kernels of a mode: INT8 tokens run the bf16 GEMMs on their widened codes
 inline int gemm_mode(int mode) { return mode == MOE_MODE_INT8 ? MOE_MODE_BF16 : mode; }
 inline int gemm1_block_n(int mode) { return mode_fp8(mode) ? 128 : 64; }
-inline int gemm2_block_n(int) { return 128; }
-inline int gemm2_row_blocks(int mode) { return mode == MOE_MODE_MXFP8 ? kSmallRowBlocks : kMaxRowBlocks2; }
+inline int gemm2_block_n(int, bool wide2) { return wide2 ? 256 : 128; }
+inline int gemm2_row_blocks(int mode, bool wide2) {
+    return wide2 ? kMaxRowBlocksFp8G2 : mode == MOE_MODE_MXFP8 ? kSmallRowBlocks : kMaxRowBlocks2;
+}
 
 struct RouteArgs {
     const int32_t* ids;
@@ -208,7 +220,7 @@ hipError_t launch_pack(const void* w, void* wp, int64_t E, int64_t n_out, int64_
 // wide: FP8 only, the 8-wave kernel (fp8_wide)
 hipError_t launch_gemm1(int mode, bool wide, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
-hipError_t launch_gemm2(int mode, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
+hipError_t launch_gemm2(int mode, bool wide, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
 hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEvent_t t0 = nullptr,
                           hipEvent_t t1 = nullptr);

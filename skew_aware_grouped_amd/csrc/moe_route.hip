@@ -245,9 +245,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     // M-tiles of 8 group blocks (fewer weight re-reads) when that still leaves
     // min_tasks1 (min_tasks2) tasks, otherwise kSmallRowBlocks (more tasks to
-    // spread over the CUs); FP8 GEMM-1 (mb1_max 16) takes 16-block M-tiles
-    // when those still leave min_tasks1 tasks.  The last wave decides for both
-    // lists after its share of the ranking
+    // spread over the CUs); the 8-wave FP8 GEMMs (mb1_max 16, mb2 16) take
+    // 16-block M-tiles when those still leave min_tasks1 (min_tasks2) tasks.
+    // The last wave decides for both lists after its share of the ranking
     if (wave == kRouteWaves - 1) {
         int big = 0, big16 = 0;
         for (int e = lane; e < E; e += 64) {
@@ -260,7 +260,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             s_mb1 = a.mb1_max == 16 && big16 * a.nb1 >= a.min_tasks1 ? 16
                     : big * a.nb1 >= a.min_tasks1                   ? kMaxRowBlocks1
                                                                     : kSmallRowBlocks;
-            s_mb2 = a.mb2 == 8 && big * a.nb2 >= a.min_tasks2 ? 8 : kSmallRowBlocks;
+            s_mb2 = a.mb2 == 16 && big16 * a.nb2 >= a.min_tasks2  ? 16
+                    : a.mb2 >= 8 && big * a.nb2 >= a.min_tasks2 ? 8
+                                                                 : kSmallRowBlocks;
         }
     }
     __syncthreads();
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // group blocks per GEMM-1 M-tile of rank r
     auto lg1 = [&](int r) { return mb1 == 16 ? 4 : r < r8 ? 3 : 2; };
     auto mb1_of = [&](int r) { return 1 << lg1(r); };
-    const int lg_mb2 = mb2 == 8 ? 3 : 2;
+    const int lg_mb2 = mb2 == 16 ? 4 : mb2 == 8 ? 3 : 2;
     auto mtiles = [&](int list, int r) {
         const int lg = list == 0 ? lg1(r) : lg_mb2;
         return (s_rtiles[r] + (1 << lg) - 1) >> lg;

@@ -43,6 +43,24 @@ def test_workspace_layout_is_disjoint_and_aligned():
         assert moe.moe_workspace_bytes(d) == L.total
 
 
+def test_gemm_task_shapes_follow_batch_and_launch():
+    """Column blocks and M-tile limit in the layout: FP8 batches of at least
+    8192 assignments take the 8-wave GEMMs (16-block M-tiles; GEMM-2 with
+    256-column tasks when d_h is a multiple of 256 and the layer runs as four
+    launches), everything else 128-column GEMM-2 tasks."""
+    big = dict(mode=moe.MOE_MODE_FP8, T=8192, E=32, k=2, d_h=7168, d_e=2048)
+    L = moe.moe_workspace_layout(_dims(**big))
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 256, 16)
+    L = moe.moe_workspace_layout(_dims(**dict(big, d_h=7296)))  # 57 * 128: GEMM-2 keeps 128 columns
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 128, 16)
+    L = moe.moe_workspace_layout(_dims(**dict(big, T=4095)))  # 8190 assignments: 4-wave GEMMs
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 128, 8)
+    L = moe.moe_workspace_layout(_dims(**dict(big, mode=moe.MOE_MODE_MXFP8)))
+    assert L.block_n2 == 128
+    L = moe.moe_workspace_layout(_dims(**dict(big, T=1024, launch=moe.MOE_LAUNCH_SINGLE)))
+    assert L.block_n2 == 128
+
+
 def test_invalid_dims_rejected():
     assert moe.moe_workspace_bytes(_dims(d_h=100)) == 0
     assert moe.moe_workspace_bytes(_dims(E=0)) == 0

@@ -159,6 +159,14 @@ def test_large_batch_routing_path(oracle, mode):
     _check(w, oracle, label="large_batch")
 
 
+def test_fp8_wide_gemm1_with_narrow_gemm2(oracle):
+    """8400 assignments take the 8-wave FP8 GEMM-1; d_h = 384 is not a
+    multiple of 256, so GEMM-2 keeps the 4-wave kernel and 128-column tasks
+    (its grid then comes from that kernel's occupancy).  Every row compared."""
+    w = W.custom(4200, 16, 2, 384, 256, W.MODE_FP8, seed=45, routing=("zipf", 1.1, 2))
+    _check(w, oracle, label="wide1_narrow2")
+
+
 def test_more_m_tiles_than_rank_table(oracle):
     """About 1.08 million assignments over 64 experts: more than 8192 GEMM
     M-tiles per task list, so the task builder finds each task's expert by
