@@ -673,8 +673,8 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
             const float wt = roww[row_l + 32 * i];  // 0 on padding rows
 #pragma unroll
             for (int f = 0; f < 4; ++f) {
-                const unsigned lo = f32_to_bf16(acc[i][f][0] * wt) | (f32_to_bf16(acc[i][f][1] * wt) << 16);
-                const unsigned hi = f32_to_bf16(acc[i][f][2] * wt) | (f32_to_bf16(acc[i][f][3] * wt) << 16);
+                const unsigned lo = pk_bf16(acc[i][f][0] * wt, acc[i][f][1] * wt);
+                const unsigned hi = pk_bf16(acc[i][f][2] * wt, acc[i][f][3] * wt);
                 *reinterpret_cast<uint2*>(stage_l + 32 * i * g2w::kOutRow + 2 * 16 * f) = make_uint2(lo, hi);
             }
         }

@@ -121,6 +121,14 @@ __device__ __forceinline__ unsigned f32_to_bf16(float f) {
     return u >> 16;
 }
 
+// two binary32 -> bf16 in one v_cvt_pk_bf16_f32 (round to nearest even, as
+// f32_to_bf16 for every finite value): a in the low half, b in the high half
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned pk_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
 // binary32 -> E4M3FN code via the hardware converter (round to nearest even)
 __device__ __forceinline__ unsigned f32_to_e4m3(float f) {
     return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(f, 0.0f, 0, false) & 0xffu;
