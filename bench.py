@@ -63,13 +63,19 @@ def gemm1_alg_bytes(w):
     return float(b)
 
 
-KERNEL_SOURCES = ["moe_gemm.hip", "moe_gemm_task.h", "moe_internal.h", "moe_route.hip", "moe_layer.hip"]
+# The sources each timed kernel is compiled from: a traffic record stays valid
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "layer_kernel": ["moe_layer.hip", "moe_gemm_task.h", "moe_wave.h", "moe_internal.h"],
+    "route_kernel": ["moe_route.hip", "moe_wave.h", "moe_internal.h"],
+}
+GEMM_SOURCES = ["moe_gemm.hip", "moe_gemm_task.h", "moe_internal.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel):
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES.get(kernel, GEMM_SOURCES):
         with open(os.path.join(ROOT, "skew_aware_grouped_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -80,7 +86,7 @@ def measured_traffic(kernel, workload, weights):
     (profiles/, FETCH_SIZE + WRITE_SIZE scaled by a copy of known size), or
     None when no record exists or the kernel sources changed since it was taken."""
     import glob
-    src = kernel_source_hash()
+    src = kernel_source_hash(kernel)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path) as f:
             for line in f:
