@@ -90,13 +90,38 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // 1. per-wave histograms (LDS atomics on the wave's own row); the ids
     // stay in LDS for the scatter when they fit
     int my_drop = 0;
-    for (int p = c_lo + lane; p < c_hi; p += 64) {
-        const int id = a.ids[p];
-        if (in_lds) s_ids[p] = (unsigned)id < (unsigned)E ? (short)id : (short)-1;
-        if ((unsigned)id < (unsigned)E)
-            atomicAdd(&s_wcnt[wave][id], 1);
-        else
-            ++my_drop;
+    if (in_lds) {
+        // the wave's whole chunk (at most kLdsIds / kRouteWaves ids) as one
+        // batch of independent loads: one memory round trip, where a loop
+        // whose every step ends in an LDS atomic on the loaded id waits for
+        // each load in turn
+        constexpr int kPer = kLdsIds / kRouteWaves / 64;
+        int idv[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int p = c_lo + lane + 64 * u;
+            idv[u] = p < c_hi ? a.ids[p] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int p = c_lo + lane + 64 * u;
+            if (p < c_hi) {
+                const bool ok = (unsigned)idv[u] < (unsigned)E;
+                s_ids[p] = ok ? (short)idv[u] : (short)-1;
+                if (ok)
+                    atomicAdd(&s_wcnt[wave][idv[u]], 1);
+                else
+                    ++my_drop;
+            }
+        }
+    } else {
+        for (int p = c_lo + lane; p < c_hi; p += 64) {
+            const int id = a.ids[p];
+            if ((unsigned)id < (unsigned)E)
+                atomicAdd(&s_wcnt[wave][id], 1);
+            else
+                ++my_drop;
+        }
     }
     if (my_drop) atomicAdd(&s_dropped, my_drop);
     __syncthreads();
