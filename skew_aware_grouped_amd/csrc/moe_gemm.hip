@@ -501,11 +501,10 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a
 // blocks: waves 0, 1, 4, 5 take the first, the others the second).  The
 // stage loads come from the four waves of wave row 0, one per SIMD.  Output:
 // y[p] = bf16(acc * routing weight of the row), for the task's rows with a
-// source assignment p (padding rows store nothing).
+// source assignment p (padding rows store nothing), stored from registers.
 namespace g2w {
-constexpr int kBRows = 256;  // output columns per task = W2 rows per stage
-constexpr int kOutRow = 2 * kBRows;  // bytes of one staged output row (bf16)
-static_assert(kOutRow * 16 * kMaxRowBlocksFp8G1 <= G1F8::kRing, "output staging must fit in the ring");
+constexpr int kBRows = 256;          // output columns per task = W2 rows per stage
+constexpr int kOutRow = 2 * kBRows;  // bytes of one task's part of an output row (bf16)
 }  // namespace g2w
 
 template <int NW, int NA>
@@ -635,7 +634,6 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
     const int claim_at = nk > kClaimLead ? nk - kClaimLead : 0;
     const int settle_at = nk > kClaimLead - 2 ? nk - (kClaimLead - 2) : 0;
     const int rows_at = nk > kClaimLead - 4 ? nk - (kClaimLead - 4) : 0;
-    unsigned char* stage = smem;  // [kRows][kOutRow]
 
     auto body = [&](auto nw_c) {
         constexpr int NW = decltype(nw_c)::value;
@@ -662,36 +660,31 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
         }
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
 
-        // ---- epilogue: routing weight, bf16, staged rows, 16-byte stores.
-        // Row block i of this lane: tile row 32 i + 16 wm + lr, columns
-        // 64 wn + 16 f + 4 lg + j (four consecutive bf16 = 8 bytes)
-        lds_barrier();
+        // ---- epilogue: routing weight, bf16, stored from registers.  Row
+        // block i of this lane: tile row 32 i + 16 wm + lr, columns
+        // 64 wn + 16 f + 4 lg + j (four consecutive bf16 = 8 bytes), so a
+        // row's 64 columns of this wave go out as four 32-byte pieces, which
+        // the L2 merges into whole lines; no staging pass, no barrier before
+        // the stores.  Padding rows (no source assignment) store nothing.
         const int row_l = 16 * wm + lr;
-        unsigned char* stage_l = stage + row_l * g2w::kOutRow + 2 * (64 * wn + 4 * lg);
+        unsigned char* ycol = static_cast<unsigned char*>(g.y) + (int64_t)cb * g2w::kOutRow + 2 * (64 * wn + 4 * lg);
+        const int64_t yrow_bytes = (int64_t)N_out * 2;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const float wt = roww[row_l + 32 * i];  // 0 on padding rows
+            const int p = rows[row_l + 32 * i];
+            const float wt = roww[row_l + 32 * i];
+            if (p >= 0) {
+                unsigned char* dst = ycol + (int64_t)p * yrow_bytes;
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const unsigned lo = pk_bf16(acc[i][f][0] * wt, acc[i][f][1] * wt);
-                const unsigned hi = pk_bf16(acc[i][f][2] * wt, acc[i][f][3] * wt);
-                *reinterpret_cast<uint2*>(stage_l + 32 * i * g2w::kOutRow + 2 * 16 * f) = make_uint2(lo, hi);
+                for (int f = 0; f < 4; ++f) {
+                    const unsigned lo = pk_bf16(acc[i][f][0] * wt, acc[i][f][1] * wt);
+                    const unsigned hi = pk_bf16(acc[i][f][2] * wt, acc[i][f][3] * wt);
+                    *reinterpret_cast<uint2*>(dst + 2 * 16 * f) = make_uint2(lo, hi);
+                }
             }
         }
-        lds_barrier();
-        constexpr int kChunks = g2w::kOutRow / 16;
-        unsigned char* y = static_cast<unsigned char*>(g.y);
-        const int64_t yrow_bytes = (int64_t)N_out * 2;
-        if (w != C::kSched)
-            for (int i = threadIdx.x; i < kRows * kChunks; i += C::kStoreThreads) {
-                const int r = i / kChunks, c = i - r * kChunks;
-                const int p = rows[r];
-                if (p < 0) continue;
-                *reinterpret_cast<v4i*>(y + (int64_t)p * yrow_bytes + (int64_t)cb * g2w::kOutRow + c * 16) =
-                    *reinterpret_cast<const v4i*>(stage + r * g2w::kOutRow + c * 16);
-            }
         if (w == C::kSched) sch.publish();
-        lds_barrier();  // the ring and the staging area are refilled by the next task
+        lds_barrier();  // the ring is refilled by the next task
     };
     if (wm == 0)
         body(std::integral_constant<int, G1F8Rows<NSUB, 0>::n>{});
