@@ -50,9 +50,12 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
     const int64_t mtile_cap1 = L->tile_cap / kSmallRowBlocks + (E < N ? E : N);
     const int64_t mtile_cap2 = mtile_cap1;
     L->block_n1 = gemm1_block_n(d->mode);
-    L->block_n2 = gemm2_block_n(
-        d->mode, fp8_wide2(d->mode, d->launch, d->num_tokens, d->top_k, d->num_experts, d->d_hidden, d->d_expert));
-    L->max_row_blocks = gemm1_max_row_blocks(d->mode, d->num_tokens, d->top_k, d->d_hidden, d->d_expert);
+    const bool wide2 =
+        fp8_wide2(d->mode, d->launch, d->num_tokens, d->top_k, d->num_experts, d->d_hidden, d->d_expert);
+    L->block_n2 = gemm2_block_n(d->mode, wide2);
+    // the largest task of either list, in group blocks
+    L->max_row_blocks = std::max(gemm1_max_row_blocks(d->mode, d->num_tokens, d->top_k, d->d_hidden, d->d_expert),
+                                 gemm2_row_blocks(d->mode, wide2));
     L->task1_cap = mtile_cap1 * (d->d_expert / L->block_n1);
     L->task2_cap = mtile_cap2 * (d->d_hidden / L->block_n2);
     const size_t hb = mode_fp8(d->mode) ? 1 : 2;

@@ -32,13 +32,14 @@ constexpr int kMaxRowBlocks = kMaxRowBlocks1;
 constexpr int kMaxRowBlocksFp8G1 = 16;
 constexpr int kGemm1Fp8Waves = 8;
 constexpr int kGemm1Fp8Threads = 64 * kGemm1Fp8Waves;
-// It serves batches of at least kFp8WideMinAssignments routed rows (an
-// average of 256 rows per expert at 32 experts); smaller FP8 batches stream
-// weights and take the 4-wave kernel, whose stage loads and epilogue are
-// shorter per task.
+// It serves batches of at least kFp8WideMinAssignments routed rows (64 rows
+// per expert on average at 32 experts; measured: at 2048 assignments of the
+// DeepSeek shapes it is 13% faster than the 4-wave kernel, at 1024 3%
+// slower); smaller FP8 batches take the 4-wave kernel, whose stage loads and
+// epilogue are shorter per task.
 // The 8-wave kernel addresses x, one expert's W1 and the scales with 32-bit
 // offsets from uniform bases, so it also needs T*d_h and 2*d_e*d_h below 2^31.
-constexpr int64_t kFp8WideMinAssignments = 8192;
+constexpr int64_t kFp8WideMinAssignments = 2048;
 inline bool fp8_wide(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
     return mode == MOE_MODE_FP8 && T * k >= kFp8WideMinAssignments && T * d_h < ((int64_t)1 << 31) &&
            2 * d_e * d_h < ((int64_t)1 << 31);
@@ -46,14 +47,16 @@ inline bool fp8_wide(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
 inline int gemm1_max_row_blocks(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
     return fp8_wide(mode, T, k, d_h, d_e) ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
 }
-// FP8 GEMM-2 at the same batches (four launches only: the single launch keeps
-// its own task shapes) runs an 8-wave kernel on the same geometry: tasks of
-// up to 16 group blocks by 256 output columns, so it also needs d_h a
-// multiple of 256 and n_pad*d_e below 2^31 (32-bit offsets into h).
+// FP8 GEMM-2 from kFp8Wide2MinAssignments routed rows on (four launches
+// only: the single launch keeps its own task shapes) runs an 8-wave kernel on
+// the same geometry: tasks of up to 16 group blocks by 256 output columns, so
+// it needs d_h a multiple of 256 and n_pad*d_e below 2^31 (32-bit offsets
+// into h).  Measured at 1024 DeepSeek-shaped assignments: 97 -> 86 us.
+constexpr int64_t kFp8Wide2MinAssignments = 1024;
 inline bool fp8_wide2(int mode, int launch, int64_t T, int64_t k, int64_t E, int64_t d_h, int64_t d_e) {
     const int64_t n_pad = T * k + (E < T * k ? E : T * k) * (kBlockM - 1);
-    return launch == MOE_LAUNCH_MULTI && fp8_wide(mode, T, k, d_h, d_e) && d_h % 256 == 0 &&
-           n_pad * d_e < ((int64_t)1 << 31);
+    return mode == MOE_MODE_FP8 && launch == MOE_LAUNCH_MULTI && T * k >= kFp8Wide2MinAssignments &&
+           d_h % 256 == 0 && n_pad * d_e < ((int64_t)1 << 31);
 }
 constexpr int kMaxRowBlocksFp8G2 = 16;
 // Workgroup of the GEMM kernels: 4 wave64s, one per SIMD.

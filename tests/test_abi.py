@@ -44,16 +44,21 @@ def test_workspace_layout_is_disjoint_and_aligned():
 
 
 def test_gemm_task_shapes_follow_batch_and_launch():
-    """Column blocks and M-tile limit in the layout: FP8 batches of at least
-    8192 assignments take the 8-wave GEMMs (16-block M-tiles; GEMM-2 with
-    256-column tasks when d_h is a multiple of 256 and the layer runs as four
-    launches), everything else 128-column GEMM-2 tasks."""
+    """Column blocks and the largest task in the layout: FP8 batches of at
+    least 2048 assignments take the 8-wave GEMM-1 (16-block M-tiles), of at
+    least 1024 the 8-wave GEMM-2 (256-column tasks, when d_h is a multiple of
+    256 and the layer runs as four launches); everything else 8-block tasks
+    and 128-column GEMM-2 blocks."""
     big = dict(mode=moe.MOE_MODE_FP8, T=8192, E=32, k=2, d_h=7168, d_e=2048)
     L = moe.moe_workspace_layout(_dims(**big))
     assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 256, 16)
     L = moe.moe_workspace_layout(_dims(**dict(big, d_h=7296)))  # 57 * 128: GEMM-2 keeps 128 columns
     assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 128, 16)
-    L = moe.moe_workspace_layout(_dims(**dict(big, T=4095)))  # 8190 assignments: 4-wave GEMMs
+    L = moe.moe_workspace_layout(_dims(**dict(big, T=1024)))  # 2048 assignments: both 8-wave
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 256, 16)
+    L = moe.moe_workspace_layout(_dims(**dict(big, T=600)))  # 1200: the 8-wave GEMM-2 only
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 256, 16)
+    L = moe.moe_workspace_layout(_dims(**dict(big, T=511)))  # 1022: both 4-wave
     assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 128, 8)
     L = moe.moe_workspace_layout(_dims(**dict(big, mode=moe.MOE_MODE_MXFP8)))
     assert L.block_n2 == 128
