@@ -343,9 +343,13 @@ def main():
     # dominant kernel: GEMM-1 (gate|up + SwiGLU), two thirds of the weights and
     # FLOPs; in the single launch, the one kernel and the whole layer's work
     kj = 0 if single else 1
-    # the FP8 GEMM-1 of large batches is its own 8-wave kernel (the library's fp8_wide rule)
-    wide = (w.mode == W.MODE_FP8 and w.T * w.k >= 8192 and w.T * w.d_h < 2 ** 31 and 2 * w.d_e * w.d_h < 2 ** 31)
-    kname = "layer_kernel" if single else ("gemm1_fp8_kernel" if wide else "gemm1_kernel")
+    # the FP8 (MXFP8) GEMM-1 of batches from 2048 (4096) assignments is an
+    # 8-wave kernel of its own (the library's fp8_wide rule)
+    min_n = 4096 if w.mode == W.MODE_MXFP8 else 2048
+    wide = (w.mode in (W.MODE_FP8, W.MODE_MXFP8) and w.T * w.k >= min_n and w.T * w.d_h < 2 ** 31
+            and 2 * w.d_e * w.d_h < 2 ** 31)
+    wide_name = "gemm1_fp8_kernel" if w.mode == W.MODE_FP8 else "gemm1_mxfp8_kernel"
+    kname = "layer_kernel" if single else (wide_name if wide else "gemm1_kernel")
     k_us = float(np.mean(stage_ms[:, kj])) * 1e3
     g1_bytes = alg_bytes if single else gemm1_alg_bytes(w)
     g1_flops = flops if single else 4.0 * w.d_h * w.d_e * w.valid_assignments()

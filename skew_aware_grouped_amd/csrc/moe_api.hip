@@ -97,12 +97,12 @@ void layout_of(const moe_dims* d, moe_ws_layout* L) {
 }
 
 // Per-device cache of the chip size and of the GEMM kernels' occupancy.
-// Slot 4 holds the 8-wave FP8 GEMM-1 and GEMM-2 (fp8_wide, fp8_wide2).
+// Slots 4 and 5 hold the 8-wave FP8 and MXFP8 GEMM-1 and GEMM-2 (fp8_wide, fp8_wide2).
 struct DeviceInfo {
     bool ready = false;
     int cus = 0;
-    int occ1[5] = {0, 0, 0, 0, 0};
-    int occ2[5] = {0, 0, 0, 0, 0};
+    int occ1[6] = {0, 0, 0, 0, 0, 0};
+    int occ2[6] = {0, 0, 0, 0, 0, 0};
     int occ_layer[4] = {0, 0, 0, 0};  // single-launch kernel, by mode (BF16, FP8, MXFP8)
 };
 std::mutex g_mu;
@@ -119,8 +119,8 @@ hipError_t device_info(int mode, bool wide, bool wide2, int* cus, int* occ1, int
     if (!di.ready) {
         err = hipDeviceGetAttribute(&di.cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        for (int m = 0; m < 5; ++m) {
-            err = gemm_occupancy(m < 4 ? m : MOE_MODE_FP8, m == 4, &di.occ1[m], &di.occ2[m]);
+        for (int m = 0; m < 6; ++m) {
+            err = gemm_occupancy(m < 4 ? m : m == 4 ? MOE_MODE_FP8 : MOE_MODE_MXFP8, m >= 4, &di.occ1[m], &di.occ2[m]);
             if (err != hipSuccess) return err;
             if (di.occ1[m] < 1) di.occ1[m] = 1;
             if (di.occ2[m] < 1) di.occ2[m] = 1;
@@ -134,8 +134,9 @@ hipError_t device_info(int mode, bool wide, bool wide2, int* cus, int* occ1, int
     }
     *cus = di.cus;
     if (occ_layer) *occ_layer = di.occ_layer[mode_fp8(mode) ? mode : MOE_MODE_BF16];
-    *occ1 = di.occ1[wide ? 4 : gemm_mode(mode)];
-    *occ2 = di.occ2[wide2 ? 4 : gemm_mode(mode)];
+    const int wide_slot = mode == MOE_MODE_MXFP8 ? 5 : 4;
+    *occ1 = di.occ1[wide ? wide_slot : gemm_mode(mode)];
+    *occ2 = di.occ2[wide2 ? wide_slot : gemm_mode(mode)];
     return hipSuccess;
 }
 
@@ -345,7 +346,7 @@ static int forward_impl(const moe_dims* dims, const void* x, const int32_t* topk
     r.min_tasks1 = cus * occ1;
     r.mb1_max = wide ? kMaxRowBlocksFp8G1 : kMaxRowBlocks1;
     r.mb2 = gemm2_row_blocks(mode, wide2);
-    r.mix1 = mode != MOE_MODE_FP8;
+    r.mix1 = mode != MOE_MODE_FP8 && !wide;
     // GEMM-2's tasks are short: 128-row tiles only when every workgroup slot
     // still gets two tasks (Qwen shapes at 1024 tokens stay at 64-row tiles);
     // the 8-wave FP8 kernel's 256-row tiles when every slot gets one

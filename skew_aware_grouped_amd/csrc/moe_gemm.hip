@@ -138,15 +138,24 @@ struct G1F8 {
     // row scales of up to 256 rows (4 B each), then the gate and up block scales
     static constexpr int kScaleBlk = 4 * kMaxRows;
     static constexpr int kStageS = kScaleBlk + 16;
-    static constexpr int stage_bytes(int nsub) { return kStageB + 16 * nsub * kRowBytes + kStageS; }
+    // MXFP8: the K block's four E8M0 bytes of each A row (one 4-byte word per
+    // row, in the positions of the FP8 row scales), then of each B row (row r
+    // at word kScaleBlk / 4 + r)
+    static constexpr int kStageSMx = kScaleBlk + 4 * kBRows;
+    static constexpr int stage_bytes(int nsub, bool mx = false) {
+        return kStageB + 16 * nsub * kRowBytes + (mx ? kStageSMx : kStageS);
+    }
     static constexpr int kRing = 160 * 1024 - 5 * 1024;
-    static constexpr int stages(int nsub) { return kRing / stage_bytes(nsub) < 8 ? kRing / stage_bytes(nsub) : 8; }
+    static constexpr int stages(int nsub, bool mx = false) {
+        return kRing / stage_bytes(nsub, mx) < 8 ? kRing / stage_bytes(nsub, mx) : 8;
+    }
     static constexpr int kEpiRow = kBN;  // one e4m3 byte per column
 };
 static_assert(G1F8::kEpiRow * G1F8::kMaxRows + 4 * G1F8::kMaxRows * 4 <= G1F8::kRing,
               "epilogue staging must fit in the ring");
-static_assert(G1F8::stages(kMaxRowBlocksFp8G1) >= 2, "ring too small");
-static_assert(G1F8::stage_bytes(1) % 16 == 0, "stages 16-byte aligned");
+static_assert(G1F8::stages(kMaxRowBlocksFp8G1) >= 2 && G1F8::stages(kMaxRowBlocksFp8G1, true) >= 2,
+              "ring too small");
+static_assert(G1F8::stage_bytes(1) % 16 == 0 && G1F8::stage_bytes(1, true) % 16 == 0, "stages 16-byte aligned");
 
 // Row blocks of the task that wave row wm computes: wm, wm + 2, ...
 template <int NSUB, int WM>
@@ -207,12 +216,57 @@ __device__ __forceinline__ void g1f8_kblock(const unsigned char* st, int nsub_ro
     }
 }
 
-template <int NSUB>
+// The same K block in MXFP8: the MFMA applies the E8M0 scales and
+// accumulates straight into acc (no promotion).  Lane (lr, lg) supplies the
+// scale byte of its fragment row for K values [32 lg, 32 lg + 32): byte lg of
+// that row's 4-byte word.  With the weight fragment as the first operand, its
+// scale is the first scale operand and the token row's the second.
+template <int NW, int NA>
+__device__ __forceinline__ void g1mx_kblock(const unsigned char* st, int nsub_rows_bytes, int wm, int wn, int lr,
+                                            int lg, int swz, v4f (&acc)[NA][2][2]) {
+    if constexpr (NW > 0) {
+        const unsigned char* sb = st;
+        const unsigned char* sa = st + G1F8::kStageB;
+        const unsigned* sc = reinterpret_cast<const unsigned*>(st + G1F8::kStageB + nsub_rows_bytes);
+        const unsigned* scb = sc + G1F8::kScaleBlk / 4;
+        const unsigned sh = 8u * (unsigned)lg;
+        v8i Bf[2][2];
+        int sbw[2][2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const int brow = 16 * (2 * wn + f) + lr;
+            Bf[f][0] = lds_frag32(sb + brow * kRowBytes, lg, swz);
+            Bf[f][1] = lds_frag32(sb + (G1F8::kBN + brow) * kRowBytes, lg, swz);
+            sbw[f][0] = (int)((scb[brow] >> sh) & 0xffu);
+            sbw[f][1] = (int)((scb[G1F8::kBN + brow] >> sh) & 0xffu);
+        }
+        const uint4 s0 = *reinterpret_cast<const uint4*>(sc + 16 * lr + 8 * wm);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(sc + 16 * lr + 8 * wm + 4);
+        const unsigned sxr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        v8i A = lds_frag32(sa + (16 * wm + lr) * kRowBytes, lg, swz);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int sa_i = (int)((sxr[i] >> sh) & 0xffu);
+            v8i An = A;
+            if (i + 1 < NW) An = lds_frag32(sa + (16 * (2 * (i + 1) + wm) + lr) * kRowBytes, lg, swz);
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int gu = 0; gu < 2; ++gu) acc[i][f][gu] = mfma_mx(Bf[f][gu], A, acc[i][f][gu], sbw[f][gu], sa_i);
+            A = An;
+        }
+    }
+}
+
+// MX: MXFP8 operands (E8M0 scales per 32 values of K, applied by the MFMA,
+// and the intermediate requantised per row per 32 columns); otherwise FP8
+// with 128x128 block scales promoted in registers.
+template <int NSUB, bool MX>
 __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, int cb, unsigned char* smem,
                                           SchedT<kRowsLdsFp8G1>& sch, const int* rows, int par) {
     using C = G1F8;
-    constexpr int S = C::stages(NSUB);
-    constexpr int kStage = C::stage_bytes(NSUB);
+    constexpr int S = C::stages(NSUB, MX);
+    constexpr int kStage = C::stage_bytes(NSUB, MX);
     constexpr int kStageA = 16 * NSUB * kRowBytes;
     constexpr int kAInstr = 2 * NSUB;  // A loads per stage: 8 rows each
     constexpr int kRows = 16 * NSUB;
@@ -224,17 +278,19 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
     const int nk = K / 128;
     const unsigned smem_lds = lds_offset(smem);
     const int64_t ld_bytes = K;  // bytes per operand row
-    const float* a_scale = static_cast<const float*>(g.x_scale);
-    const float* w_scale = static_cast<const float*>(g.w1_scale);
+    // row scales of x: fp32 per row per 128 (FP8) or four E8M0 bytes per row
+    // per 128 (MXFP8): the same 4 bytes per row and K block, at the same offsets
+    const void* a_scale = g.x_scale;
     const bool loader = w < C::kLoaders;
     // vector-memory loads per stage of this wave: B instructions w, w+4, ...,
-    // A instructions the same way, row-scale chunk c by wave c, the block
-    // scales by wave 1
+    // A instructions the same way, row-scale chunk c by wave c, and the weight
+    // scales: FP8 the two block scales by wave 1, MXFP8 the scale words of
+    // B rows 64 w .. 64 w + 63 by each loading wave
     const int n_b = loader ? (C::kBAll - 1 - w) / C::kLoaders + 1 : 0;
     const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / C::kLoaders + 1 : 0;
     const int my_chunk = w < C::kLoaders ? w : -1;  // row-scale chunk of this wave, or -1
     const bool s_rows = my_chunk >= 0;  // all four chunks: the positions are permuted
-    const int n_s = (s_rows ? 1 : 0) + (w == 1 ? 1 : 0);
+    const int n_s = (s_rows ? 1 : 0) + (MX ? (loader ? 1 : 0) : (w == 1 ? 1 : 0));
     const int loads_per_stage = n_b + n_a + n_s;
 
     // Addresses: uniform bases (the task's weight tile or expert, x, the
@@ -292,7 +348,18 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
         soff = (unsigned)(p >= 0 ? p / g.k : 0) * (unsigned)(4 * kq);
     }
     unsigned bsoff = 0;
-    if (w == 1 && lane < 2) {
+    const unsigned char* w_scale = static_cast<const unsigned char*>(g.w1_scale);
+    if constexpr (MX) {
+        // W1 scale bytes [E][2 d_e][d_h/32]: the expert's base, and for lane
+        // l of loading wave w tile row r = 64 w + l (gate rows cb*128 + r,
+        // then up rows d_e + cb*128 + r - 128)
+        w_scale += (int64_t)e * 2 * N_out * (K / 32);
+        if (loader) {
+            const int r = 64 * w + lane;
+            const int wrow = r < C::kBN ? cb * C::kBN + r : N_out + cb * C::kBN + (r - C::kBN);
+            bsoff = (unsigned)wrow * (unsigned)(K / 32);
+        }
+    } else if (w == 1 && lane < 2) {
         // W1 scales [E][2 d_e/128][d_h/128]: gate block row cb, up block row d_e/128 + cb
         const int nrb = 2 * N_out / kQ;
         const int brow = lane == 0 ? cb : N_out / kQ + cb;
@@ -326,8 +393,10 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
         }
         const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
         if (s_rows) g2l4s(a_scale, soff + 4u * (unsigned)kc, ss + (unsigned)(256 * my_chunk));
-        // lanes 0 and 1 only: the other lanes would land past the stage
-        if (w == 1 && lane < 2) g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)C::kScaleBlk);
+        if constexpr (MX)
+            g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)(C::kScaleBlk + 256 * w));
+        else if (w == 1 && lane < 2)  // lanes 0 and 1 only: the other lanes would land past the stage
+            g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)C::kScaleBlk);
     };
 
     const int swz = lr & 7;
@@ -364,12 +433,16 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
                 if (kc == settle_at) sch.settle(true);
                 if (kc == rows_at) sch.load_rows(par ^ 1);
             }
-            g1f8_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
+            if constexpr (MX)
+                g1mx_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
+            else
+                g1f8_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
         }
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
 
         // ---- epilogue: SwiGLU, amax per row over the task's 128 columns
-        // (four waves hold 32 columns each), requantisation, staging, stores
+        // (FP8: four waves hold 32 columns each) or over each wave's 32
+        // (MXFP8), requantisation, staging, stores
         lds_barrier();
         if (w_owner) g.row_w[row0 + w_row] = ep_w;
         float hv[NA][2][4];
@@ -387,44 +460,85 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
         // plus a compile-time offset, so the loops keep no per-row addresses
         // in registers.
         const int row_l = 16 * wm + lr;
-        float* amax_w = s_amax + wn * C::kMaxRows + row_l;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            float m = 0.f;
-#pragma unroll
-            for (int f = 0; f < 2; ++f)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(hv[i][f][j]));
-            // the four lane groups hold the row's other columns of this wave
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            if (lg == 0) amax_w[32 * i] = m;
-        }
-        lds_barrier();
-        const int nq = N_out / kQ;
-        float* hs_l = static_cast<float*>(g.h_scale) + (int64_t)(row0 + row_l) * nq + cb;
-        const float* amax_r = s_amax + row_l;
         unsigned* stage_l = reinterpret_cast<unsigned*>(stage + row_l * C::kEpiRow + 32 * wn + 4 * lg);
-        float sc_keep[NA];  // row scales, stored after the loop (no store waits inside it)
+        if constexpr (MX) {
+            // per row per 32 columns: this wave's 32 columns of a row are one
+            // MX block, spread over the row's four lane groups.  Shared
+            // exponent floor(log2 amax) - 8 (the e4m3 maximum is 1.75 * 2^8),
+            // stored biased by 127 and clamped to [0, 254], 127 for an
+            // all-zero block; elements v * 2^-exponent saturated to +-448,
+            // rounded to e4m3
+            int hb[NA];
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            float am = amax_r[32 * i];
+            for (int i = 0; i < NW; ++i) {
+                float m = 0.f;
 #pragma unroll
-            for (int ww = 1; ww < 4; ++ww) am = fmaxf(am, amax_r[ww * C::kMaxRows + 32 * i]);
-            // scale amax/448; values are multiplied by its reciprocal
-            sc_keep[i] = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
-            const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
+                for (int f = 0; f < 2; ++f)
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                // four e4m3 codes, columns 4 lg .. 4 lg + 3 in byte order
-                int word = __builtin_amdgcn_cvt_pk_fp8_f32(hv[i][f][0] * inv, hv[i][f][1] * inv, 0, false);
-                word = __builtin_amdgcn_cvt_pk_fp8_f32(hv[i][f][2] * inv, hv[i][f][3] * inv, word, true);
-                stage_l[(32 * i * C::kEpiRow + 16 * f) / 4] = (unsigned)word;
+                    for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(hv[i][f][j]));
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                // frexp: m = f * 2^x with f in [0.5, 1), so floor(log2 m) = x - 1
+                int b = m > 0.f ? __builtin_amdgcn_frexp_expf(m) - 1 - 8 + 127 : 127;
+                b = b < 0 ? 0 : (b > 254 ? 254 : b);
+                hb[i] = b;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        v[j] = fminf(fmaxf(__builtin_amdgcn_ldexpf(hv[i][f][j], 127 - b), -448.0f), 448.0f);
+                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+                    word = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], word, true);
+                    stage_l[(32 * i * C::kEpiRow + 16 * f) / 4] = (unsigned)word;
+                }
             }
-        }
-        if (wn == 0 && lg == 0)
+            // h_scale bytes [n_pad][d_e/32]: byte cb*4 + wn of each of the lane's rows
+            if (lg == 0) {
+                uint8_t* hs_l =
+                    static_cast<uint8_t*>(g.h_scale) + (int64_t)(row0 + row_l) * (N_out / 32) + cb * 4 + wn;
 #pragma unroll
-            for (int i = 0; i < NW; ++i) hs_l[(int64_t)(32 * i) * nq] = sc_keep[i];
+                for (int i = 0; i < NW; ++i) hs_l[(int64_t)(32 * i) * (N_out / 32)] = (uint8_t)hb[i];
+            }
+        } else {
+            float* amax_w = s_amax + wn * C::kMaxRows + row_l;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                float m = 0.f;
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) m = fmaxf(m, fabsf(hv[i][f][j]));
+                // the four lane groups hold the row's other columns of this wave
+                m = fmaxf(m, __shfl_xor(m, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                if (lg == 0) amax_w[32 * i] = m;
+            }
+            lds_barrier();
+            const int nq = N_out / kQ;
+            float* hs_l = static_cast<float*>(g.h_scale) + (int64_t)(row0 + row_l) * nq + cb;
+            const float* amax_r = s_amax + row_l;
+            float sc_keep[NA];  // row scales, stored after the loop (no store waits inside it)
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                float am = amax_r[32 * i];
+#pragma unroll
+                for (int ww = 1; ww < 4; ++ww) am = fmaxf(am, amax_r[ww * C::kMaxRows + 32 * i]);
+                // scale amax/448; values are multiplied by its reciprocal
+                sc_keep[i] = am > 0.f ? am * (1.0f / 448.0f) : 1.0f;
+                const float inv = am > 0.f ? 448.0f * __builtin_amdgcn_rcpf(am) : 1.0f;
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    // four e4m3 codes, columns 4 lg .. 4 lg + 3 in byte order
+                    int word = __builtin_amdgcn_cvt_pk_fp8_f32(hv[i][f][0] * inv, hv[i][f][1] * inv, 0, false);
+                    word = __builtin_amdgcn_cvt_pk_fp8_f32(hv[i][f][2] * inv, hv[i][f][3] * inv, word, true);
+                    stage_l[(32 * i * C::kEpiRow + 16 * f) / 4] = (unsigned)word;
+                }
+            }
+            if (wn == 0 && lg == 0)
+#pragma unroll
+                for (int i = 0; i < NW; ++i) hs_l[(int64_t)(32 * i) * nq] = sc_keep[i];
+        }
         lds_barrier();
         // h[row0 + r][cb*128 ...]: 128 bytes per row
         constexpr int kChunks = C::kEpiRow / 16;
@@ -444,9 +558,10 @@ __device__ __forceinline__ void g1f8_task(const Gemm1Args& g, int e, int row0, i
         body(std::integral_constant<int, G1F8Rows<NSUB, 1>::n>{});
 }
 
-__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
-    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+// The persistent 8-wave GEMM-1: scheduler set-up, then tasks until the
+// queues are empty.
+template <bool MX>
+__device__ __forceinline__ void gemm1_wide(const Gemm1Args& a, unsigned char* smem, QueueLdsT<kRowsLdsFp8G1>& q) {
     const int xcd = my_xcd();
     if (threadIdx.x <= kXcds) q.seg[threadIdx.x] = a.ctl[kCtlSeg1 + threadIdx.x];
     if (threadIdx.x == 0) q.mask = 0;
@@ -467,7 +582,7 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a
         const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
         const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
         SchedT<kRowsLdsFp8G1> sch{a.ctl, kCtlQueue1, a.tasks, a.row_src, nullptr, &q, xcd};
-#define MOE_G1F8(NS) g1f8_task<NS>(a, e, row0, cb, smem, sch, q.rows[par], par)
+#define MOE_G1F8(NS) g1f8_task<NS, MX>(a, e, row0, cb, smem, sch, q.rows[par], par)
         switch (nsub) {
             case 1: MOE_G1F8(1); break;
             case 2: MOE_G1F8(2); break;
@@ -488,6 +603,18 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a
         }
 #undef MOE_G1F8
     }
+}
+
+__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_fp8_kernel(Gemm1Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
+    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+    gemm1_wide<false>(a, smem, q);
+}
+
+__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_mxfp8_kernel(Gemm1Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
+    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+    gemm1_wide<true>(a, smem, q);
 }
 
 // ------------------------------------------------------- FP8 GEMM-2 (8 waves)
@@ -542,12 +669,49 @@ __device__ __forceinline__ void g2f8_kblock(const unsigned char* st, int nsub_ro
     }
 }
 
-template <int NSUB>
+// MXFP8 form of the K block: scales applied by the MFMA (as in g1mx_kblock);
+// the weight fragments' scale words are those of W2 rows 64 wn + 16 f + lr.
+template <int NW, int NA>
+__device__ __forceinline__ void g2mx_kblock(const unsigned char* st, int nsub_rows_bytes, int wm, int wn, int lr,
+                                            int lg, int swz, v4f (&acc)[NA][4]) {
+    if constexpr (NW > 0) {
+        const unsigned char* sb = st;
+        const unsigned char* sa = st + G1F8::kStageB;
+        const unsigned* sc = reinterpret_cast<const unsigned*>(st + G1F8::kStageB + nsub_rows_bytes);
+        const unsigned* scb = sc + G1F8::kScaleBlk / 4;
+        const unsigned sh = 8u * (unsigned)lg;
+        v8i Bf[4];
+        int sbw[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int brow = 64 * wn + 16 * f + lr;
+            Bf[f] = lds_frag32(sb + brow * kRowBytes, lg, swz);
+            sbw[f] = (int)((scb[brow] >> sh) & 0xffu);
+        }
+        const uint4 s0 = *reinterpret_cast<const uint4*>(sc + 16 * lr + 8 * wm);
+        const uint4 s1 = *reinterpret_cast<const uint4*>(sc + 16 * lr + 8 * wm + 4);
+        const unsigned sxr[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        v8i A = lds_frag32(sa + (16 * wm + lr) * kRowBytes, lg, swz);
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int sa_i = (int)((sxr[i] >> sh) & 0xffu);
+            v8i An = A;
+            if (i + 1 < NW) An = lds_frag32(sa + (16 * (2 * (i + 1) + wm) + lr) * kRowBytes, lg, swz);
+#pragma unroll
+            for (int f = 0; f < 4; ++f) acc[i][f] = mfma_mx(Bf[f], A, acc[i][f], sbw[f], sa_i);
+            A = An;
+        }
+    }
+}
+
+// MX: MXFP8 operands (h and W2 with E8M0 scales per 32 values of K);
+// otherwise FP8 with per-row-per-128 h scales and 128x128 W2 block scales.
+template <int NSUB, bool MX>
 __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, int cb, unsigned char* smem,
                                           SchedT<kRowsLdsFp8G1>& sch, const int* rows, const float* roww, int par) {
     using C = G1F8;
-    constexpr int S = C::stages(NSUB);
-    constexpr int kStage = C::stage_bytes(NSUB);
+    constexpr int S = C::stages(NSUB, MX);
+    constexpr int kStage = C::stage_bytes(NSUB, MX);
     constexpr int kStageA = 16 * NSUB * kRowBytes;
     constexpr int kAInstr = 2 * NSUB;  // A loads per stage: 8 rows each
     constexpr int kRows = 16 * NSUB;
@@ -565,10 +729,11 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
     const int64_t ld_bytes = K;  // bytes per operand row (h and W2 rows)
     const bool loader = w < kLoaders;
     // loads per stage of a loading wave: B and A instructions w, w+4, ...,
-    // one 64-position chunk of row scales, and in wave 1 the two block scales
+    // one 64-position chunk of row scales, and the weight scales: FP8 the two
+    // block scales in wave 1, MXFP8 the scale words of W2 rows 64 w .. 64 w + 63
     const int n_b = loader ? (kBAll - 1 - w) / kLoaders + 1 : 0;
     const int n_a = loader && w < kAInstr ? (kAInstr - 1 - w) / kLoaders + 1 : 0;
-    const int n_s = (loader ? 1 : 0) + (w == 1 ? 1 : 0);
+    const int n_s = (loader ? 1 : 0) + (MX ? (loader ? 1 : 0) : (w == 1 ? 1 : 0));
     const int loads_per_stage = n_b + n_a + n_s;
 
     // Addresses: a uniform part per instruction (scalar arithmetic) plus one
@@ -590,8 +755,10 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
     };
     const unsigned b_step = g.packed ? 16384u : (unsigned)kRowBytes;
     const unsigned char* hbase = static_cast<const unsigned char*>(g.h) + (int64_t)row0 * ld_bytes;
-    const float* h_scale = static_cast<const float*>(g.h_scale);
-    const float* w_scale = static_cast<const float*>(g.w2_scale);
+    // h row scales: fp32 per row per 128 (FP8) or four E8M0 bytes per row per
+    // 128 (MXFP8), the same 4 bytes per row and K block at the same offsets
+    const void* h_scale = g.h_scale;
+    const unsigned char* w_scale = static_cast<const unsigned char*>(g.w2_scale);
     // row scales: stage position p = 64 w + lane holds the scale of tile row
     // 16 (2 (p & 7) + ((p >> 3) & 1)) + (p >> 4), where g2f8_kblock reads it
     // (row 0's past the task's rows); wave 1 lanes 0 and 1: the two W2 block
@@ -604,7 +771,14 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
         soff = (unsigned)(row0 + (srow < kRows ? srow : 0)) * (unsigned)(4 * kq);
     }
     unsigned bsoff = 0;
-    if (w == 1 && lane < 2) bsoff = (unsigned)(((int64_t)e * (N_out / kQ) + 2 * cb + lane) * kq) * 4u;
+    if constexpr (MX) {
+        // W2 scale bytes [E][d_h][d_e/32]: the expert's base, and for lane l
+        // of loading wave w the task's W2 row 64 w + l
+        w_scale += (int64_t)e * N_out * (K / 32);
+        if (loader) bsoff = (unsigned)(cb * g2w::kBRows + 64 * w + lane) * (unsigned)(K / 32);
+    } else if (w == 1 && lane < 2) {
+        bsoff = (unsigned)(((int64_t)e * (N_out / kQ) + 2 * cb + lane) * kq) * 4u;
+    }
 
     auto issue = [&](int kc) {
         const unsigned st = smem_lds + (unsigned)((kc % S) * kStage);
@@ -624,8 +798,10 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
         }
         const unsigned ss = st + (unsigned)(C::kStageB + kStageA);
         g2l4s(h_scale, soff + 4u * (unsigned)kc, ss + (unsigned)(256 * w));
-        // lanes 0 and 1 only: the other lanes would land past the stage
-        if (w == 1 && lane < 2) g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)C::kScaleBlk);
+        if constexpr (MX)
+            g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)(C::kScaleBlk + 256 * w));
+        else if (w == 1 && lane < 2)  // lanes 0 and 1 only: the other lanes would land past the stage
+            g2l4s(w_scale, bsoff + 4u * (unsigned)kc, ss + (unsigned)C::kScaleBlk);
     };
 
     const int swz = lr & 7;
@@ -656,7 +832,10 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
                 if (kc == settle_at) sch.settle(true);
                 if (kc == rows_at) sch.load_rows(par ^ 1);
             }
-            g2f8_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
+            if constexpr (MX)
+                g2mx_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
+            else
+                g2f8_kblock<NW>(smem + (kc % S) * kStage, kStageA, wm, wn, lr, lg, swz, acc);
         }
         __builtin_amdgcn_s_waitcnt(VmCnt<0>::imm);
 
@@ -692,9 +871,8 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
         body(std::integral_constant<int, G1F8Rows<NSUB, 1>::n>{});
 }
 
-__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm2_fp8_kernel(Gemm2Args a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
-    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+template <bool MX>
+__device__ __forceinline__ void gemm2_wide(const Gemm2Args& a, unsigned char* smem, QueueLdsT<kRowsLdsFp8G1>& q) {
     const int xcd = my_xcd();
     if (threadIdx.x <= kXcds) q.seg[threadIdx.x] = a.ctl[kCtlSeg2 + threadIdx.x];
     if (threadIdx.x == 0) q.mask = 0;
@@ -707,12 +885,12 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm2_fp8_kernel(Gemm2Args a
     }
     lds_barrier();
     for (int par = 0;; par ^= 1) {
-        const int t = __builtin_amdgcn_readfirstlane(q.slot);  // uniform, as in gemm1_fp8_kernel
+        const int t = __builtin_amdgcn_readfirstlane(q.slot);  // uniform, as in gemm1_wide
         if (t < 0) break;
         const int e = __builtin_amdgcn_readfirstlane(q.task.x), row0 = __builtin_amdgcn_readfirstlane(q.task.y);
         const int nsub = __builtin_amdgcn_readfirstlane(q.task.z), cb = __builtin_amdgcn_readfirstlane(q.task.w);
         SchedT<kRowsLdsFp8G1> sch{a.ctl, kCtlQueue2, a.tasks, a.row_src, a.row_w, &q, xcd};
-#define MOE_G2F8(NS) g2f8_task<NS>(a, e, row0, cb, smem, sch, q.rows[par], q.roww[par], par)
+#define MOE_G2F8(NS) g2f8_task<NS, MX>(a, e, row0, cb, smem, sch, q.rows[par], q.roww[par], par)
         switch (nsub) {
             case 1: MOE_G2F8(1); break;
             case 2: MOE_G2F8(2); break;
@@ -733,6 +911,18 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm2_fp8_kernel(Gemm2Args a
         }
 #undef MOE_G2F8
     }
+}
+
+__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm2_fp8_kernel(Gemm2Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
+    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+    gemm2_wide<false>(a, smem, q);
+}
+
+__global__ __launch_bounds__(kGemm1Fp8Threads) void gemm2_mxfp8_kernel(Gemm2Args a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[G1F8::kRing];
+    __shared__ QueueLdsT<kRowsLdsFp8G1> q;
+    gemm2_wide<true>(a, smem, q);
 }
 
 // ---------------------------------------------------------------- combine
@@ -887,7 +1077,9 @@ hipError_t launch_x_to_bf16(const float* x, uint16_t* xb, int64_t n, hipStream_t
 
 hipError_t launch_gemm1(int mode, bool wide, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0,
                         hipEvent_t t1) {
-    if (mode == MOE_MODE_MXFP8)
+    if (mode == MOE_MODE_MXFP8 && wide)
+        hipExtLaunchKernelGGL(gemm1_mxfp8_kernel, dim3(grid), dim3(kGemm1Fp8Threads), 0, s, t0, t1, 0, a);
+    else if (mode == MOE_MODE_MXFP8)
         hipExtLaunchKernelGGL(gemm1_kernel<MOE_MODE_MXFP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_FP8 && wide)
         hipExtLaunchKernelGGL(gemm1_fp8_kernel, dim3(grid), dim3(kGemm1Fp8Threads), 0, s, t0, t1, 0, a);
@@ -902,6 +1094,8 @@ hipError_t launch_gemm2(int mode, bool wide, const Gemm2Args& a, int grid, hipSt
                         hipEvent_t t1) {
     if (mode == MOE_MODE_FP8 && wide)
         hipExtLaunchKernelGGL(gemm2_fp8_kernel, dim3(grid), dim3(kGemm1Fp8Threads), 0, s, t0, t1, 0, a);
+    else if (mode == MOE_MODE_MXFP8 && wide)
+        hipExtLaunchKernelGGL(gemm2_mxfp8_kernel, dim3(grid), dim3(kGemm1Fp8Threads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_MXFP8)
         hipExtLaunchKernelGGL(gemm2_kernel<MOE_MODE_MXFP8>, dim3(grid), dim3(kGemmThreads), 0, s, t0, t1, 0, a);
     else if (mode == MOE_MODE_FP8)
@@ -927,8 +1121,10 @@ hipError_t launch_combine(int mode, const CombineArgs& a, hipStream_t s, hipEven
 hipError_t gemm_occupancy(int mode, bool wide, int* g1, int* g2) {
     hipError_t e1, e2;
     if (mode == MOE_MODE_MXFP8) {
-        e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
-        e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
+        e1 = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_mxfp8_kernel, kGemm1Fp8Threads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
+        e2 = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_mxfp8_kernel, kGemm1Fp8Threads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(g2, gemm2_kernel<MOE_MODE_MXFP8>, kGemmThreads, 0);
     } else if (mode == MOE_MODE_FP8) {
         e1 = wide ? hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_fp8_kernel, kGemm1Fp8Threads, 0)
                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(g1, gemm1_kernel<MOE_MODE_FP8>, kGemmThreads, 0);

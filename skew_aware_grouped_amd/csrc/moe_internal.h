@@ -40,8 +40,14 @@ constexpr int kGemm1Fp8Threads = 64 * kGemm1Fp8Waves;
 // The 8-wave kernel addresses x, one expert's W1 and the scales with 32-bit
 // offsets from uniform bases, so it also needs T*d_h and 2*d_e*d_h below 2^31.
 constexpr int64_t kFp8WideMinAssignments = 2048;
+// MXFP8 runs the same kernels with its scale bytes (four loads of scale words
+// per stage more) from kMxWideMinAssignments (measured at 2048 assignments
+// of the Qwen shapes: 41 us against the 4-wave kernel's 35; at 8192 tokens of
+// the DeepSeek shapes 491 against 680).
+constexpr int64_t kMxWideMinAssignments = 4096;
 inline bool fp8_wide(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
-    return mode == MOE_MODE_FP8 && T * k >= kFp8WideMinAssignments && T * d_h < ((int64_t)1 << 31) &&
+    const int64_t min_n = mode == MOE_MODE_MXFP8 ? kMxWideMinAssignments : kFp8WideMinAssignments;
+    return (mode == MOE_MODE_FP8 || mode == MOE_MODE_MXFP8) && T * k >= min_n && T * d_h < ((int64_t)1 << 31) &&
            2 * d_e * d_h < ((int64_t)1 << 31);
 }
 inline int gemm1_max_row_blocks(int mode, int64_t T, int64_t k, int64_t d_h, int64_t d_e) {
@@ -52,10 +58,14 @@ inline int gemm1_max_row_blocks(int mode, int64_t T, int64_t k, int64_t d_h, int
 // the same geometry: tasks of up to 16 group blocks by 256 output columns, so
 // it needs d_h a multiple of 256 and n_pad*d_e below 2^31 (32-bit offsets
 // into h).  Measured at 1024 DeepSeek-shaped assignments: 97 -> 86 us.
+// MXFP8 takes it only with d_e of at least 1024 (K blocks enough to carry a
+// 256x256 task's fixed costs; measured at 2048 assignments: DeepSeek shapes,
+// d_e = 2048, 134 -> 114 us; Qwen shapes, d_e = 768, 21.5 -> 24 us).
 constexpr int64_t kFp8Wide2MinAssignments = 1024;
 inline bool fp8_wide2(int mode, int launch, int64_t T, int64_t k, int64_t E, int64_t d_h, int64_t d_e) {
     const int64_t n_pad = T * k + (E < T * k ? E : T * k) * (kBlockM - 1);
-    return mode == MOE_MODE_FP8 && launch == MOE_LAUNCH_MULTI && T * k >= kFp8Wide2MinAssignments &&
+    return (mode == MOE_MODE_FP8 || (mode == MOE_MODE_MXFP8 && d_e >= 1024)) && launch == MOE_LAUNCH_MULTI &&
+           T * k >= kFp8Wide2MinAssignments &&
            d_h % 256 == 0 && n_pad * d_e < ((int64_t)1 << 31);
 }
 constexpr int kMaxRowBlocksFp8G2 = 16;
@@ -220,7 +230,7 @@ hipError_t launch_i8_to_bf16(const int8_t* x, uint16_t* xb, int64_t n, hipStream
 // output columns (gated: gate and up rows of a column block together)
 hipError_t launch_pack(const void* w, void* wp, int64_t E, int64_t n_out, int64_t k_bytes, int bn, bool gated,
                        hipStream_t s);
-// wide: FP8 only, the 8-wave kernel (fp8_wide)
+// wide: FP8 and MXFP8 only, the 8-wave kernels (fp8_wide, fp8_wide2)
 hipError_t launch_gemm1(int mode, bool wide, const Gemm1Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
                         hipEvent_t t1 = nullptr);
 hipError_t launch_gemm2(int mode, bool wide, const Gemm2Args& a, int grid, hipStream_t s, hipEvent_t t0 = nullptr,
@@ -254,7 +264,7 @@ hipError_t layer_occupancy(int mode, int* blocks_per_cu);
 hipError_t launch_sync_clear(int32_t* sync, hipStream_t s);
 
 // Resident workgroups per CU of the persistent GEMM kernels (occupancy query;
-// wide: the 8-wave FP8 GEMM-1).
+// wide: the 8-wave FP8 or MXFP8 GEMM-1 and GEMM-2).
 hipError_t gemm_occupancy(int mode, bool wide, int* g1_blocks_per_cu, int* g2_blocks_per_cu);
 
 }  // namespace moe

@@ -45,10 +45,11 @@ def test_workspace_layout_is_disjoint_and_aligned():
 
 def test_gemm_task_shapes_follow_batch_and_launch():
     """Column blocks and the largest task in the layout: FP8 batches of at
-    least 2048 assignments take the 8-wave GEMM-1 (16-block M-tiles), of at
-    least 1024 the 8-wave GEMM-2 (256-column tasks, when d_h is a multiple of
-    256 and the layer runs as four launches); everything else 8-block tasks
-    and 128-column GEMM-2 blocks."""
+    least 2048 assignments (MXFP8: 4096) take the 8-wave GEMM-1 (16-block
+    M-tiles), of at least 1024 the 8-wave GEMM-2 (256-column tasks, when d_h
+    is a multiple of 256, the layer runs as four launches and, in MXFP8,
+    d_e >= 1024); everything else 8-block tasks and 128-column GEMM-2
+    blocks."""
     big = dict(mode=moe.MOE_MODE_FP8, T=8192, E=32, k=2, d_h=7168, d_e=2048)
     L = moe.moe_workspace_layout(_dims(**big))
     assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 256, 16)
@@ -61,7 +62,14 @@ def test_gemm_task_shapes_follow_batch_and_launch():
     L = moe.moe_workspace_layout(_dims(**dict(big, T=511)))  # 1022: both 4-wave
     assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 128, 8)
     L = moe.moe_workspace_layout(_dims(**dict(big, mode=moe.MOE_MODE_MXFP8)))
-    assert L.block_n2 == 128
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 256, 16)
+    L = moe.moe_workspace_layout(_dims(**dict(big, T=511, mode=moe.MOE_MODE_MXFP8)))
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (128, 128, 8)
+    mx = dict(big, mode=moe.MOE_MODE_MXFP8)
+    assert moe.moe_workspace_layout(_dims(**dict(mx, T=1024))).block_n2 == 256  # 2048: GEMM-2 only
+    assert moe.moe_workspace_layout(_dims(**dict(mx, T=1024, d_h=2048, d_e=768))).block_n2 == 128  # short K
+    L = moe.moe_workspace_layout(_dims(**dict(big, mode=moe.MOE_MODE_BF16)))  # 64-column bf16 GEMM-1 tasks
+    assert (L.block_n1, L.block_n2, L.max_row_blocks) == (64, 128, 8)
     L = moe.moe_workspace_layout(_dims(**dict(big, T=1024, launch=moe.MOE_LAUNCH_SINGLE)))
     assert L.block_n2 == 128
 

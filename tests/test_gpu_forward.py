@@ -159,11 +159,15 @@ def test_large_batch_routing_path(oracle, mode):
     _check(w, oracle, label="large_batch")
 
 
-def test_fp8_wide_gemm1_with_narrow_gemm2(oracle):
-    """8400 assignments take the 8-wave FP8 GEMM-1; d_h = 384 is not a
-    multiple of 256, so GEMM-2 keeps the 4-wave kernel and 128-column tasks
-    (its grid then comes from that kernel's occupancy).  Every row compared."""
-    w = W.custom(4200, 16, 2, 384, 256, W.MODE_FP8, seed=45, routing=("zipf", 1.1, 2))
+@pytest.mark.parametrize("mode", FP8_MODES)
+def test_fp8_wide_gemm1_with_narrow_gemm2(oracle, mode):
+    """8400 assignments take the 8-wave FP8 (MXFP8) GEMM-1; d_h = 384 is not
+    a multiple of 256, so GEMM-2 keeps the 4-wave kernel and 128-column tasks
+    (its grid then comes from that kernel's occupancy).  Every row compared.
+    MXFP8 at d_e = 1024: at d_e = 256 its worst row is 3.1% off, the same
+    bit for bit from the 4-wave kernels (rounding flips of the intermediate,
+    as in test_large_batch_routing_path)."""
+    w = W.custom(4200, 16, 2, 384, 256 if mode == W.MODE_FP8 else 1024, mode, seed=45, routing=("zipf", 1.1, 2))
     _check(w, oracle, label="wide1_narrow2")
 
 
@@ -290,15 +294,17 @@ def test_packed_weights_bitwise_equal_row_major(name):
                        b.view(torch.int16) if b.dtype != torch.float32 else b.view(torch.int32))
 
 
+@pytest.mark.parametrize("T,d_e", [(150, 256), (2100, 1024)])
 @pytest.mark.parametrize("packed", [False, True])
-def test_mxfp8_scales_vary_across_k(oracle, packed):
+def test_mxfp8_scales_vary_across_k(oracle, packed, T, d_e):
     """MXFP8 with scale bytes that differ by up to 2^7 between neighbouring
     32-value blocks of K, for x, W1 and W2 alike (still valid MX inputs): the
     output is right only if every 32-value slice of K meets its own scale in
     both operands.  Shifts are kept small enough that no product under- or
-    overflows fp32."""
+    overflows fp32.  300 assignments run the 4-wave GEMMs, 4200 the 8-wave
+    ones (whose stages carry the scale words of 256 weight rows)."""
     import dataclasses
-    w = W.custom(150, 6, 2, 512, 256, W.MODE_MXFP8, seed=31, routing=("zipf", 1.1, 2))
+    w = W.custom(T, 6, 2, 512, d_e, W.MODE_MXFP8, seed=31, routing=("zipf", 1.1, 2))
     rng = np.random.default_rng(4)
 
     def shifted(sc, lo, hi):
