@@ -841,25 +841,41 @@ __device__ __forceinline__ void g2f8_task(const Gemm2Args& g, int e, int row0, i
 
         // ---- epilogue: routing weight, bf16, stored from registers.  Row
         // block i of this lane: tile row 32 i + 16 wm + lr, columns
-        // 64 wn + 16 f + 4 lg + j (four consecutive bf16 = 8 bytes), so a
-        // row's 64 columns of this wave go out as four 32-byte pieces, which
-        // the L2 merges into whole lines; no staging pass, no barrier before
-        // the stores.  Padding rows (no source assignment) store nothing.
+        // 64 wn + 16 f + 4 lg + j (four consecutive bf16 = 8 bytes); no
+        // staging pass, no barrier before the stores.  Padding rows (no
+        // source assignment) store nothing.
+        // Fragments 2q and 2q + 1 (32 columns) go out as one 16-byte store
+        // per lane: lane groups lg and lg ^ 1 trade halves (one lane shuffle
+        // per word), so an even group holds 8 consecutive columns of fragment
+        // 2q, an odd group 8 of fragment 2q + 1, and the four groups of a row
+        // cover its 32 columns (64 bytes) in one instruction: half the store
+        // requests of 8-byte pieces.
         const int row_l = 16 * wm + lr;
-        unsigned char* ycol = static_cast<unsigned char*>(g.y) + (int64_t)cb * g2w::kOutRow + 2 * (64 * wn + 4 * lg);
+        const bool odd = lg & 1;
+        const int col0 = 64 * wn + (odd ? 16 + 4 * (lg - 1) : 4 * lg);
+        unsigned char* ycol = static_cast<unsigned char*>(g.y) + (int64_t)cb * g2w::kOutRow + 2 * col0;
         const int64_t yrow_bytes = (int64_t)N_out * 2;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
             const int p = rows[row_l + 32 * i];
             const float wt = roww[row_l + 32 * i];
+            uint4 v[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const unsigned a0 = pk_bf16(acc[i][2 * q][0] * wt, acc[i][2 * q][1] * wt);
+                const unsigned a1 = pk_bf16(acc[i][2 * q][2] * wt, acc[i][2 * q][3] * wt);
+                const unsigned b0 = pk_bf16(acc[i][2 * q + 1][0] * wt, acc[i][2 * q + 1][1] * wt);
+                const unsigned b1 = pk_bf16(acc[i][2 * q + 1][2] * wt, acc[i][2 * q + 1][3] * wt);
+                // an even group sends its fragment 2q + 1 words, an odd one its 2q words
+                const unsigned r0 = __shfl_xor(odd ? a0 : b0, 16);
+                const unsigned r1 = __shfl_xor(odd ? a1 : b1, 16);
+                v[q] = odd ? make_uint4(r0, r1, b0, b1) : make_uint4(a0, a1, r0, r1);
+            }
+            // the partner group holds the same row, so both take this branch alike
             if (p >= 0) {
                 unsigned char* dst = ycol + (int64_t)p * yrow_bytes;
-#pragma unroll
-                for (int f = 0; f < 4; ++f) {
-                    const unsigned lo = pk_bf16(acc[i][f][0] * wt, acc[i][f][1] * wt);
-                    const unsigned hi = pk_bf16(acc[i][f][2] * wt, acc[i][f][3] * wt);
-                    *reinterpret_cast<uint2*>(dst + 2 * 16 * f) = make_uint2(lo, hi);
-                }
+                *reinterpret_cast<uint4*>(dst) = v[0];
+                *reinterpret_cast<uint4*>(dst + 64) = v[1];
             }
         }
         if (w == C::kSched) sch.publish();
