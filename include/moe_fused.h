@@ -376,9 +376,11 @@ MOE_API int moe_route(int32_t num_tokens, int32_t top_k, int32_t num_experts, co
  * (each such call's output is not valid; 0 unless the grid could not make
  * progress), and no call resets it.  y holds fp32 rows with MOE_LAUNCH_SINGLE.
  * block_n1 / block_n2: output columns of a GEMM-1 / GEMM-2 task (GEMM-2 takes
- * 256 in FP8 mode from 1024 assignments on, with four launches and d_h a
- * multiple of 256, else 128); max_row_blocks: the largest task of either list,
- * in 16-row group blocks.
+ * 256 from 1024 assignments on in FP8 mode, and in MXFP8 mode with d_e of at
+ * least 1024, with four launches and d_h a multiple of 256; else 128);
+ * max_row_blocks: the largest task of either list, in 16-row group blocks (16
+ * where an 8-wave GEMM runs: GEMM-1 from 2048 assignments in FP8 mode, 4096 in
+ * MXFP8 mode, or the 256-column GEMM-2; else 8).
  * Returns MOE_ERR_INVALID_ARG for invalid dims. */
 typedef struct {
     size_t counts, offsets, padded_offsets, pos, sorted_p, ppos, row_src, row_w, tile_expert, tile_row0, stats;
