@@ -121,6 +121,15 @@ def test_clamped_activation_small_shapes(oracle, mode, packed):
     _check(w, oracle, label="clamped", packed=packed)
 
 
+@pytest.mark.parametrize("mode", FP8_MODES)
+def test_clamped_activation_wide_kernels(oracle, mode):
+    """The clamped activation (x scaled by 4) at 4200 assignments, where both
+    FP8 modes run the 8-wave GEMM-1 and GEMM-2; every row compared."""
+    w = W.custom(2100, 6, 2, 512, 1024, mode, seed=47, routing=("zipf", 1.1, 1),
+                 activation=W.ACT_SWIGLU_CLAMPED, x_gain=4.0)
+    _check(w, oracle, label="clamped_wide", packed=True)
+
+
 @pytest.mark.parametrize("name", ["qwen_bf16", "ds_fp8_1024", "ds_mxfp8_1024"])
 def test_clamped_activation_sampled(oracle, name):
     import dataclasses
