@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
     }
 }
 
-// ------------------------------------------------------- FP8 GEMM-1 (8 waves)
+// ---------------------------------------------- FP8 / MXFP8 GEMM-1 (8 waves)
 // Block-scaled FP8 GEMM-1 with SwiGLU and the per-row-per-128 requantisation
 // of h, for tasks of up to 16 group blocks (256 rows) by 128 output columns
 // (256 weight rows: 128 gate, 128 up).  Eight waves, two per SIMD: wave
@@ -122,6 +122,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm2_kernel(Gemm2Args a) {
 // loads waits while the CU's address unit works through them (about 1 KB
 // per 16 cycles), and on each SIMD the other wave's MFMAs run meanwhile.  The
 // last wave is the scheduler (as in gemm_task) and computes.
+//
+// The MXFP8 form (gemm1_mxfp8_kernel, the same task code with MX set) keeps
+// the geometry: its stages also carry the E8M0 scale words of the 256 weight
+// rows, the scaled MFMA accumulates in place (no promotion), and h is
+// requantised per row per 32 columns, one MX block per wave.
 struct G1F8 {
     static constexpr int kWaves = kGemm1Fp8Waves;
     static constexpr int kSched = kWaves - 1;
@@ -617,7 +622,7 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_mxfp8_kernel(Gemm1Args
     gemm1_wide<true>(a, smem, q);
 }
 
-// ------------------------------------------------------- FP8 GEMM-2 (8 waves)
+// ---------------------------------------------- FP8 / MXFP8 GEMM-2 (8 waves)
 // Block-scaled FP8 GEMM-2 for tasks of up to 16 group blocks (256 rows of h)
 // by 256 output columns, on the geometry of the 8-wave GEMM-1: a stage holds
 // 256 rows of W2 (32 KB), the task's h rows and their row scales; wave
@@ -629,6 +634,8 @@ __global__ __launch_bounds__(kGemm1Fp8Threads) void gemm1_mxfp8_kernel(Gemm1Args
 // stage loads come from the four waves of wave row 0, one per SIMD.  Output:
 // y[p] = bf16(acc * routing weight of the row), for the task's rows with a
 // source assignment p (padding rows store nothing), stored from registers.
+// The MXFP8 form (gemm2_mxfp8_kernel) carries the scale words of the 256 W2
+// rows in each stage and accumulates through the scaled MFMA.
 namespace g2w {
 constexpr int kBRows = 256;          // output columns per task = W2 rows per stage
 constexpr int kOutRow = 2 * kBRows;  // bytes of one task's part of an output row (bf16)
