@@ -207,6 +207,69 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         // order); the first lane of each expert group advances it
         if (valid && wrank == 0) s_wcnt[wave][id] += __popcll(m);
     }
+    // Ranking and M-tile sizes of the task lists (step 5 below) need only the
+    // counts, so they run before the scatter barrier: waves with no scatter
+    // work (most of them at small N) rank while the others scatter, and the
+    // scatter barrier also publishes s_order, s_rtiles, s_mb1 and s_mb2.
+    if (a.nb1 > 0) {
+        // 5. task lists.  Experts are ranked by descending row count (ties by id):
+        // longest work first.  An expert's tasks are its M-tiles (up to
+        // kMaxRowBlocks1 / kMaxRowBlocks2 group blocks) times the column blocks.  The task group
+        // (rank r, column block cb) -- every M-tile of one weight block -- goes to
+        // XCD (r*nb + cb) mod 8, so the M-tiles that read the same weights run
+        // side by side on one L2; each XCD's segment of the list keeps rank order.
+        {
+            // lane l of every wave holds the counts of experts l, l + 64, ...;
+            // wave w ranks experts w, w + 16, ...: the number of experts ranked
+            // before e is a popcount of ballots over the lanes, with no LDS
+            // round trip per comparison
+            constexpr int kJ = kMaxExperts / 64;
+            int cj[kJ];
+#pragma unroll
+            for (int j = 0; j < kJ; ++j) cj[j] = lane + 64 * j < E ? s_cnt[lane + 64 * j] : -1;
+            for (int e = wave; e < E; e += kRouteWaves) {
+                const int je = e >> 6;  // wave-uniform
+                int c = 0;
+#pragma unroll
+                for (int j = 0; j < kJ; ++j)
+                    if (j == je) c = __builtin_amdgcn_readlane(cj[j], e & 63);
+                int r = 0;
+#pragma unroll
+                for (int j = 0; j < kJ; ++j) {
+                    if (64 * j >= E) break;
+                    const int e2 = lane + 64 * j;
+                    const bool before = e2 < E && ((cj[j] > c) || (cj[j] == c && e2 < e));
+                    r += __popcll(__ballot(before));
+                }
+                if (lane == 0) {
+                    s_order[r] = e;
+                    s_rtiles[r] = s_tiles[e];
+                }
+            }
+        }
+        // M-tiles of 8 group blocks (fewer weight re-reads) when that still leaves
+        // min_tasks1 (min_tasks2) tasks, otherwise kSmallRowBlocks (more tasks to
+        // spread over the CUs); the 8-wave FP8 GEMMs (mb1_max 16, mb2 16) take
+        // 16-block M-tiles when those still leave min_tasks1 (min_tasks2) tasks.
+        // The last wave decides for both lists after its share of the ranking
+        if (wave == kRouteWaves - 1) {
+            int big = 0, big16 = 0;
+            for (int e = lane; e < E; e += 64) {
+                big += (s_tiles[e] + 7) >> 3;
+                big16 += (s_tiles[e] + 15) >> 4;
+            }
+            big = __builtin_amdgcn_readlane(wave_inclusive_scan(big, lane), 63);
+            big16 = __builtin_amdgcn_readlane(wave_inclusive_scan(big16, lane), 63);
+            if (lane == 0) {
+                s_mb1 = a.mb1_max == 16 && big16 * a.nb1 >= a.min_tasks1 ? 16
+                        : big * a.nb1 >= a.min_tasks1                   ? kMaxRowBlocks1
+                                                                        : kSmallRowBlocks;
+                s_mb2 = a.mb2 == 16 && big16 * a.nb2 >= a.min_tasks2  ? 16
+                        : a.mb2 >= 8 && big * a.nb2 >= a.min_tasks2 ? 8
+                                                                     : kSmallRowBlocks;
+            }
+        }
+    }
     __syncthreads();
 
     if (stage_rows)  // row_src out of LDS, coalesced
@@ -233,64 +296,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     }
     if (a.nb1 <= 0) return;
 
-    // 5. task lists.  Experts are ranked by descending row count (ties by id):
-    // longest work first.  An expert's tasks are its M-tiles (up to
-    // kMaxRowBlocks1 / kMaxRowBlocks2 group blocks) times the column blocks.  The task group
-    // (rank r, column block cb) -- every M-tile of one weight block -- goes to
-    // XCD (r*nb + cb) mod 8, so the M-tiles that read the same weights run
-    // side by side on one L2; each XCD's segment of the list keeps rank order.
-    {
-        // lane l of every wave holds the counts of experts l, l + 64, ...;
-        // wave w ranks experts w, w + 16, ...: the number of experts ranked
-        // before e is a popcount of ballots over the lanes, with no LDS
-        // round trip per comparison
-        constexpr int kJ = kMaxExperts / 64;
-        int cj[kJ];
-#pragma unroll
-        for (int j = 0; j < kJ; ++j) cj[j] = lane + 64 * j < E ? s_cnt[lane + 64 * j] : -1;
-        for (int e = wave; e < E; e += kRouteWaves) {
-            const int je = e >> 6;  // wave-uniform
-            int c = 0;
-#pragma unroll
-            for (int j = 0; j < kJ; ++j)
-                if (j == je) c = __builtin_amdgcn_readlane(cj[j], e & 63);
-            int r = 0;
-#pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                if (64 * j >= E) break;
-                const int e2 = lane + 64 * j;
-                const bool before = e2 < E && ((cj[j] > c) || (cj[j] == c && e2 < e));
-                r += __popcll(__ballot(before));
-            }
-            if (lane == 0) {
-                s_order[r] = e;
-                s_rtiles[r] = s_tiles[e];
-            }
-        }
-    }
-    // M-tiles of 8 group blocks (fewer weight re-reads) when that still leaves
-    // min_tasks1 (min_tasks2) tasks, otherwise kSmallRowBlocks (more tasks to
-    // spread over the CUs); the 8-wave FP8 GEMMs (mb1_max 16, mb2 16) take
-    // 16-block M-tiles when those still leave min_tasks1 (min_tasks2) tasks.
-    // The last wave decides for both lists after its share of the ranking
-    if (wave == kRouteWaves - 1) {
-        int big = 0, big16 = 0;
-        for (int e = lane; e < E; e += 64) {
-            big += (s_tiles[e] + 7) >> 3;
-            big16 += (s_tiles[e] + 15) >> 4;
-        }
-        big = __builtin_amdgcn_readlane(wave_inclusive_scan(big, lane), 63);
-        big16 = __builtin_amdgcn_readlane(wave_inclusive_scan(big16, lane), 63);
-        if (lane == 0) {
-            s_mb1 = a.mb1_max == 16 && big16 * a.nb1 >= a.min_tasks1 ? 16
-                    : big * a.nb1 >= a.min_tasks1                   ? kMaxRowBlocks1
-                                                                    : kSmallRowBlocks;
-            s_mb2 = a.mb2 == 16 && big16 * a.nb2 >= a.min_tasks2  ? 16
-                    : a.mb2 >= 8 && big * a.nb2 >= a.min_tasks2 ? 8
-                                                                 : kSmallRowBlocks;
-        }
-    }
-    __syncthreads();
     const int mb1 = s_mb1, mb2 = s_mb2;
     // M-tiles of the expert of rank r in list 0 (GEMM-1) or 1 (GEMM-2); the
     // M-tile sizes are powers of two
