@@ -7,9 +7,14 @@
 // the expert of each group block).  Here it is produced on the device so that
 // no host round trip of the routing is needed.
 //
-// One workgroup of 16 wave64s does everything: N = T*k is at most a few ten
-// thousand assignments on the paths this serves.  Each wave owns a contiguous
-// chunk of the assignments.  Up to kLdsIds ids are read from HBM once, into
+// One workgroup of 16 wave64s does everything up to kRouteMultiMin
+// assignments.  Each wave owns a contiguous chunk of the assignments.  From
+// kRouteMultiMin on, 1 + 16 workgroups run: every one counts the
+// whole batch per chunk (the same numbers everywhere, no communication between
+// workgroups), workgroup 0 writes the counts and offsets and builds the task
+// lists, and workgroup 1 + c scatters chunk c with its 16 waves (sub-chunk
+// counts, then the same ballot ranking), so the scatter -- bound by one
+// workgroup's VALU issue -- runs on 16 CUs.  Up to kLdsIds ids are read from HBM once, into
 // LDS, and the scatter reads them there and builds row_src in LDS, which then
 // goes out with coalesced stores; larger N reads the ids twice and scatters
 // row_src straight to memory.
@@ -25,6 +30,9 @@ constexpr int kLdsRows = kLdsIds + kMaxExperts * (kBlockM - 1);
 // M-tiles per list that the rank-lookup table (kept in the ids' LDS once the
 // scatter is done) can hold
 constexpr int kRankTable = kLdsIds / 2;
+// From this many assignments the routing runs on 1 + kRouteWaves workgroups
+// (workgroup 1 + c scatters chunk c); below, one workgroup does everything.
+constexpr int kRouteMultiMin = 4096;
 
 // Largest e in [0,n) with off[e] <= r, for a non-decreasing off[0..n]
 // and r < off[n].  Empty entries (off[e] == off[e+1]) are never returned.
@@ -69,14 +77,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int wave = tid >> 6;
     const int E = a.E;
     const int N = a.N;
+    const int g = blockIdx.x;
+    const bool multi = gridDim.x > 1;  // N >= kRouteMultiMin (launch_route)
     const bool in_lds = N <= kLdsIds;
     // row_src is built in LDS when the ids are there and the scatter is large
     // enough for its scattered stores to cost more than the extra pass
-    const bool stage_rows = in_lds && N > kRouteThreads;
+    const bool stage_rows = in_lds && N > kRouteThreads && !multi;
+    // multi: the sub-chunk counts of the workgroup's chunk, [kRouteWaves][E],
+    // in s_rows (not staged in that mode)
+    int* s_sub = s_rows;
 
     for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wcnt[i / E][i % E] = 0;
+    if (multi)
+        for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_sub[i] = 0;
     if (tid == 0) s_dropped = 0;
-    if (a.zero)
+    if (a.zero && g == 0)
         for (int i = tid; i < kZeroBytes / 4; i += kRouteThreads) reinterpret_cast<int*>(a.zero)[i] = 0;
     __syncthreads();
 
@@ -147,23 +162,90 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __syncthreads();
     const int n_valid = s_off[E];
     const int n_pad = s_poff[E];
-    for (int e = tid; e < E; e += kRouteThreads) a.counts[e] = s_cnt[e];
-    for (int e = tid; e <= E; e += kRouteThreads) {
-        a.offsets[e] = s_off[e];
-        a.padded_offsets[e] = s_poff[e];
+    if (g == 0) {
+        for (int e = tid; e < E; e += kRouteThreads) a.counts[e] = s_cnt[e];
+        for (int e = tid; e <= E; e += kRouteThreads) {
+            a.offsets[e] = s_off[e];
+            a.padded_offsets[e] = s_poff[e];
+        }
     }
     // padding rows of each group (in LDS: every row, the scatter then fills
     // the valid ones) and the unused tail of the padded space
     if (stage_rows) {
         for (int i = tid; i < n_pad; i += kRouteThreads) s_rows[i] = -1;
         __syncthreads();
-    } else {
+    } else if (g == 0) {
         for (int e = wave; e < E; e += kRouteWaves)
             for (int r = s_poff[e] + s_cnt[e] + lane; r < s_poff[e + 1]; r += 64) a.row_src[r] = -1;
     }
-    for (int64_t i = n_pad + tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
-    if (a.full)
-        for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
+    if (g == 0) {
+        for (int64_t i = n_pad + tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
+        if (a.full)
+            for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
+    }
+
+    if (multi && g > 0) {
+        // 3'. workgroup 1 + c scatters chunk c (workgroup 0 skips the scatter
+        // and goes on to the task lists): wave v takes the v-th sub-chunk,
+        // counts it, and ranks within it as the single-workgroup scatter
+        // below does within a chunk.  The rank of p: chunk base (earlier
+        // chunks' counts, s_wcnt[c]) + earlier sub-chunks' counts + the
+        // running count within the sub-chunk.
+        {
+            const int c = g - 1;
+            const int q_lo = c * chunk, q_hi = min(N, q_lo + chunk);
+            const int sub = ((chunk + kRouteWaves - 1) / kRouteWaves + 63) / 64 * 64;
+            const int s_lo = q_lo + wave * sub;
+            const int s_hi = min(q_hi, s_lo + sub);
+            for (int p = s_lo + lane; p < s_hi; p += 64) {
+                const int id = in_lds ? s_ids[p] : a.ids[p];
+                if ((unsigned)id < (unsigned)E) atomicAdd(&s_sub[wave * E + id], 1);
+            }
+            __syncthreads();
+            for (int e = tid; e < E; e += kRouteThreads) {
+                int run = 0;
+                for (int v = 0; v < kRouteWaves; ++v) {
+                    const int n = s_sub[v * E + e];
+                    s_sub[v * E + e] = run;
+                    run += n;
+                }
+            }
+            __syncthreads();
+            const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            const int kb = 32 - __clz(E);
+            for (int base = s_lo; base < s_hi; base += 64) {
+                const int p = base + lane;
+                const int id = p < s_hi ? (in_lds ? s_ids[p] : a.ids[p]) : -1;
+                const bool valid = (unsigned)id < (unsigned)E;
+                const int key = valid ? id : E;
+                uint64_t m = ~0ull;
+#pragma unroll
+                for (int b = 0; b < 9; ++b) {
+                    if (b >= kb) break;
+                    const bool bit = (key >> b) & 1;
+                    const uint64_t bal = __ballot(bit);
+                    m &= bit ? bal : ~bal;
+                }
+                const int wrank = __popcll(m & lt);
+                if (valid) {
+                    const int r = s_wcnt[c][id] + s_sub[wave * E + id] + wrank;
+                    if (a.full) {
+                        a.pos[p] = s_off[id] + r;
+                        a.ppos[p] = s_poff[id] + r;
+                        a.sorted_p[s_off[id] + r] = p;
+                    }
+                    a.row_src[s_poff[id] + r] = p;
+                } else if (p < s_hi && a.full) {
+                    a.pos[p] = -1;
+                    a.ppos[p] = -1;
+                }
+                // every lane has read its base above; the first lane of each
+                // expert group advances it
+                if (valid && wrank == 0) s_sub[wave * E + id] += __popcll(m);
+            }
+        }
+        return;
+    }
 
     // 3. stable scatter: each wave walks its chunk 64 assignments at a time.
     // Lanes with the same expert find each other with one ballot per bit of
@@ -171,10 +253,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     // at most 9); the rank of an assignment is its wave's running base for
     // that expert plus the number of lower lanes with the same expert.  The
     // lowest such lane then advances the base.  No workgroup barrier: the
-    // bases of a wave are its own.
+    // bases of a wave are its own.  (Single workgroup only: with several,
+    // workgroup 0 has no scatter.)
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int key_bits = 32 - __clz(E);
-    for (int base = c_lo; base < c_lo + chunk; base += 64) {
+    for (int base = c_lo; !multi && base < c_lo + chunk; base += 64) {
         const int p = base + lane;
         const int id = p < c_hi ? (in_lds ? s_ids[p] : a.ids[p]) : -1;
         const bool valid = (unsigned)id < (unsigned)E;
@@ -415,7 +498,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    hipExtLaunchKernelGGL(route_kernel, dim3(1), dim3(kRouteThreads), 0, s, t0, t1, 0, a);
+    const unsigned grid = a.N >= kRouteMultiMin ? 1u + kRouteWaves : 1u;
+    hipExtLaunchKernelGGL(route_kernel, dim3(grid), dim3(kRouteThreads), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 
