@@ -7,17 +7,14 @@
 // the expert of each group block).  Here it is produced on the device so that
 // no host round trip of the routing is needed.
 //
-// One workgroup of 16 wave64s does everything up to kRouteMultiMin
-// assignments.  Each wave owns a contiguous chunk of the assignments.  From
-// kRouteMultiMin on, 1 + 16 workgroups run: every one counts the
-// whole batch per chunk (the same numbers everywhere, no communication between
-// workgroups), workgroup 0 writes the counts and offsets and builds the task
-// lists, and workgroup 1 + c scatters chunk c with its 16 waves (sub-chunk
-// counts, then the same ballot ranking), so the scatter -- bound by one
-// workgroup's VALU issue -- runs on 16 CUs.  Up to kLdsIds ids are read from HBM once, into
-// LDS, and the scatter reads them there and builds row_src in LDS, which then
-// goes out with coalesced stores; larger N reads the ids twice and scatters
-// row_src straight to memory.
+// 1 + 16 workgroups of 16 wave64s, with no communication between them.
+// Every workgroup counts the whole batch per chunk (wave w of each counts
+// chunk w, so all hold the same numbers): up to kLdsIds ids are read once
+// into LDS, larger N reads them from memory again in the scatter.
+// Workgroup 0 writes the counts, offsets and padding rows and builds the task
+// lists; workgroup 1 + c scatters chunk c with its 16 waves (sub-chunk counts,
+// then a ballot ranking within each sub-chunk).  The scatter is bound by a
+// workgroup's VALU issue, so it runs on 16 CUs while workgroup 0 plans.
 #include "moe_internal.h"
 #include "moe_wave.h"
 
@@ -25,14 +22,9 @@ namespace moe {
 namespace {
 
 constexpr int kLdsIds = 16384;
-// padded rows of kLdsIds assignments over up to kMaxExperts experts
-constexpr int kLdsRows = kLdsIds + kMaxExperts * (kBlockM - 1);
-// M-tiles per list that the rank-lookup table (kept in the ids' LDS once the
-// scatter is done) can hold
+// M-tiles per list that the rank-lookup table (kept in the ids' LDS, which
+// workgroup 0 no longer needs when it builds the lists) can hold
 constexpr int kRankTable = kLdsIds / 2;
-// From this many assignments the routing runs on 1 + kRouteWaves workgroups
-// (workgroup 1 + c scatters chunk c); below, one workgroup does everything.
-constexpr int kRouteMultiMin = 4096;
 
 // Largest e in [0,n) with off[e] <= r, for a non-decreasing off[0..n]
 // and r < off[n].  Empty entries (off[e] == off[e+1]) are never returned.
@@ -58,7 +50,7 @@ __device__ __forceinline__ int cbs_on(int r, int nb, int x) {
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     __shared__ short s_ids[kLdsIds];   // valid ids, -1 for the others; later the rank tables
-    __shared__ int s_rows[kLdsRows];    // row_src while it is built
+    __shared__ int s_sub[kRouteWaves * kMaxExperts];  // [wave][E]: sub-chunk counts of the scattered chunk
     __shared__ int s_cnt[kMaxExperts];
     __shared__ int s_tiles[kMaxExperts];
     __shared__ int s_off[kMaxExperts + 1];
@@ -77,19 +69,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
     const int wave = tid >> 6;
     const int E = a.E;
     const int N = a.N;
-    const int g = blockIdx.x;
-    const bool multi = gridDim.x > 1;  // N >= kRouteMultiMin (launch_route)
+    const int g = blockIdx.x;  // 0: counts, offsets, task lists; 1 + c: scatter of chunk c
     const bool in_lds = N <= kLdsIds;
-    // row_src is built in LDS when the ids are there and the scatter is large
-    // enough for its scattered stores to cost more than the extra pass
-    const bool stage_rows = in_lds && N > kRouteThreads && !multi;
-    // multi: the sub-chunk counts of the workgroup's chunk, [kRouteWaves][E],
-    // in s_rows (not staged in that mode)
-    int* s_sub = s_rows;
 
-    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_wcnt[i / E][i % E] = 0;
-    if (multi)
-        for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) s_sub[i] = 0;
+    for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) {
+        s_wcnt[i / E][i % E] = 0;
+        s_sub[i] = 0;
+    }
     if (tid == 0) s_dropped = 0;
     if (a.zero && g == 0)
         for (int i = tid; i < kZeroBytes / 4; i += kRouteThreads) reinterpret_cast<int*>(a.zero)[i] = 0;
@@ -169,28 +155,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
             a.padded_offsets[e] = s_poff[e];
         }
     }
-    // padding rows of each group (in LDS: every row, the scatter then fills
-    // the valid ones) and the unused tail of the padded space
-    if (stage_rows) {
-        for (int i = tid; i < n_pad; i += kRouteThreads) s_rows[i] = -1;
-        __syncthreads();
-    } else if (g == 0) {
+    // padding rows of each group and the unused tail of the padded space
+    if (g == 0) {
         for (int e = wave; e < E; e += kRouteWaves)
             for (int r = s_poff[e] + s_cnt[e] + lane; r < s_poff[e + 1]; r += 64) a.row_src[r] = -1;
-    }
-    if (g == 0) {
         for (int64_t i = n_pad + tid; i < a.n_pad_cap; i += kRouteThreads) a.row_src[i] = -1;
         if (a.full)
             for (int i = n_valid + tid; i < N; i += kRouteThreads) a.sorted_p[i] = -1;
     }
 
-    if (multi && g > 0) {
-        // 3'. workgroup 1 + c scatters chunk c (workgroup 0 skips the scatter
-        // and goes on to the task lists): wave v takes the v-th sub-chunk,
-        // counts it, and ranks within it as the single-workgroup scatter
-        // below does within a chunk.  The rank of p: chunk base (earlier
-        // chunks' counts, s_wcnt[c]) + earlier sub-chunks' counts + the
-        // running count within the sub-chunk.
+    if (g > 0) {
+        // 3. stable scatter of chunk c = g - 1 (workgroup 0 goes on to the
+        // task lists): wave v takes the v-th sub-chunk and counts it; then it
+        // walks the sub-chunk 64 assignments at a time.  Lanes with the same
+        // expert find each other with one ballot per bit of the key (the
+        // expert id, or E for an invalid id: as many bits as E has, at most
+        // 9).  The rank of p: chunk base (earlier chunks' counts, s_wcnt[c])
+        // + earlier sub-chunks' counts + the wave's running count for the
+        // expert + the number of lower lanes with the same expert; the lowest
+        // such lane then advances the running count.  Ranks follow ascending p.
         {
             const int c = g - 1;
             const int q_lo = c * chunk, q_hi = min(N, q_lo + chunk);
@@ -247,53 +230,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         return;
     }
 
-    // 3. stable scatter: each wave walks its chunk 64 assignments at a time.
-    // Lanes with the same expert find each other with one ballot per bit of
-    // the key (the expert id, or E for an invalid id: as many bits as E has,
-    // at most 9); the rank of an assignment is its wave's running base for
-    // that expert plus the number of lower lanes with the same expert.  The
-    // lowest such lane then advances the base.  No workgroup barrier: the
-    // bases of a wave are its own.  (Single workgroup only: with several,
-    // workgroup 0 has no scatter.)
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int key_bits = 32 - __clz(E);
-    for (int base = c_lo; !multi && base < c_lo + chunk; base += 64) {
-        const int p = base + lane;
-        const int id = p < c_hi ? (in_lds ? s_ids[p] : a.ids[p]) : -1;
-        const bool valid = (unsigned)id < (unsigned)E;
-        const int key = valid ? id : E;
-        uint64_t m = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 9; ++b) {
-            if (b >= key_bits) break;
-            const bool bit = (key >> b) & 1;
-            const uint64_t bal = __ballot(bit);
-            m &= bit ? bal : ~bal;
-        }
-        const int wrank = __popcll(m & lt_mask);
-        if (valid) {
-            const int r = s_wcnt[wave][id] + wrank;
-            if (a.full) {
-                a.pos[p] = s_off[id] + r;
-                a.ppos[p] = s_poff[id] + r;
-                a.sorted_p[s_off[id] + r] = p;
-            }
-            if (stage_rows)
-                s_rows[s_poff[id] + r] = p;
-            else
-                a.row_src[s_poff[id] + r] = p;
-        } else if (p < c_hi && a.full) {
-            a.pos[p] = -1;
-            a.ppos[p] = -1;
-        }
-        // every lane has read its base above (the wave's LDS accesses stay in
-        // order); the first lane of each expert group advances it
-        if (valid && wrank == 0) s_wcnt[wave][id] += __popcll(m);
-    }
-    // Ranking and M-tile sizes of the task lists (step 5 below) need only the
-    // counts, so they run before the scatter barrier: waves with no scatter
-    // work (most of them at small N) rank while the others scatter, and the
-    // scatter barrier also publishes s_order, s_rtiles, s_mb1 and s_mb2.
+    // (workgroup 0 from here on)
     if (a.nb1 > 0) {
         // 5. task lists.  Experts are ranked by descending row count (ties by id):
         // longest work first.  An expert's tasks are its M-tiles (up to
@@ -354,9 +291,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
         }
     }
     __syncthreads();
-
-    if (stage_rows)  // row_src out of LDS, coalesced
-        for (int i = tid; i < n_pad; i += kRouteThreads) a.row_src[i] = s_rows[i];
 
     // 4. block map: expert and first padded row of each group block (the
     // layer's GEMMs take the task lists instead, so only for moe_route)
@@ -498,8 +432,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(RouteArgs a) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    const unsigned grid = a.N >= kRouteMultiMin ? 1u + kRouteWaves : 1u;
-    hipExtLaunchKernelGGL(route_kernel, dim3(grid), dim3(kRouteThreads), 0, s, t0, t1, 0, a);
+    hipExtLaunchKernelGGL(route_kernel, dim3(1 + kRouteWaves), dim3(kRouteThreads), 0, s, t0, t1, 0, a);
     return hipGetLastError();
 }
 
